@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Benchmark of the FSDP unit pipeline on one MI355X.
+
+Metric: GB/s and % of HBM peak for the fused reduce-scatter + AdamW + unshard
+per FSDP unit.  One step = every unit slot of the workload, each through
+  fused reduce-scatter + AdamW + cast (rank 0's shard)  ->  all-gather x G
+  ->  per-tensor views,
+on synthetic inputs already resident in HBM.  Flatten + pad is an init-time
+step: it is timed separately and reported beside the line.
+
+Bytes are algorithmic: per shard element, N*g (read the N ranks' gradient
+blocks) + 12 (read master, m, v) + 12 (write them) + c (write the compute
+copy) + G * 2*N*c (each gather reads N shards and writes N), with g and c the
+gradient and compute element sizes.  A unit pool of distinct blocks larger than
+the 256 MB Infinity Cache is cycled over the slots so every step streams HBM.
+
+Prints one JSON line.  --gpus above 1 exits: this measures one GPU.
+"""
+import argparse
+import ctypes
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "GB/s and % HBM peak for fused reduce-scatter+AdamW+unshard per FSDP unit"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2-large-block",
+                    help="gpt2-large-block (default), gpt2-xl-model, gpt3-13b-block, llama70b-block, tiny")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time budget of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="skip the per-launch HIP events (the roofline figure needs them)")
+    ap.add_argument("--probe", choices=["copy"], default=None,
+                    help="copy: time a plain 1 GiB copy with the gather kernel (counter calibration)")
+    return ap.parse_args()
+
+
+def sizes(cfg):
+    g = 4 if cfg.grad_dt == "f32" else 2
+    c = 4 if cfg.compute_dt == "f32" else 2
+    N, G = cfg.world, cfg.gathers
+    fused = N * g + 24 + c
+    gather = 2 * N * c
+    return g, c, fused, gather, fused + G * gather
+
+
+class Unit:
+    """Rank 0's resident buffers for one distinct block of the pool."""
+
+    def __init__(self, cfg, block, ss, torch, workloads):
+        dev = "cuda"
+        P, Pp, S = ss.fsdp_layout(cfg.numels, cfg.world)
+        self.P, self.Pp, self.S = P, Pp, S
+        params = workloads.param_tensors(cfg, block, dev)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        flat = ss.fsdp_flatten_pad(params, cfg.world)
+        ev1.record()
+        torch.cuda.synchronize()
+        self.flatten_ms = ev0.elapsed_time(ev1)
+        self.flatten_bytes = 2 * P * 4 + (Pp - P) * 4
+        del params
+        self.grads = [workloads.rank_grad(cfg, block, q, Pp, dev) for q in range(cfg.world)]
+        cdt = workloads.TORCH_DTYPE[cfg.compute_dt]
+        hp = ss.AdamWHP(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.step)
+        # peers' compute shards: the other ranks' own steps on the same unit
+        self.peers = []
+        for q in range(1, cfg.world):
+            mq, vq = workloads.moments(cfg, block, q * S, S, P, dev)
+            pq = flat[q * S:(q + 1) * S].clone()
+            cq = torch.empty(S, dtype=cdt, device=dev)
+            ss.fsdp_sharded_adamw(pq, mq, vq, self.grads, q, cfg.fp32_reduce, hp, compute_shard=cq)
+            self.peers.append(cq)
+            del mq, vq, pq
+        self.master = flat[:S].clone()
+        del flat
+        self.m, self.v = workloads.moments(cfg, block, 0, S, P, dev)
+        self.compute = torch.empty(S, dtype=cdt, device=dev)
+        self.full = torch.empty(Pp, dtype=cdt, device=dev)
+        torch.cuda.synchronize()
+
+
+def cpu_baseline(cfg, unit, budget_s, np_of_bytes):
+    """The oracle, single-threaded on one host core, on rank 0's step of one
+    resident block, repeated until the budget is spent."""
+    import numpy as np
+    import oracle
+    g, c, fused, gather, per_elt = sizes(cfg)
+    S = unit.S
+    cap = min(S, 4 * 1024 * 1024)          # bounded sample: first `cap` shard elements
+    # rank 0's block of each rank's gradient is its first S elements
+    grads = [np_of_bytes(x[:cap]) for x in unit.grads]
+    peers = [np_of_bytes(p[:cap]) for p in unit.peers]
+    p0, m0, v0 = (np_of_bytes(t[:cap]) for t in (unit.master, unit.m, unit.v))
+    h = oracle.hp(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.step)
+    try:
+        cores_before = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {sorted(cores_before)[0]})
+    except (AttributeError, OSError):
+        cores_before = None
+    elems = 0
+    t0 = time.perf_counter()
+    while True:
+        p, m, v = p0.copy(), m0.copy(), v0.copy()
+        avg = oracle.grad_average(grads, 0, cap, cfg.grad_dt, cfg.fp32_reduce)
+        g32 = avg if avg.dtype == np.float32 else oracle.to_f32(avg, cfg.grad_dt)
+        oracle.adamw(p, m, v, g32, h)
+        comp = oracle.cast(p, cfg.compute_dt)
+        for _ in range(cfg.gathers):
+            oracle.gather([comp] + peers, cfg.compute_dt)
+        elems += cap
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    if cores_before is not None:
+        os.sched_setaffinity(0, cores_before)
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": round(elems * per_elt / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": "rank 0's step (reduce-scatter, AdamW, cast, %d gather) on the first %d shard "
+                  "elements of one %s block, repeated %d times in %.1f s; host %s (%s cpus)"
+                  % (cfg.gathers, cap, cfg.name, elems // cap, dt, model or platform.machine(),
+                     os.cpu_count()),
+        "elements_per_s": round(elems / dt, 1),
+    }
+
+
+def traffic_from_profiles(kernel_tag, src_hash):
+    """Counter-measured HBM bytes per launch, if a summary for this exact kernel
+    source is committed under profiles/."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % kernel_tag)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != src_hash:
+        return None
+    try:
+        return float(vals["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("fsdp_kernels.hip", "fsdp_kernels.h"):
+        h.update(open(os.path.join(ROOT, "sharded_state_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures the one-GPU hot path only; --gpus %d is not supported "
+              "(run with --gpus 1)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sharded_state_amd as ss
+    from sharded_state_amd import _native as N
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    lib = N.lib()
+    torch.cuda.set_device(0)
+
+    if args.probe == "copy":
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        copy = (N.ptr_array([a.data_ptr()]), 1, n // 4, N.F32, ctypes.c_void_p(b.data_ptr()), st)
+        for _ in range(3):
+            N.check("fsdp_unshard_gather", lib.fsdp_unshard_gather(*copy))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        reps = 20
+        for _ in range(reps):
+            lib.fsdp_unshard_gather(*copy)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "ms": ms,
+                          "gbps": 2 * n / ms / 1e6}))
+        return
+
+    cfg = workloads.CONFIGS[args.workload]
+    g, c, fused_b, gather_b, per_elt = sizes(cfg)
+    pool = [Unit(cfg, b, ss, torch, workloads) for b in range(cfg.pool)]
+    S = pool[0].S
+    stream = torch.cuda.current_stream()
+    st = ctypes.c_void_p(stream.cuda_stream)
+    hp = ss.AdamWHP(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.step)
+    hp_ref = ctypes.byref(hp)
+    gcode, ccode = ss.dtype_code(pool[0].grads[0].dtype), ss.dtype_code(pool[0].compute.dtype)
+    numels = N.i64_array(cfg.numels)
+    views = (N.View * len(cfg.numels))()
+
+    # prepared ctypes arguments: marshalling happens once, outside the timed region
+    plans = []
+    for u in pool:
+        fused = (ctypes.c_void_p(u.master.data_ptr()), ctypes.c_void_p(u.m.data_ptr()),
+                 ctypes.c_void_p(u.v.data_ptr()), N.ptr_array([x.data_ptr() for x in u.grads]),
+                 cfg.world, 0, gcode, int(cfg.fp32_reduce), ctypes.c_void_p(u.compute.data_ptr()),
+                 ccode, S, hp_ref, st)
+        gather = (N.ptr_array([u.compute.data_ptr()] + [p.data_ptr() for p in u.peers]), cfg.world, S,
+                  ccode, ctypes.c_void_p(u.full.data_ptr()), st)
+        unflat = (numels, len(cfg.numels), u.Pp, views, None, ccode, None, None)
+        plans.append((fused, gather, unflat))
+    f_adamw, f_gather, f_views = lib.fsdp_sharded_adamw, lib.fsdp_unshard_gather, lib.fsdp_unflatten_views
+    G = cfg.gathers
+    slots = [plans[s % len(plans)] for s in range(cfg.blocks)]
+    use_events = not args.no_kernel_events
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(cfg.blocks * args.steps)] if use_events else []
+
+    def step(ev_base=None):
+        for i, (fa, ga, va) in enumerate(slots):
+            if ev_base is not None:
+                evs[ev_base + i][0].record(stream)
+            rc = f_adamw(*fa)
+            if ev_base is not None:
+                evs[ev_base + i][1].record(stream)
+            if rc:
+                N.check("fsdp_sharded_adamw", rc)
+            for _ in range(G):
+                rc = f_gather(*ga)
+                if rc:
+                    N.check("fsdp_unshard_gather", rc)
+            rc = f_views(*va)
+            if rc:
+                N.check("fsdp_unflatten_views", rc)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for k in range(args.steps):
+        step(k * cfg.blocks if use_events else None)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+    bytes_step = per_elt * S * cfg.blocks
+    gbps = bytes_step / (ms_step * 1e-3) / 1e9
+
+    roof = None
+    if use_events:
+        durs = [a.elapsed_time(b) for a, b in evs]
+        avg_ms = statistics.fmean(durs)
+        achieved = fused_b * S / (avg_ms * 1e-3) / 1e9
+        traffic = traffic_from_profiles("fused_rs_adamw_%s" % cfg.name, kernel_source_hash())
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "k_rs_adamw_cast (fused reduce-scatter + AdamW + cast)",
+                "bytes_per_launch": fused_b * S, "avg_launch_ms": round(avg_ms, 5),
+                "median_launch_ms": round(statistics.median(durs), 5)}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        def np_of_bytes(t):
+            import numpy as np
+            t = t.detach().cpu()
+            if t.dtype in (torch.float16, torch.bfloat16):
+                return t.view(torch.int16).numpy().view(np.uint16)
+            return t.numpy()
+        cpu = cpu_baseline(cfg, pool[0], args.cpu_seconds, np_of_bytes)
+
+    flat_ms = statistics.fmean(u.flatten_ms for u in pool)
+    out = {
+        "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "config": {"workload": "%s x%d" % (cfg.name, cfg.blocks), "world": cfg.world, "rank": 0,
+                   "shard_numel": S, "unit_numel": pool[0].P, "blocks_per_step": cfg.blocks,
+                   "distinct_blocks": cfg.pool, "grad_dtype": cfg.grad_dt,
+                   "fp32_reduce_scatter": cfg.fp32_reduce, "compute_dtype": cfg.compute_dt,
+                   "gathers_per_step": G, "bytes_per_shard_element": per_elt,
+                   "bytes_per_step": bytes_step},
+        "shard_elements_per_s": round(S * cfg.blocks / (ms_step * 1e-3), 1),
+        "wall_s_timed": round(wall, 3),
+        "flatten": {"avg_ms": round(flat_ms, 4),
+                    "gbps": round(pool[0].flatten_bytes / (flat_ms * 1e-3) / 1e9, 1)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+/*
+ * fsdp_shard.h -- C ABI of libfsdp_shard.so: the one-device data-parallel hot
+ * path of Fully Sharded Data Parallel (ZeRO stage 3) on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * One training step of one FSDP unit, as the pages state the problem:
+ *   flatten + pad   the unit's tensors become one flat buffer, padded at the
+ *                   tail with +0 to a multiple of the world size N;
+ *   reduce-scatter  N ranks' flat gradients are averaged, (1/N) * sum_i G_i,
+ *                   and rank r keeps block r;
+ *   sharded AdamW   each rank updates only its own fp32 master/m/v shard;
+ *   cast            the master shard is rounded to the compute dtype;
+ *   all-gather      the N compute shards are concatenated into the full buffer;
+ *   views           each tensor is a slice of the full buffer.
+ * Sources (cited per call below):
+ *   [TR] "Fully Sharded Data Parallel: faster AI training with fewer GPUs"
+ *        (techreport.ngo)
+ *   [P3] "FSDP (Fully Sharded Data Parallel)" (vanos001 placement-prep notes)
+ *   [P4] "fairseq 中的 Fully Sharded Data Parallel (FSDP) 实战指南" (zskr.cn)
+ *   [P5] "Data Parallelism" (vanos001 placement-prep notes)
+ *
+ * Conventions shared by every call:
+ *  - Memory.  The caller owns every buffer.  "device" pointers are HIP device
+ *    memory on the current device; arrays of pointers (srcs, rank_grads,
+ *    shards, dsts) are HOST arrays holding device pointers; numels, views_out
+ *    and *_out scalars are host memory.  The library keeps no pointer after a
+ *    call returns and allocates no device memory.
+ *  - Streams.  `stream` is a hipStream_t (NULL = the null stream).  Work is
+ *    enqueued asynchronously; nothing synchronizes.  Any pointer alignment is
+ *    accepted; 16-byte-aligned buffers take the wide (dwordx4) path.
+ *  - Errors.  Every argument is validated on the host before anything is
+ *    enqueued; on a negative status nothing was launched and
+ *    fsdp_last_error() returns a message (thread-local).  Nothing throws or
+ *    aborts across the ABI.  FSDP_E_HIP reports a HIP runtime error at enqueue.
+ *  - Aliasing.  No output may overlap an input or another output, except the
+ *    in-place master/m/v of fsdp_sharded_adamw and a shard already sitting in
+ *    its slot of the full buffer in fsdp_unshard_gather; overlaps are reported
+ *    as FSDP_E_ALIAS.
+ *  - Arithmetic.  fp32 operations are single IEEE-754 operations with round to
+ *    nearest even (no FMA contraction, correctly rounded divide and square
+ *    root, subnormals kept); 16-bit outputs are rounded to nearest even.
+ */
+#ifndef FSDP_SHARD_H
+#define FSDP_SHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FSDP_API __attribute__((visibility("default")))
+
+#define FSDP_ABI_VERSION 1
+#define FSDP_MAX_WORLD 128
+
+typedef enum fsdp_dtype {
+    FSDP_F32 = 0,   /* IEEE binary32 */
+    FSDP_F16 = 1,   /* IEEE binary16 */
+    FSDP_BF16 = 2   /* bfloat16 */
+} fsdp_dtype;
+
+enum {
+    FSDP_OK = 0,
+    FSDP_E_INVAL = -1,  /* null pointer, world/rank out of range, negative size, bad step */
+    FSDP_E_DTYPE = -2,  /* unsupported dtype or dtype combination */
+    FSDP_E_SIZE = -3,   /* output capacity too small or inconsistent sizes */
+    FSDP_E_ALIAS = -4,  /* an output overlaps an input or another output */
+    FSDP_E_HIP = -5     /* HIP runtime error while enqueueing */
+};
+
+/* AdamW hyper-parameters of one flat unit.  Flattening puts the whole unit in
+ * one parameter group, so one set applies to every element, biases and norm
+ * weights included ([TR] "Adoption paths for FSDP", advanced concern 3).
+ * step is t >= 1, the index of the step being taken. */
+typedef struct fsdp_adamw_hp {
+    float lr;
+    float beta1;
+    float beta2;
+    float eps;
+    float weight_decay;
+    int64_t step;
+} fsdp_adamw_hp;
+
+/* Tensor k of a flat unit is elements [offset, offset + numel). */
+typedef struct fsdp_view {
+    int64_t offset;
+    int64_t numel;
+} fsdp_view;
+
+/* Version of this ABI (FSDP_ABI_VERSION). */
+FSDP_API int fsdp_abi_version(void);
+
+/* Message for the last negative status returned on this thread ("" if none). */
+FSDP_API const char* fsdp_last_error(void);
+
+/* Sizes of a flat unit (host only, no device work).
+ * numels[n_tensors]: element counts of the unit's tensors, in flat order.
+ * Outputs: total P = sum numels; padded P_pad = smallest multiple of world
+ * >= P; shard S = P_pad / world.  Padding follows from the tail-padding rule
+ * of fsdp_flatten_pad. */
+FSDP_API int fsdp_layout(const int64_t* numels, int32_t n_tensors, int32_t world,
+                         int64_t* numel_out, int64_t* padded_numel_out,
+                         int64_t* shard_numel_out);
+
+/* Flatten + pad.  [TR] "Adoption paths for FSDP" (advanced concern 3) and
+ * [P4] flag table (flatten_parameters): a wrapped unit's parameters become one
+ * flat tensor.  flat[off_k + i] = srcs[k][i] with off_k = numel_0 + ... +
+ * numel_{k-1} (tensors in caller order, each contiguous row-major, no padding
+ * between tensors), then flat[P .. P_pad) = +0 so the buffer splits into
+ * `world` equal shards.
+ *   srcs[n_tensors]   host array of device pointers, each numels[k] elements of dt
+ *                     (may be NULL where numels[k] == 0)
+ *   flat              device, flat_capacity elements of dt; must not overlap a source
+ *   padded_numel_out  host, receives P_pad (may be NULL)
+ * FSDP_E_SIZE if flat_capacity < P_pad. */
+FSDP_API int fsdp_flatten_pad(const void* const* srcs, const int64_t* numels, int32_t n_tensors,
+                              fsdp_dtype dt, int32_t world, void* flat, int64_t flat_capacity,
+                              int64_t* padded_numel_out, void* stream);
+
+/* Reduce-scatter, emulated on one device.  [TR] figure on the decomposition of
+ * all-reduce into reduce-scatter and all-gather: blocks are reduced by rank
+ * index, rank r keeping block r; [P5] "The Basic Protocol": the average is
+ * (1/N) * sum_i G_i; [P4] flag table: --fp32-reduce-scatter reduces in fp32.
+ *   rank_grads[world]  host array of device pointers; rank q's flat gradient,
+ *                      world * shard_numel elements of grad_dt (only block
+ *                      `rank` is read)
+ *   grad_shard_out     device, shard_numel elements: fp32 when fp32_reduce != 0
+ *                      or grad_dt == FSDP_F32, else grad_dt
+ * Element i (j = rank * shard_numel + i), ranks folded left to right:
+ *   fp32 mode:   acc = G_0[j]; acc = acc + G_q[j] (q = 1..N-1); out = acc / N
+ *   16-bit mode: a = G_0[j]; a = round16(a + G_q[j]); out = round16(a / N)
+ * 1 <= world <= FSDP_MAX_WORLD, 0 <= rank < world. */
+FSDP_API int fsdp_reduce_scatter_local(const void* const* rank_grads, int32_t world, int32_t rank,
+                                       int64_t shard_numel, fsdp_dtype grad_dt, int32_t fp32_reduce,
+                                       void* grad_shard_out, void* stream);
+
+/* Sharded AdamW, fused with the reduce-scatter and the cast, one pass over the
+ * shard.  [P4] "工作原理" and "限制与兼容性说明": each rank runs the pointwise
+ * optimizer on its own shard only (AdamW is among the supported pointwise
+ * optimizers); [P5] "The Basic Protocol": W = W - lr * Adam(G_avg, m, v);
+ * [P3] "Mixed Precision and FSDP": fp32 master with a 16-bit compute copy.
+ * The gradient of element i is the reduce-scatter average defined above,
+ * converted to fp32.  Passing world = 1, rank = 0 and rank_grads = {g} steps
+ * with an already reduced gradient shard g of dtype grad_dt.
+ * Update (the published AdamW; t = hp->step; host scalars computed in double
+ * and rounded once to fp32: decay = 1 - lr*wd, step_size = lr / (1 - beta1^t),
+ * bc2 = sqrt(1 - beta2^t)):
+ *   p1 = p * decay;  m1 = beta1*m + (1-beta1)*g;  v1 = beta2*v + (1-beta2)*(g*g)
+ *   p2 = p1 - step_size * (m1 / (sqrt(v1) / bc2 + eps))
+ *   master = p2, exp_avg = m1, exp_avg_sq = v1, compute_shard = round(p2)
+ *   master, exp_avg, exp_avg_sq  device fp32, shard_numel each, updated in place
+ *   compute_shard                device, shard_numel of compute_dt, or NULL (no cast)
+ *   hp                           host; hp->step >= 1 */
+FSDP_API int fsdp_sharded_adamw(float* master, float* exp_avg, float* exp_avg_sq,
+                                const void* const* rank_grads, int32_t world, int32_t rank,
+                                fsdp_dtype grad_dt, int32_t fp32_reduce,
+                                void* compute_shard, fsdp_dtype compute_dt, int64_t shard_numel,
+                                const fsdp_adamw_hp* hp, void* stream);
+
+/* All-gather unshard.  [P3] "The Per-Layer Communication" and [TR] "From
+ * all-reduce to sharded parameters": the full parameters are gathered from the
+ * N shards before compute; full[q * S + i] = shards[q][i].
+ *   shards[world]  host array of device pointers, shard_numel elements of dt each
+ *   full_out       device, world * shard_numel elements of dt
+ * A shard that already sits at its slot (shards[q] == full_out + q*S) is not
+ * copied; any other overlap with full_out is FSDP_E_ALIAS.  Call it twice per
+ * step when parameters are resharded after the forward ([TR] pseudo-code). */
+FSDP_API int fsdp_unshard_gather(const void* const* shards, int32_t world, int64_t shard_numel,
+                                 fsdp_dtype dt, void* full_out, void* stream);
+
+/* Per-tensor views of the full buffer.  [P3] "The FSDP Unit" (use_orig_params):
+ * tensor k is full[off_k : off_k + numel_k]; the padding belongs to no view.
+ *   views_out[n_tensors]  host, receives {off_k, numel_k}
+ *   padded_numel          length of the full buffer (>= sum numels)
+ *   full, dsts            if dsts is NULL only the views are produced (no device
+ *                         work; full may be NULL).  Otherwise dsts[k] (host
+ *                         array of device pointers) receives a copy of tensor k. */
+FSDP_API int fsdp_unflatten_views(const int64_t* numels, int32_t n_tensors, int64_t padded_numel,
+                                  fsdp_view* views_out, const void* full, fsdp_dtype dt,
+                                  void* const* dsts, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSDP_SHARD_H */

@@ -1,0 +1,27 @@
+"""sharded_state_amd -- the one-device data-parallel hot path of Fully Sharded
+Data Parallel (ZeRO stage 3) on AMD Instinct MI355X (gfx950).
+
+The pipeline of one FSDP unit per training step -- flatten + pad, emulated
+reduce-scatter of N ranks' gradients, sharded AdamW on the fp32 master shard,
+cast to the compute dtype, all-gather unshard, per-tensor views -- runs in the
+hand-written HIP kernels of ``libfsdp_shard.so`` behind the C ABI declared in
+``include/fsdp_shard.h``.  This package is its Python binding: argument
+marshalling over ctypes, with PyTorch for device memory and streams.
+"""
+from ._native import AdamWHP, FsdpError, MAX_WORLD, lib  # noqa: F401
+from .api import (  # noqa: F401
+    dtype_code,
+    fsdp_flatten_pad,
+    fsdp_layout,
+    fsdp_reduce_scatter_local,
+    fsdp_sharded_adamw,
+    fsdp_unflatten_views,
+    fsdp_unshard_gather,
+    view_table,
+)
+
+__all__ = [
+    "AdamWHP", "FsdpError", "MAX_WORLD", "lib", "dtype_code", "fsdp_layout", "fsdp_flatten_pad",
+    "fsdp_reduce_scatter_local", "fsdp_sharded_adamw", "fsdp_unshard_gather",
+    "fsdp_unflatten_views", "view_table",
+]

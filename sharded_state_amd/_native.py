@@ -1,0 +1,93 @@
+"""ctypes declarations of libfsdp_shard.so (the C ABI in include/fsdp_shard.h).
+
+The library is built in-tree by ``sharded_state_amd/build.py`` (or
+``__graft_entry__.build()``).  There is no fallback: if the library is missing
+or fails to load, every entry point raises.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfsdp_shard.so")
+
+F32, F16, BF16 = 0, 1, 2
+OK, E_INVAL, E_DTYPE, E_SIZE, E_ALIAS, E_HIP = 0, -1, -2, -3, -4, -5
+MAX_WORLD = 128
+ABI_VERSION = 1
+
+
+class AdamWHP(ctypes.Structure):
+    """fsdp_adamw_hp: one hyper-parameter set per flat unit."""
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64)]
+
+    def __init__(self, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1):
+        super().__init__(lr, beta1, beta2, eps, weight_decay, step)
+
+    def __repr__(self):
+        return ("AdamWHP(lr=%g, beta1=%g, beta2=%g, eps=%g, weight_decay=%g, step=%d)"
+                % (self.lr, self.beta1, self.beta2, self.eps, self.weight_decay, self.step))
+
+
+class View(ctypes.Structure):
+    """fsdp_view"""
+    _fields_ = [("offset", ctypes.c_int64), ("numel", ctypes.c_int64)]
+
+
+class FsdpError(RuntimeError):
+    def __init__(self, func, code, msg):
+        super().__init__("%s failed (status %d): %s" % (func, code, msg))
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load the HIP library (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libfsdp_shard.so not found at %s: build it first with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'` or "
+                          "`python sharded_state_amd/build.py`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    vpp = ctypes.POINTER(ctypes.c_void_p)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    L.fsdp_abi_version.restype = ctypes.c_int
+    L.fsdp_abi_version.argtypes = []
+    L.fsdp_last_error.restype = ctypes.c_char_p
+    L.fsdp_last_error.argtypes = []
+    L.fsdp_layout.restype = ctypes.c_int
+    L.fsdp_layout.argtypes = [i64p, i32, i32, i64p, i64p, i64p]
+    L.fsdp_flatten_pad.restype = ctypes.c_int
+    L.fsdp_flatten_pad.argtypes = [vpp, i64p, i32, ctypes.c_int, i32, vp, i64, i64p, vp]
+    L.fsdp_reduce_scatter_local.restype = ctypes.c_int
+    L.fsdp_reduce_scatter_local.argtypes = [vpp, i32, i32, i64, ctypes.c_int, i32, vp, vp]
+    L.fsdp_sharded_adamw.restype = ctypes.c_int
+    L.fsdp_sharded_adamw.argtypes = [vp, vp, vp, vpp, i32, i32, ctypes.c_int, i32, vp, ctypes.c_int,
+                                     i64, ctypes.POINTER(AdamWHP), vp]
+    L.fsdp_unshard_gather.restype = ctypes.c_int
+    L.fsdp_unshard_gather.argtypes = [vpp, i32, i64, ctypes.c_int, vp, vp]
+    L.fsdp_unflatten_views.restype = ctypes.c_int
+    L.fsdp_unflatten_views.argtypes = [i64p, i32, i64, ctypes.POINTER(View), vp, ctypes.c_int, vpp, vp]
+    v = L.fsdp_abi_version()
+    if v != ABI_VERSION:
+        raise ImportError("libfsdp_shard.so ABI version %d, binding expects %d" % (v, ABI_VERSION))
+    _lib = L
+    return L
+
+
+def check(func, code):
+    if code != OK:
+        raise FsdpError(func, code, lib().fsdp_last_error().decode(errors="replace"))
+
+
+def ptr_array(ptrs):
+    return (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
+
+
+def i64_array(vals):
+    return (ctypes.c_int64 * max(len(vals), 1))(*[int(v) for v in vals])

@@ -1,0 +1,212 @@
+"""Python binding of the C ABI, one function per entry point, same names.
+
+Argument marshalling only: tensors are turned into device pointers, element
+counts and the current HIP stream; every step of the pipeline runs in the HIP
+kernels of libfsdp_shard.so.  PyTorch supplies device memory and streams.
+
+Gradient, shard and full buffers are 1-D contiguous tensors on one device.
+"""
+import ctypes
+
+import torch
+
+from . import _native as N
+from ._native import AdamWHP, View, check, i64_array, ptr_array
+
+_DT = {torch.float32: N.F32, torch.float16: N.F16, torch.bfloat16: N.BF16}
+_TORCH = {v: k for k, v in _DT.items()}
+
+
+def dtype_code(dtype):
+    try:
+        return _DT[dtype]
+    except KeyError:
+        raise TypeError("unsupported dtype %s (float32, float16, bfloat16)" % dtype) from None
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor, got %s" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _same_device(tensors):
+    devs = {t.device for t in tensors}
+    if len(devs) > 1:
+        raise ValueError("all tensors must be on one device, got %s" % sorted(map(str, devs)))
+
+
+def fsdp_layout(numels, world):
+    """(P, P_pad, S) of a unit with tensor sizes `numels` over `world` ranks."""
+    total, padded, shard = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    check("fsdp_layout", N.lib().fsdp_layout(i64_array(numels), len(numels), int(world),
+                                              ctypes.byref(total), ctypes.byref(padded),
+                                              ctypes.byref(shard)))
+    return total.value, padded.value, shard.value
+
+
+def fsdp_flatten_pad(tensors, world, flat=None, stream=None):
+    """Flatten the unit's tensors into one buffer padded with +0 to a multiple of
+    `world`.  Returns the flat buffer (allocated if `flat` is None)."""
+    tensors = [_dev(t, "tensors[%d]" % i) for i, t in enumerate(tensors)]
+    if not tensors:
+        raise ValueError("a unit needs at least one tensor")
+    dt = tensors[0].dtype
+    if any(t.dtype != dt for t in tensors):
+        raise TypeError("all tensors of a unit must share one dtype")
+    numels = [t.numel() for t in tensors]
+    _, padded, _ = fsdp_layout(numels, world)
+    device = tensors[0].device
+    if flat is None:
+        flat = torch.empty(padded, dtype=dt, device=device)
+    _dev(flat, "flat")
+    if flat.dtype != dt:
+        raise TypeError("flat dtype %s differs from the tensors' %s" % (flat.dtype, dt))
+    _same_device(tensors + [flat])
+    out = ctypes.c_int64()
+    with torch.cuda.device(device):
+        check("fsdp_flatten_pad", N.lib().fsdp_flatten_pad(
+            ptr_array([t.data_ptr() for t in tensors]), i64_array(numels), len(tensors),
+            dtype_code(dt), int(world), ctypes.c_void_p(flat.data_ptr()), flat.numel(),
+            ctypes.byref(out), _stream(stream, device)))
+    return flat[:out.value] if flat.numel() != out.value else flat
+
+
+def _grads(rank_grads, shard_numel):
+    rank_grads = [_dev(g, "rank_grads[%d]" % i) for i, g in enumerate(rank_grads)]
+    if not rank_grads:
+        raise ValueError("rank_grads is empty")
+    world = len(rank_grads)
+    gdt = rank_grads[0].dtype
+    for i, g in enumerate(rank_grads):
+        if g.dtype != gdt:
+            raise TypeError("rank_grads[%d] dtype %s differs from %s" % (i, g.dtype, gdt))
+        if g.numel() < world * shard_numel:
+            raise ValueError("rank_grads[%d] holds %d elements, need world*shard = %d"
+                             % (i, g.numel(), world * shard_numel))
+    return rank_grads, world, gdt
+
+
+def fsdp_reduce_scatter_local(rank_grads, rank, fp32_reduce, out=None, shard_numel=None, stream=None):
+    """Rank `rank`'s averaged gradient shard from the N ranks' flat gradients.
+    Output dtype: float32 if fp32_reduce or the grads are float32, else the grad dtype."""
+    world = len(rank_grads)
+    if shard_numel is None:
+        shard_numel = rank_grads[0].numel() // world if world else 0
+    rank_grads, world, gdt = _grads(rank_grads, shard_numel)
+    odt = torch.float32 if (fp32_reduce or gdt == torch.float32) else gdt
+    device = rank_grads[0].device
+    if out is None:
+        out = torch.empty(shard_numel, dtype=odt, device=device)
+    _dev(out, "out")
+    if out.dtype != odt or out.numel() != shard_numel:
+        raise ValueError("out must be %d elements of %s" % (shard_numel, odt))
+    _same_device(rank_grads + [out])
+    with torch.cuda.device(device):
+        check("fsdp_reduce_scatter_local", N.lib().fsdp_reduce_scatter_local(
+            ptr_array([g.data_ptr() for g in rank_grads]), world, int(rank), shard_numel,
+            dtype_code(gdt), int(bool(fp32_reduce)), ctypes.c_void_p(out.data_ptr()),
+            _stream(stream, device)))
+    return out
+
+
+def fsdp_sharded_adamw(master, exp_avg, exp_avg_sq, rank_grads, rank, fp32_reduce, hp,
+                       compute_shard=None, stream=None):
+    """Fused reduce-scatter + AdamW + cast on rank `rank`'s shard (master, exp_avg,
+    exp_avg_sq updated in place; compute_shard, if given, receives the rounded
+    master).  With one already-reduced gradient shard g: rank_grads=[g], rank=0."""
+    for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        _dev(t, name)
+        if t.dtype != torch.float32:
+            raise TypeError("%s must be float32" % name)
+        if t.numel() != master.numel():
+            raise ValueError("%s has %d elements, master %d" % (name, t.numel(), master.numel()))
+    S = master.numel()
+    rank_grads, world, gdt = _grads(rank_grads, S)
+    tensors = rank_grads + [master, exp_avg, exp_avg_sq]
+    cdt = N.F32
+    cptr = None
+    if compute_shard is not None:
+        _dev(compute_shard, "compute_shard")
+        if compute_shard.numel() != S:
+            raise ValueError("compute_shard has %d elements, need %d" % (compute_shard.numel(), S))
+        cdt = dtype_code(compute_shard.dtype)
+        cptr = compute_shard.data_ptr()
+        tensors.append(compute_shard)
+    _same_device(tensors)
+    if not isinstance(hp, AdamWHP):
+        hp = AdamWHP(**hp)
+    device = master.device
+    with torch.cuda.device(device):
+        check("fsdp_sharded_adamw", N.lib().fsdp_sharded_adamw(
+            ctypes.c_void_p(master.data_ptr()), ctypes.c_void_p(exp_avg.data_ptr()),
+            ctypes.c_void_p(exp_avg_sq.data_ptr()), ptr_array([g.data_ptr() for g in rank_grads]),
+            world, int(rank), dtype_code(gdt), int(bool(fp32_reduce)), ctypes.c_void_p(cptr),
+            cdt, S, ctypes.byref(hp), _stream(stream, device)))
+    return compute_shard
+
+
+def fsdp_unshard_gather(shards, full=None, stream=None):
+    """Concatenate the N compute shards into the full flat buffer (a shard already
+    at its slot of `full` is left in place)."""
+    shards = [_dev(s, "shards[%d]" % i) for i, s in enumerate(shards)]
+    if not shards:
+        raise ValueError("shards is empty")
+    world, S, dt = len(shards), shards[0].numel(), shards[0].dtype
+    for i, s in enumerate(shards):
+        if s.numel() != S or s.dtype != dt:
+            raise ValueError("shards[%d] must hold %d elements of %s" % (i, S, dt))
+    device = shards[0].device
+    if full is None:
+        full = torch.empty(world * S, dtype=dt, device=device)
+    _dev(full, "full")
+    if full.numel() != world * S or full.dtype != dt:
+        raise ValueError("full must hold %d elements of %s" % (world * S, dt))
+    _same_device(shards + [full])
+    with torch.cuda.device(device):
+        check("fsdp_unshard_gather", N.lib().fsdp_unshard_gather(
+            ptr_array([s.data_ptr() for s in shards]), world, S, dtype_code(dt),
+            ctypes.c_void_p(full.data_ptr()), _stream(stream, device)))
+    return full
+
+
+def fsdp_unflatten_views(full, shapes, materialize=False, stream=None):
+    """Per-tensor views of the full buffer (the padding belongs to none).  With
+    materialize=True each tensor is copied out into its own allocation."""
+    numels = []
+    for s in shapes:
+        n = 1
+        for x in s:
+            n *= int(x)
+        numels.append(n)
+    views = (View * max(len(numels), 1))()
+    if materialize:
+        _dev(full, "full")
+        outs = [torch.empty(n, dtype=full.dtype, device=full.device) for n in numels]
+        with torch.cuda.device(full.device):
+            check("fsdp_unflatten_views", N.lib().fsdp_unflatten_views(
+                i64_array(numels), len(numels), full.numel(), views, ctypes.c_void_p(full.data_ptr()),
+                dtype_code(full.dtype), ptr_array([o.data_ptr() for o in outs]),
+                _stream(stream, full.device)))
+        return [o.view(s) for o, s in zip(outs, shapes)]
+    check("fsdp_unflatten_views", N.lib().fsdp_unflatten_views(
+        i64_array(numels), len(numels), full.numel(), views, None, N.F32, None, None))
+    return [full.narrow(0, views[k].offset, views[k].numel).view(shapes[k]) for k in range(len(shapes))]
+
+
+def view_table(numels, padded_numel):
+    """[(offset, numel)] of each tensor (host only, no device work)."""
+    views = (View * max(len(numels), 1))()
+    check("fsdp_unflatten_views", N.lib().fsdp_unflatten_views(
+        i64_array(numels), len(numels), int(padded_numel), views, None, N.F32, None, None))
+    return [(views[k].offset, views[k].numel) for k in range(len(numels))]

@@ -1,0 +1,377 @@
+// fsdp_abi.cpp -- host layer of libfsdp_shard.so: argument validation, alias
+// checks, host-side scalars, launch geometry and error reporting for the C ABI
+// declared in include/fsdp_shard.h.  Every check runs before anything is
+// enqueued; a negative status means nothing was launched.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "fsdp_kernels.h"
+#include "fsdp_shard.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = 0;
+    return FSDP_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(FSDP_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_dtype(int dt) { return dt == FSDP_F32 || dt == FSDP_F16 || dt == FSDP_BF16; }
+int64_t dt_size(int dt) { return dt == FSDP_F32 ? 4 : 2; }
+
+// Byte range [lo, lo + n) of device memory.
+struct Range {
+    uintptr_t lo;
+    uint64_t n;
+};
+Range range(const void* p, int64_t elems, int64_t esize) {
+    return Range{(uintptr_t)p, (uint64_t)elems * (uint64_t)esize};
+}
+bool overlaps(Range a, Range b) {
+    if (a.n == 0 || b.n == 0) return false;
+    return a.lo < b.lo + b.n && b.lo < a.lo + a.n;
+}
+
+// Compute units of the current device (cached per device).
+std::atomic<int> g_cus[64];
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < 64) {
+        int c = g_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev >= 0 && dev < 64) g_cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+fsdp::ReduceScalars reduce_scalars(int world) {
+    fsdp::ReduceScalars r;
+    r.n = (float)world;
+    r.inv_n = (float)(1.0 / (double)world);
+    return r;
+}
+
+// AdamW constants: the per-element update uses these fp32 values.
+fsdp::AdamScalars adam_scalars(const fsdp_adamw_hp& hp) {
+    const double b1 = hp.beta1, b2 = hp.beta2, lr = hp.lr, t = (double)hp.step;
+    const double bias1 = 1.0 - std::pow(b1, t);
+    const double bias2 = 1.0 - std::pow(b2, t);
+    fsdp::AdamScalars s;
+    s.decay = (float)(1.0 - lr * (double)hp.weight_decay);
+    s.b1 = hp.beta1;
+    s.omb1 = 1.0f - hp.beta1;
+    s.b2 = hp.beta2;
+    s.omb2 = 1.0f - hp.beta2;
+    s.step_size = (float)(lr / bias1);
+    s.bc2_sqrt = (float)std::sqrt(bias2);
+    s.eps = hp.eps;
+    return s;
+}
+
+// Shared validation of the N gradient inputs; fills the block pointers.
+int check_grads(const void* const* rank_grads, int32_t world, int32_t rank, int64_t S, int grad_dt,
+                std::vector<const void*>& blocks, std::vector<Range>& in_ranges) {
+    if (world < 1 || world > FSDP_MAX_WORLD)
+        return fail(FSDP_E_INVAL, "world = %d outside [1, %d]", world, FSDP_MAX_WORLD);
+    if (rank < 0 || rank >= world) return fail(FSDP_E_INVAL, "rank = %d outside [0, %d)", rank, world);
+    if (S < 0) return fail(FSDP_E_INVAL, "shard_numel = %lld < 0", (long long)S);
+    if (!valid_dtype(grad_dt)) return fail(FSDP_E_DTYPE, "grad dtype %d unsupported", grad_dt);
+    if (S > 0 && !rank_grads) return fail(FSDP_E_INVAL, "rank_grads is NULL");
+    const int64_t g = dt_size(grad_dt);
+    blocks.resize(world);
+    for (int q = 0; q < world; ++q) {
+        const void* base = S > 0 ? rank_grads[q] : nullptr;
+        if (S > 0 && !base) return fail(FSDP_E_INVAL, "rank_grads[%d] is NULL", q);
+        blocks[q] = base ? (const char*)base + (int64_t)rank * S * g : nullptr;
+        in_ranges.push_back(range(blocks[q], S, g));
+    }
+    return FSDP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fsdp_abi_version(void) { return FSDP_ABI_VERSION; }
+
+const char* fsdp_last_error(void) { return g_err; }
+
+int fsdp_layout(const int64_t* numels, int32_t n_tensors, int32_t world, int64_t* numel_out,
+                int64_t* padded_numel_out, int64_t* shard_numel_out) {
+    if (world < 1) return fail(FSDP_E_INVAL, "world = %d < 1", world);
+    if (n_tensors < 0) return fail(FSDP_E_INVAL, "n_tensors = %d < 0", n_tensors);
+    if (n_tensors > 0 && !numels) return fail(FSDP_E_INVAL, "numels is NULL");
+    int64_t total = 0;
+    for (int32_t k = 0; k < n_tensors; ++k) {
+        if (numels[k] < 0) return fail(FSDP_E_INVAL, "numels[%d] < 0", k);
+        if (total > INT64_MAX / 16 - numels[k]) return fail(FSDP_E_SIZE, "unit too large");
+        total += numels[k];
+    }
+    const int64_t padded = (total + world - 1) / world * world;
+    if (numel_out) *numel_out = total;
+    if (padded_numel_out) *padded_numel_out = padded;
+    if (shard_numel_out) *shard_numel_out = padded / world;
+    return ok();
+}
+
+int fsdp_flatten_pad(const void* const* srcs, const int64_t* numels, int32_t n_tensors, fsdp_dtype dt,
+                     int32_t world, void* flat, int64_t flat_capacity, int64_t* padded_numel_out,
+                     void* stream) {
+    int64_t total = 0, padded = 0;
+    int rc = fsdp_layout(numels, n_tensors, world, &total, &padded, nullptr);
+    if (rc) return rc;
+    if (!valid_dtype(dt)) return fail(FSDP_E_DTYPE, "dtype %d unsupported", (int)dt);
+    if (flat_capacity < padded)
+        return fail(FSDP_E_SIZE, "flat_capacity %lld < padded numel %lld", (long long)flat_capacity,
+                    (long long)padded);
+    if (padded > 0 && !flat) return fail(FSDP_E_INVAL, "flat is NULL");
+    if (n_tensors > 0 && !srcs) return fail(FSDP_E_INVAL, "srcs is NULL");
+    const int64_t es = dt_size(dt);
+    const Range out = range(flat, padded, es);
+    for (int32_t k = 0; k < n_tensors; ++k) {
+        if (numels[k] > 0 && !srcs[k]) return fail(FSDP_E_INVAL, "srcs[%d] is NULL", k);
+        if (overlaps(range(srcs[k], numels[k], es), out))
+            return fail(FSDP_E_ALIAS, "srcs[%d] overlaps the flat buffer", k);
+    }
+    if (padded_numel_out) *padded_numel_out = padded;
+
+    // Segments: every non-empty tensor, then the zero tail; batched per launch.
+    fsdp::SegBatch b;
+    int nseg = 0;
+    int64_t chunks = 0;
+    auto flush = [&]() -> hipError_t {
+        if (nseg == 0) return hipSuccess;
+        b.count = nseg;
+        b.chunk_begin[nseg] = chunks;
+        hipError_t e = fsdp::launch_segments(b, chunks, stream);
+        nseg = 0;
+        chunks = 0;
+        return e;
+    };
+    auto add = [&](const void* src, void* dst, int64_t bytes) -> hipError_t {
+        if (bytes <= 0) return hipSuccess;
+        b.src[nseg] = (const char*)src;
+        b.dst[nseg] = (char*)dst;
+        b.bytes[nseg] = bytes;
+        b.chunk_begin[nseg] = chunks;
+        chunks += (bytes + fsdp::kSegChunkBytes - 1) / fsdp::kSegChunkBytes;
+        if (++nseg == fsdp::kSegMax) return flush();
+        return hipSuccess;
+    };
+    (void)hipGetLastError();
+    int64_t pos = 0;
+    for (int32_t k = 0; k < n_tensors; ++k) {
+        hipError_t e = add(srcs[k], (char*)flat + pos * es, numels[k] * es);
+        if (e != hipSuccess) return hip_fail(e, "flatten launch");
+        pos += numels[k];
+    }
+    hipError_t e = add(nullptr, (char*)flat + total * es, (padded - total) * es);
+    if (e == hipSuccess) e = flush();
+    if (e != hipSuccess) return hip_fail(e, "flatten launch");
+    return ok();
+}
+
+int fsdp_reduce_scatter_local(const void* const* rank_grads, int32_t world, int32_t rank,
+                              int64_t shard_numel, fsdp_dtype grad_dt, int32_t fp32_reduce,
+                              void* grad_shard_out, void* stream) {
+    std::vector<const void*> blocks;
+    std::vector<Range> ins;
+    int rc = check_grads(rank_grads, world, rank, shard_numel, grad_dt, blocks, ins);
+    if (rc) return rc;
+    const int out_dt = (fp32_reduce || grad_dt == FSDP_F32) ? FSDP_F32 : grad_dt;
+    if (shard_numel == 0) return ok();
+    if (!grad_shard_out) return fail(FSDP_E_INVAL, "grad_shard_out is NULL");
+    const Range out = range(grad_shard_out, shard_numel, dt_size(out_dt));
+    for (int q = 0; q < world; ++q)
+        if (overlaps(out, ins[q])) return fail(FSDP_E_ALIAS, "grad_shard_out overlaps rank_grads[%d]", q);
+
+    bool vec = aligned16(grad_shard_out);
+    for (int q = 0; q < world; ++q) vec = vec && aligned16(blocks[q]);
+    fsdp::FusedArgs a{};
+    a.grads = blocks.data();
+    a.world = world;
+    a.grad_dt = grad_dt;
+    a.fp32_reduce = fp32_reduce != 0;
+    a.compute_dt = out_dt;
+    a.S = shard_numel;
+    a.nvec = vec ? shard_numel / 8 : 0;
+    a.out = grad_shard_out;
+    a.rs = reduce_scalars(world);
+    a.cus = cu_count();
+    a.stream = stream;
+    (void)hipGetLastError();
+    hipError_t e = fsdp::launch_fused(a, false);
+    if (e != hipSuccess) return hip_fail(e, "reduce-scatter launch");
+    return ok();
+}
+
+int fsdp_sharded_adamw(float* master, float* exp_avg, float* exp_avg_sq, const void* const* rank_grads,
+                       int32_t world, int32_t rank, fsdp_dtype grad_dt, int32_t fp32_reduce,
+                       void* compute_shard, fsdp_dtype compute_dt, int64_t shard_numel,
+                       const fsdp_adamw_hp* hp, void* stream) {
+    std::vector<const void*> blocks;
+    std::vector<Range> ins;
+    int rc = check_grads(rank_grads, world, rank, shard_numel, grad_dt, blocks, ins);
+    if (rc) return rc;
+    if (!valid_dtype(compute_dt)) return fail(FSDP_E_DTYPE, "compute dtype %d unsupported", (int)compute_dt);
+    if (!hp) return fail(FSDP_E_INVAL, "hp is NULL");
+    if (hp->step < 1) return fail(FSDP_E_INVAL, "hp->step = %lld < 1", (long long)hp->step);
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+        return fail(FSDP_E_INVAL, "betas must lie in [0, 1)");
+    if (shard_numel == 0) return ok();
+    if (!master || !exp_avg || !exp_avg_sq)
+        return fail(FSDP_E_INVAL, "master, exp_avg and exp_avg_sq must be non-NULL");
+    const Range outs[4] = {range(master, shard_numel, 4), range(exp_avg, shard_numel, 4),
+                           range(exp_avg_sq, shard_numel, 4),
+                           range(compute_shard, compute_shard ? shard_numel : 0, dt_size(compute_dt))};
+    const char* names[4] = {"master", "exp_avg", "exp_avg_sq", "compute_shard"};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outs[j])) return fail(FSDP_E_ALIAS, "%s overlaps %s", names[i], names[j]);
+        for (int q = 0; q < world; ++q)
+            if (overlaps(outs[i], ins[q]))
+                return fail(FSDP_E_ALIAS, "%s overlaps the block of rank_grads[%d]", names[i], q);
+    }
+
+    bool vec = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) &&
+               (!compute_shard || aligned16(compute_shard));
+    for (int q = 0; q < world; ++q) vec = vec && aligned16(blocks[q]);
+    fsdp::FusedArgs a{};
+    a.grads = blocks.data();
+    a.world = world;
+    a.grad_dt = grad_dt;
+    a.fp32_reduce = fp32_reduce != 0;
+    a.compute_dt = compute_dt;
+    a.S = shard_numel;
+    a.nvec = vec ? shard_numel / 8 : 0;
+    a.p = master;
+    a.m = exp_avg;
+    a.v = exp_avg_sq;
+    a.out = compute_shard;
+    a.rs = reduce_scalars(world);
+    a.as = adam_scalars(*hp);
+    a.cus = cu_count();
+    a.stream = stream;
+    (void)hipGetLastError();
+    hipError_t e = fsdp::launch_fused(a, true);
+    if (e != hipSuccess) return hip_fail(e, "sharded AdamW launch");
+    return ok();
+}
+
+int fsdp_unshard_gather(const void* const* shards, int32_t world, int64_t shard_numel, fsdp_dtype dt,
+                        void* full_out, void* stream) {
+    if (world < 1 || world > FSDP_MAX_WORLD)
+        return fail(FSDP_E_INVAL, "world = %d outside [1, %d]", world, FSDP_MAX_WORLD);
+    if (shard_numel < 0) return fail(FSDP_E_INVAL, "shard_numel = %lld < 0", (long long)shard_numel);
+    if (!valid_dtype(dt)) return fail(FSDP_E_DTYPE, "dtype %d unsupported", (int)dt);
+    if (shard_numel == 0) return ok();
+    if (!shards) return fail(FSDP_E_INVAL, "shards is NULL");
+    if (!full_out) return fail(FSDP_E_INVAL, "full_out is NULL");
+    const int64_t es = dt_size(dt);
+    const int64_t bytes = shard_numel * es;
+    const Range full = range(full_out, (int64_t)world * shard_numel, es);
+    std::vector<const void*> src;
+    std::vector<void*> dst;
+    for (int q = 0; q < world; ++q) {
+        if (!shards[q]) return fail(FSDP_E_INVAL, "shards[%d] is NULL", q);
+        char* slot = (char*)full_out + (int64_t)q * bytes;
+        if (shards[q] == slot) continue;  // already in place
+        if (overlaps(range(shards[q], shard_numel, es), full))
+            return fail(FSDP_E_ALIAS, "shards[%d] overlaps full_out outside its own slot", q);
+        src.push_back(shards[q]);
+        dst.push_back(slot);
+    }
+    (void)hipGetLastError();
+    hipError_t e = fsdp::launch_gather(src.data(), dst.data(), (int)src.size(), bytes, cu_count(), stream);
+    if (e != hipSuccess) return hip_fail(e, "gather launch");
+    return ok();
+}
+
+int fsdp_unflatten_views(const int64_t* numels, int32_t n_tensors, int64_t padded_numel,
+                         fsdp_view* views_out, const void* full, fsdp_dtype dt, void* const* dsts,
+                         void* stream) {
+    int64_t total = 0;
+    int rc = fsdp_layout(numels, n_tensors, 1, &total, nullptr, nullptr);
+    if (rc) return rc;
+    if (total > padded_numel)
+        return fail(FSDP_E_SIZE, "tensors hold %lld elements, more than padded_numel %lld",
+                    (long long)total, (long long)padded_numel);
+    if (n_tensors > 0 && !views_out) return fail(FSDP_E_INVAL, "views_out is NULL");
+    if (dsts) {
+        if (!valid_dtype(dt)) return fail(FSDP_E_DTYPE, "dtype %d unsupported", (int)dt);
+        if (total > 0 && !full) return fail(FSDP_E_INVAL, "full is NULL");
+        const int64_t es = dt_size(dt);
+        const Range in = range(full, padded_numel, es);
+        std::vector<Range> outs;
+        for (int32_t k = 0; k < n_tensors; ++k) {
+            if (numels[k] > 0 && !dsts[k]) return fail(FSDP_E_INVAL, "dsts[%d] is NULL", k);
+            Range r = range(dsts[k], numels[k], es);
+            if (overlaps(r, in)) return fail(FSDP_E_ALIAS, "dsts[%d] overlaps the full buffer", k);
+            for (size_t j = 0; j < outs.size(); ++j)
+                if (overlaps(r, outs[j])) return fail(FSDP_E_ALIAS, "dsts[%d] overlaps another output", k);
+            outs.push_back(r);
+        }
+    }
+    int64_t off = 0;
+    for (int32_t k = 0; k < n_tensors; ++k) {
+        views_out[k].offset = off;
+        views_out[k].numel = numels[k];
+        off += numels[k];
+    }
+    if (!dsts) return ok();
+
+    const int64_t es = dt_size(dt);
+    fsdp::SegBatch b;
+    int nseg = 0;
+    int64_t chunks = 0;
+    (void)hipGetLastError();
+    for (int32_t k = 0; k <= n_tensors; ++k) {
+        const bool last = k == n_tensors;
+        if (!last && numels[k] > 0) {
+            const int64_t bytes = numels[k] * es;
+            b.src[nseg] = (const char*)full + views_out[k].offset * es;
+            b.dst[nseg] = (char*)dsts[k];
+            b.bytes[nseg] = bytes;
+            b.chunk_begin[nseg] = chunks;
+            chunks += (bytes + fsdp::kSegChunkBytes - 1) / fsdp::kSegChunkBytes;
+            ++nseg;
+        }
+        if (nseg > 0 && (nseg == fsdp::kSegMax || last)) {
+            b.count = nseg;
+            b.chunk_begin[nseg] = chunks;
+            hipError_t e = fsdp::launch_segments(b, chunks, stream);
+            if (e != hipSuccess) return hip_fail(e, "unflatten launch");
+            nseg = 0;
+            chunks = 0;
+        }
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,390 @@
+// fsdp_kernels.hip -- gfx950 (CDNA4) kernels of the FSDP flat-parameter shard
+// pipeline.  Every kernel is an HBM stream: no contraction, so no MFMA.
+//
+// Design (MI355X, 256 CUs in 8 XCDs, 64-wide waves, HBM3E ~8 TB/s):
+//  * 16-byte (dwordx4) global loads/stores per lane; a lane owns 8 consecutive
+//    elements of the shard per step (one dwordx4 of 16-bit data, two of fp32);
+//  * grid-stride loops over a grid sized to a multiple of the CU count, so a
+//    launch is a few thousand workgroups regardless of the unit size;
+//  * the N simulated ranks' gradient blocks are accumulated in registers, all N
+//    loads issued before the first add (N is a template parameter for
+//    N in {1, 2, 4, 8});
+//  * reduce-scatter + AdamW + cast run in one pass over the shard (one read of
+//    N gradient blocks and master/m/v, one write of master/m/v and the compute
+//    copy);
+//  * arithmetic matches the definition bit for bit: no FMA contraction,
+//    correctly rounded divide and sqrt, fp32 subnormals preserved.
+//
+// Sources: "Fully Sharded Data Parallel: faster AI training with fewer GPUs"
+// (techreport.ngo) -- figure on all-reduce as reduce-scatter + all-gather,
+// section "From all-reduce to sharded parameters"; "Data Parallelism"
+// (vanos001 notes) -- section "The Basic Protocol"; "FSDP (Fully Sharded Data
+// Parallel)" (vanos001 notes) -- sections "The Per-Layer Communication" and
+// "Mixed Precision and FSDP"; "fairseq 中的 Fully Sharded Data Parallel (FSDP)
+// 实战指南" (zskr.cn) -- flag table (--fp32-reduce-scatter) and "工作原理".
+
+#include "fsdp_kernels.h"
+
+#include <hip/hip_runtime.h>
+
+#pragma clang fp contract(off)
+
+namespace fsdp {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ----------------------------------------------------------------- formats
+template <int F> __device__ __forceinline__ float to_f32(uint32_t bits);
+template <> __device__ __forceinline__ float to_f32<FSDP_F32>(uint32_t bits) { return __uint_as_float(bits); }
+template <> __device__ __forceinline__ float to_f32<FSDP_F16>(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);      // exact
+}
+template <> __device__ __forceinline__ float to_f32<FSDP_BF16>(uint32_t bits) {
+    return __uint_as_float(bits << 16);                                // exact
+}
+
+template <int F> __device__ __forceinline__ uint32_t from_f32(float x);
+template <> __device__ __forceinline__ uint32_t from_f32<FSDP_F32>(float x) { return __float_as_uint(x); }
+template <> __device__ __forceinline__ uint32_t from_f32<FSDP_F16>(float x) {
+    // v_cvt_f16_f32: round to nearest even, binary16 subnormals kept
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+template <> __device__ __forceinline__ uint32_t from_f32<FSDP_BF16>(float x) {
+    // Round the fp32 encoding at bit 16, ties to even; NaN stays a quiet NaN.
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int F> __device__ __forceinline__ float round_to(float x) { return to_f32<F>(from_f32<F>(x)); }
+
+// 8 consecutive elements of format F starting at element 8*vi (16-byte aligned).
+template <int F>
+__device__ __forceinline__ void load8(const void* __restrict__ base, int64_t vi, float (&x)[8]) {
+    if constexpr (F == FSDP_F32) {
+        const u32x4* q = reinterpret_cast<const u32x4*>(base) + 2 * vi;
+        u32x4 a = q[0], b = q[1];
+        x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
+        x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+        x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
+        x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
+    } else {
+        u32x4 a = reinterpret_cast<const u32x4*>(base)[vi];
+        uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[2 * k] = to_f32<F>(w[k] & 0xffffu);
+            x[2 * k + 1] = to_f32<F>(w[k] >> 16);
+        }
+    }
+}
+
+template <int F>
+__device__ __forceinline__ void store8(void* __restrict__ base, int64_t vi, const float (&x)[8]) {
+    if constexpr (F == FSDP_F32) {
+        u32x4* q = reinterpret_cast<u32x4*>(base) + 2 * vi;
+        u32x4 a, b;
+        a.x = __float_as_uint(x[0]); a.y = __float_as_uint(x[1]);
+        a.z = __float_as_uint(x[2]); a.w = __float_as_uint(x[3]);
+        b.x = __float_as_uint(x[4]); b.y = __float_as_uint(x[5]);
+        b.z = __float_as_uint(x[6]); b.w = __float_as_uint(x[7]);
+        q[0] = a;
+        q[1] = b;
+    } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = from_f32<F>(x[2 * k]) | (from_f32<F>(x[2 * k + 1]) << 16);
+        u32x4 a;
+        a.x = w[0]; a.y = w[1]; a.z = w[2]; a.w = w[3];
+        reinterpret_cast<u32x4*>(base)[vi] = a;
+    }
+}
+
+template <int F>
+__device__ __forceinline__ float load1(const void* __restrict__ base, int64_t i) {
+    if constexpr (F == FSDP_F32) return reinterpret_cast<const float*>(base)[i];
+    else return to_f32<F>(reinterpret_cast<const uint16_t*>(base)[i]);
+}
+
+template <int F>
+__device__ __forceinline__ void store1(void* __restrict__ base, int64_t i, float x) {
+    if constexpr (F == FSDP_F32) reinterpret_cast<float*>(base)[i] = x;
+    else reinterpret_cast<uint16_t*>(base)[i] = (uint16_t)from_f32<F>(x);
+}
+
+// ----------------------------------------------------------------- reduction
+// One step of the left fold over ranks.  fp32 mode: a single fp32 add.
+// 16-bit mode: the sum rounded back to the gradient format.
+template <int GF, bool FP32R>
+__device__ __forceinline__ float fold(float acc, float x) {
+    if constexpr (FP32R || GF == FSDP_F32) return acc + x;
+    else return round_to<GF>(acc + x);
+}
+
+// acc / N.  The specialised kernels (N in {1, 2, 4, 8}) multiply by 1/N: for a
+// power of two that product is the same correctly rounded value as the
+// quotient.  The generic kernel divides.  In 16-bit mode the quotient is then
+// rounded to the gradient format.
+template <int NW, int GF, bool FP32R>
+__device__ __forceinline__ float finish(float acc, const ReduceScalars& r) {
+    static_assert(NW == 0 || (NW & (NW - 1)) == 0, "specialised world sizes are powers of two");
+    float q = NW > 0 ? acc * r.inv_n : acc / r.n;
+    if constexpr (FP32R || GF == FSDP_F32) return q;
+    else return round_to<GF>(q);
+}
+
+// ----------------------------------------------------------------- AdamW
+__device__ __forceinline__ void adamw1(float g, float& p, float& m, float& v, const AdamScalars& s) {
+    float p1 = p * s.decay;
+    float m1 = (s.b1 * m) + (s.omb1 * g);
+    float v1 = (s.b2 * v) + (s.omb2 * (g * g));
+    float den = (__builtin_sqrtf(v1) / s.bc2_sqrt) + s.eps;
+    float p2 = p1 - (s.step_size * (m1 / den));
+    p = p2;
+    m = m1;
+    v = v1;
+}
+
+// Accumulate the N rank blocks of 8 elements into acc (all loads first).
+template <int NW, int GF, bool FP32R>
+__device__ __forceinline__ void reduce8(const GradPtrs<NW>& g, int world, int64_t vi, float (&acc)[8]) {
+    if constexpr (NW > 0) {
+        float x[NW][8];
+#pragma unroll
+        for (int q = 0; q < NW; ++q) load8<GF>(g.p[q], vi, x[q]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = x[0][k];
+#pragma unroll
+        for (int q = 1; q < NW; ++q)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = fold<GF, FP32R>(acc[k], x[q][k]);
+    } else {
+        load8<GF>(g.p[0], vi, acc);
+        int q = 1;
+        for (; q + 4 <= world; q += 4) {
+            float x[4][8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) load8<GF>(g.p[q + j], vi, x[j]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] = fold<GF, FP32R>(acc[k], x[j][k]);
+        }
+        for (; q < world; ++q) {
+            float x[8];
+            load8<GF>(g.p[q], vi, x);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = fold<GF, FP32R>(acc[k], x[k]);
+        }
+    }
+}
+
+template <int NW, int GF, bool FP32R>
+__device__ __forceinline__ float reduce1(const GradPtrs<NW>& g, int world, int64_t i) {
+    constexpr int kN = NW > 0 ? NW : 1;
+    float acc = load1<GF>(g.p[0], i);
+    const int n = NW > 0 ? kN : world;
+    for (int q = 1; q < n; ++q) acc = fold<GF, FP32R>(acc, load1<GF>(g.p[q], i));
+    return acc;
+}
+
+// ----------------------------------------------------------------- kernels
+// Fused reduce-scatter + AdamW + cast over one shard of S elements.
+// g.p[q] points at element 0 of rank q's block `rank` (shard-relative).
+// Elements [0, 8*nvec) take the vector path, [8*nvec, S) the scalar path.
+template <int NW, int GF, bool FP32R, int CF>
+__global__ __launch_bounds__(kThreads) void k_rs_adamw_cast(
+    GradPtrs<NW> g, int world, int64_t S, int64_t nvec, float* __restrict__ p,
+    float* __restrict__ m, float* __restrict__ v, void* __restrict__ out, ReduceScalars rs,
+    AdamScalars as) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (int64_t vi = t0; vi < nvec; vi += stride) {
+        float acc[8], pp[8], mm[8], vv[8];
+        reduce8<NW, GF, FP32R>(g, world, vi, acc);
+        load8<FSDP_F32>(p, vi, pp);
+        load8<FSDP_F32>(m, vi, mm);
+        load8<FSDP_F32>(v, vi, vv);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) adamw1(finish<NW, GF, FP32R>(acc[k], rs), pp[k], mm[k], vv[k], as);
+        store8<FSDP_F32>(p, vi, pp);
+        store8<FSDP_F32>(m, vi, mm);
+        store8<FSDP_F32>(v, vi, vv);
+        if (out) store8<CF>(out, vi, pp);
+    }
+    for (int64_t i = nvec * 8 + t0; i < S; i += stride) {
+        float pp = p[i], mm = m[i], vv = v[i];
+        adamw1(finish<NW, GF, FP32R>(reduce1<NW, GF, FP32R>(g, world, i), rs), pp, mm, vv, as);
+        p[i] = pp;
+        m[i] = mm;
+        v[i] = vv;
+        if (out) store1<CF>(out, i, pp);
+    }
+}
+
+// Reduce-scatter alone: averaged gradient shard in fp32 (fp32 mode) or in the
+// gradient format (16-bit mode).
+template <int NW, int GF, bool FP32R>
+__global__ __launch_bounds__(kThreads) void k_reduce_scatter(
+    GradPtrs<NW> g, int world, int64_t S, int64_t nvec, void* __restrict__ out, ReduceScalars rs) {
+    constexpr int OF = (FP32R || GF == FSDP_F32) ? FSDP_F32 : GF;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (int64_t vi = t0; vi < nvec; vi += stride) {
+        float acc[8];
+        reduce8<NW, GF, FP32R>(g, world, vi, acc);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = finish<NW, GF, FP32R>(acc[k], rs);
+        store8<OF>(out, vi, acc);
+    }
+    for (int64_t i = nvec * 8 + t0; i < S; i += stride)
+        store1<OF>(out, i, finish<NW, GF, FP32R>(reduce1<NW, GF, FP32R>(g, world, i), rs));
+}
+
+// Copy `bytes` bytes from src to dst (or write zeros when src is null) with the
+// widest access both addresses allow.  Called by every lane of a range of
+// `nthreads` lanes, lane index `lane`.
+__device__ __forceinline__ void copy_range(char* __restrict__ dst, const char* __restrict__ src,
+                                           int64_t bytes, int64_t lane, int64_t nthreads) {
+    const uintptr_t a = (uintptr_t)dst | (src ? (uintptr_t)src : 0);
+    if ((a & 15) == 0) {
+        const int64_t nv = bytes >> 4;
+        u32x4* d = reinterpret_cast<u32x4*>(dst);
+        const u32x4* s = reinterpret_cast<const u32x4*>(src);
+        if (src) {
+            for (int64_t i = lane; i < nv; i += nthreads) d[i] = s[i];
+        } else {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            for (int64_t i = lane; i < nv; i += nthreads) d[i] = z;
+        }
+        for (int64_t i = (nv << 4) + lane; i < bytes; i += nthreads) dst[i] = src ? src[i] : 0;
+    } else if ((a & 3) == 0) {
+        const int64_t nw = bytes >> 2;
+        uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+        const uint32_t* s = reinterpret_cast<const uint32_t*>(src);
+        for (int64_t i = lane; i < nw; i += nthreads) d[i] = src ? s[i] : 0u;
+        for (int64_t i = (nw << 2) + lane; i < bytes; i += nthreads) dst[i] = src ? src[i] : 0;
+    } else if ((a & 1) == 0) {
+        const int64_t nh = bytes >> 1;
+        uint16_t* d = reinterpret_cast<uint16_t*>(dst);
+        const uint16_t* s = reinterpret_cast<const uint16_t*>(src);
+        for (int64_t i = lane; i < nh; i += nthreads) d[i] = src ? s[i] : (uint16_t)0;
+        for (int64_t i = (nh << 1) + lane; i < bytes; i += nthreads) dst[i] = src ? src[i] : 0;
+    } else {
+        for (int64_t i = lane; i < bytes; i += nthreads) dst[i] = src ? src[i] : 0;
+    }
+}
+
+// All-gather unshard: copy j of the list moves `bytes` bytes src[j] -> dst[j].
+// blockIdx.y selects the copy; blocks along x stride over its bytes.
+template <int MAXN>
+__global__ __launch_bounds__(kThreads) void k_gather(CopyList<MAXN> L, int64_t bytes) {
+    const int j = blockIdx.y;
+    copy_range(L.dst[j], L.src[j], bytes, (int64_t)blockIdx.x * kThreads + threadIdx.x,
+               (int64_t)gridDim.x * kThreads);
+}
+
+// Segmented copy for flatten/unflatten: workgroup b handles chunk b of the
+// batch; segment k owns chunks [chunk_begin[k], chunk_begin[k+1]).
+__global__ __launch_bounds__(kThreads) void k_segments(SegBatch B) {
+    const int64_t c = blockIdx.x;
+    int lo = 0, hi = B.count - 1;          // find k with chunk_begin[k] <= c < chunk_begin[k+1]
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (B.chunk_begin[mid] <= c) lo = mid;
+        else hi = mid - 1;
+    }
+    const int k = lo;
+    const int64_t start = (c - B.chunk_begin[k]) * kSegChunkBytes;
+    int64_t n = B.bytes[k] - start;
+    if (n > kSegChunkBytes) n = kSegChunkBytes;
+    if (n <= 0) return;
+    copy_range(B.dst[k] + start, B.src[k] ? B.src[k] + start : nullptr, n, threadIdx.x, kThreads);
+}
+
+// ----------------------------------------------------------------- launchers
+static int64_t grid_for(int64_t work, int cus) {
+    int64_t want = (work + kThreads - 1) / kThreads;
+    int64_t cap = (int64_t)cus * kBlocksPerCU;
+    if (want > cap) want = cap;
+    return want < 1 ? 1 : want;
+}
+
+template <int NW, int GF, bool FP32R>
+static hipError_t fused_cf(const FusedArgs& a, const GradPtrs<NW>& g) {
+    const int64_t work = a.nvec > 0 ? a.nvec : a.S;
+    dim3 grid((unsigned)grid_for(work, a.cus));
+    hipStream_t st = (hipStream_t)a.stream;
+    switch (a.compute_dt) {
+    case FSDP_F32:
+        k_rs_adamw_cast<NW, GF, FP32R, FSDP_F32><<<grid, kThreads, 0, st>>>(g, a.world, a.S, a.nvec, a.p, a.m, a.v, a.out, a.rs, a.as);
+        break;
+    case FSDP_F16:
+        k_rs_adamw_cast<NW, GF, FP32R, FSDP_F16><<<grid, kThreads, 0, st>>>(g, a.world, a.S, a.nvec, a.p, a.m, a.v, a.out, a.rs, a.as);
+        break;
+    default:
+        k_rs_adamw_cast<NW, GF, FP32R, FSDP_BF16><<<grid, kThreads, 0, st>>>(g, a.world, a.S, a.nvec, a.p, a.m, a.v, a.out, a.rs, a.as);
+        break;
+    }
+    return hipGetLastError();
+}
+
+template <int NW, int GF, bool FP32R>
+static hipError_t rs_only(const FusedArgs& a, const GradPtrs<NW>& g) {
+    const int64_t work = a.nvec > 0 ? a.nvec : a.S;
+    dim3 grid((unsigned)grid_for(work, a.cus));
+    k_reduce_scatter<NW, GF, FP32R><<<grid, kThreads, 0, (hipStream_t)a.stream>>>(g, a.world, a.S, a.nvec, a.out, a.rs);
+    return hipGetLastError();
+}
+
+template <int NW>
+static hipError_t dispatch_grad(const FusedArgs& a, bool fused) {
+    GradPtrs<NW> g;
+    const int n = NW > 0 ? NW : a.world;
+    for (int q = 0; q < n; ++q) g.p[q] = a.grads[q];
+    const bool f32r = a.fp32_reduce || a.grad_dt == FSDP_F32;
+#define FSDP_GO(GF, R) return fused ? fused_cf<NW, GF, R>(a, g) : rs_only<NW, GF, R>(a, g)
+    if (a.grad_dt == FSDP_F32) FSDP_GO(FSDP_F32, true);
+    if (a.grad_dt == FSDP_F16) { if (f32r) FSDP_GO(FSDP_F16, true); FSDP_GO(FSDP_F16, false); }
+    if (f32r) FSDP_GO(FSDP_BF16, true);
+    FSDP_GO(FSDP_BF16, false);
+#undef FSDP_GO
+}
+
+hipError_t launch_fused(const FusedArgs& a, bool fused) {
+    switch (a.world) {
+    case 1: return dispatch_grad<1>(a, fused);
+    case 2: return dispatch_grad<2>(a, fused);
+    case 4: return dispatch_grad<4>(a, fused);
+    case 8: return dispatch_grad<8>(a, fused);
+    default: return dispatch_grad<0>(a, fused);
+    }
+}
+
+hipError_t launch_gather(const void* const* srcs, void* const* dsts, int n, int64_t bytes, int cus,
+                         void* stream) {
+    if (n <= 0 || bytes <= 0) return hipSuccess;
+    int64_t per = (bytes / 16 + kThreads - 1) / kThreads;
+    int64_t cap = ((int64_t)cus * kBlocksPerCU + n - 1) / n;
+    if (per > cap) per = cap;
+    if (per < 1) per = 1;
+    dim3 grid((unsigned)per, (unsigned)n);
+    if (n <= 8) {
+        CopyList<8> L;
+        for (int j = 0; j < n; ++j) { L.src[j] = (const char*)srcs[j]; L.dst[j] = (char*)dsts[j]; }
+        k_gather<8><<<grid, kThreads, 0, (hipStream_t)stream>>>(L, bytes);
+    } else {
+        CopyList<FSDP_MAX_WORLD> L;
+        for (int j = 0; j < n; ++j) { L.src[j] = (const char*)srcs[j]; L.dst[j] = (char*)dsts[j]; }
+        k_gather<FSDP_MAX_WORLD><<<grid, kThreads, 0, (hipStream_t)stream>>>(L, bytes);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_segments(const SegBatch& b, int64_t chunks, void* stream) {
+    if (chunks <= 0) return hipSuccess;
+    k_segments<<<dim3((unsigned)chunks), kThreads, 0, (hipStream_t)stream>>>(b);
+    return hipGetLastError();
+}
+
+}  // namespace fsdp

@@ -1,0 +1,109 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+symbol the header declares, and its host-only paths work -- layout sizes, the
+view table, and argument validation, which runs before anything touches the
+device (fake, never-dereferenced pointers are enough to reach every check)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sharded_state_amd as ss
+from sharded_state_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", f)).read()
+            names += re.findall(r"FSDP_API\s+[\w\s\*]+?\b(fsdp_\w+)\s*\(", txt)
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 8, names
+    L = N.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.fsdp_abi_version() == N.ABI_VERSION
+
+
+def test_layout_matches_oracle(orc):
+    rng = np.random.default_rng(0)
+    for _ in range(50):
+        k = int(rng.integers(1, 12))
+        numels = [int(x) for x in rng.integers(0, 5000, size=k)]
+        world = int(rng.integers(1, 9))
+        P, Pp, S = ss.fsdp_layout(numels, world)
+        assert P == sum(numels) and Pp == orc.padded_numel(P, world) and S * world == Pp
+        table = ss.view_table(numels, Pp)
+        assert [o for o, _ in table] == list(orc.offsets(numels)) and [n for _, n in table] == numels
+
+
+FAKE = 1 << 40   # device-looking addresses, never dereferenced: validation fails first
+
+
+def _adamw(master, m, v, grads, world, rank, gdt=N.F16, cdt=N.F16, S=1000, step=1, out=FAKE + (1 << 32)):
+    hp = N.AdamWHP(step=step)
+    return N.lib().fsdp_sharded_adamw(ctypes.c_void_p(master), ctypes.c_void_p(m), ctypes.c_void_p(v),
+                                      N.ptr_array(grads), world, rank, gdt, 1, ctypes.c_void_p(out),
+                                      cdt, S, ctypes.byref(hp), None)
+
+
+def test_validation_errors_before_any_launch():
+    L = N.lib()
+    g = [FAKE + (1 << 36), FAKE + (2 << 36)]
+    a, b, c = FAKE, FAKE + (1 << 30), FAKE + (2 << 30)
+    assert _adamw(a, b, c, g, 0, 0) == N.E_INVAL
+    assert _adamw(a, b, c, g, 2, 2) == N.E_INVAL
+    assert _adamw(a, b, c, g, 2, -1) == N.E_INVAL
+    assert _adamw(a, b, c, g, 2, 0, gdt=7) == N.E_DTYPE
+    assert _adamw(a, b, c, g, 2, 0, cdt=9) == N.E_DTYPE
+    assert _adamw(a, b, c, g, 2, 0, step=0) == N.E_INVAL
+    assert _adamw(a, a + 100, c, g, 2, 0) == N.E_ALIAS          # master overlaps exp_avg
+    assert _adamw(a, b, c, [a, g[1]], 2, 0) == N.E_ALIAS        # grad block overlaps master
+    assert _adamw(a, b, c, g, 2, 0, out=c + 3996) == N.E_ALIAS  # compute overlaps exp_avg_sq
+    assert _adamw(0, b, c, g, 2, 0) == N.E_INVAL
+    assert _adamw(a, b, c, [g[0], 0], 2, 0) == N.E_INVAL
+    assert _adamw(a, b, c, g * 65, 130, 0) == N.E_INVAL          # world above the maximum
+    msg = L.fsdp_last_error().decode()
+    assert "world" in msg
+    # reduce-scatter: output overlapping an input block
+    rc = L.fsdp_reduce_scatter_local(N.ptr_array(g), 2, 1, 1000, N.F16, 0,
+                                     ctypes.c_void_p(g[0] + 2000), None)
+    assert rc == N.E_ALIAS
+    # gather: a shard overlapping the output outside its own slot
+    full = FAKE
+    rc = L.fsdp_unshard_gather(N.ptr_array([full + 2000, FAKE + (1 << 33)]), 2, 1000, N.F16,
+                               ctypes.c_void_p(full), None)
+    assert rc == N.E_ALIAS
+    # flatten: capacity too small, source overlapping the flat buffer
+    rc = L.fsdp_flatten_pad(N.ptr_array([FAKE + (1 << 33)]), N.i64_array([10]), 1, N.F32, 4,
+                            ctypes.c_void_p(FAKE), 11, None, None)
+    assert rc == N.E_SIZE
+    rc = L.fsdp_flatten_pad(N.ptr_array([FAKE + 8]), N.i64_array([10]), 1, N.F32, 4,
+                            ctypes.c_void_p(FAKE), 12, None, None)
+    assert rc == N.E_ALIAS
+    # unflatten: more elements than the buffer
+    views = (N.View * 2)()
+    rc = L.fsdp_unflatten_views(N.i64_array([5, 6]), 2, 10, views, None, N.F32, None, None)
+    assert rc == N.E_SIZE
+
+
+def test_empty_shard_is_a_no_op_without_device_work():
+    """shard_numel == 0 returns OK after validation, before any HIP call."""
+    assert _adamw(0, 0, 0, [0, 0], 2, 1, S=0, out=0) == N.OK
+    L = N.lib()
+    assert L.fsdp_reduce_scatter_local(N.ptr_array([0, 0]), 2, 0, 0, N.BF16, 0, None, None) == N.OK
+    assert L.fsdp_unshard_gather(N.ptr_array([0]), 1, 0, N.F16, None, None) == N.OK
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        ss.fsdp_unshard_gather([torch.zeros(4)])

@@ -1,0 +1,146 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by
+element, on seeded inputs with the dtypes and distributions of each workload,
+at sizes the oracle finishes in seconds that still span many workgroups and a
+ragged last tile; plus padding, unaligned and degenerate cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sharded_state_amd as ss
+from parity import (UnitRun, assert_bitexact, assert_rel, assert_ulp16, compare_compute, np_of)
+from workloads import CONFIGS, gpt2_model, gpt_block, llama_block, scaled
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases():
+    C = CONFIGS
+    return {
+        "tiny": C["tiny"],                                                  # full size
+        "gpt2-large-d96": scaled(C["gpt2-large-block"], gpt_block(96)),
+        "gpt2-xl-d64": scaled(C["gpt2-xl-model"], gpt2_model(64, 2, 1000, 64)),
+        "gpt3-13b-d128": scaled(C["gpt3-13b-block"], gpt_block(128)),
+        "gpt3-13b-d80-unaligned": scaled(C["gpt3-13b-block"], gpt_block(80)),
+        "llama70b-d64": scaled(C["llama70b-block"], llama_block(64, 80, 224)),
+    }
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_unit_matches_oracle(name):
+    print("case", name, flush=True)
+    run = UnitRun(CASES[name])
+    run.run_gpu()
+    run.run_oracle()
+    run.compare()
+
+
+@pytest.mark.parametrize("P,world", [(1, 8), (7, 2), (9, 8), (9, 3), (1_000_001, 2),
+                                     (1_000_001, 3), (1_000_001, 7), (4099, 1), (12345, 16)])
+@pytest.mark.parametrize("base", ["gpt2-large-block", "llama70b-block"])
+def test_padding_and_odd_world_sizes(P, world, base):
+    print("case", base, P, world, flush=True)
+    split = [P // 3, P - P // 3 - P // 5, P // 5]
+    tensors = [("t%d" % i, (n,)) for i, n in enumerate(split) if n > 0]
+    cfg = scaled(CONFIGS[base], tensors, world=world)
+    run = UnitRun(cfg)
+    run.run_gpu()
+    run.run_oracle()
+    run.compare()
+    pad = run.Pp - run.P
+    assert not np.any(np_of(run.master)[run.P:].view(np.uint32))
+    assert pad == oracle.padded_numel(P, world) - P
+
+
+@pytest.mark.parametrize("step", [1, 10, 1000])
+def test_later_steps(step):
+    run = UnitRun(scaled(CONFIGS["gpt2-xl-model"], gpt_block(64)))
+    run.run_gpu(step)
+    run.run_oracle(step)
+    run.compare()
+
+
+def test_unaligned_buffers_take_the_scalar_path():
+    """Views offset by one element defeat 16-byte alignment; results are the same."""
+    g = torch.Generator().manual_seed(5)
+    S, world = 5003, 2
+    grads = [(torch.randn(world * S + 1, generator=g) * 1e-4).half().cuda() for _ in range(world)]
+    gv = [x[1:] for x in grads]
+    master = (torch.randn(S + 1, generator=g) * 0.02).cuda()
+    m = torch.zeros(S + 1, device="cuda")
+    v = torch.zeros(S + 1, device="cuda")
+    out = torch.empty(S + 1, dtype=torch.float16, device="cuda")
+    hp = ss.AdamWHP()
+    p0 = np_of(master[1:])
+    ss.fsdp_sharded_adamw(master[1:], m[1:], v[1:], gv, 1, True, hp, compute_shard=out[1:])
+    torch.cuda.synchronize()
+    gn = [np_of(x) for x in gv]
+    p, mm, vv = p0.copy(), np.zeros(S, np.float32), np.zeros(S, np.float32)
+    _, c = oracle.rank_step(gn, 1, p, mm, vv, oracle.hp(), "f16", True, "f16")
+    assert_bitexact(np_of(master[1:]), p, "master")
+    assert_bitexact(np_of(out[1:]), c, "compute")
+    rs = ss.fsdp_reduce_scatter_local(gv, 1, False, out=torch.empty(S + 1, dtype=torch.float16,
+                                                                    device="cuda")[1:], shard_numel=S)
+    assert_bitexact(np_of(rs), oracle.reduce_scatter(gn, 1, "f16", False), "rs 16-bit")
+
+
+def test_unflatten_and_flatten_with_odd_offsets():
+    """The tiny unit's last tensor is one element at an offset that is not a
+    multiple of 4 elements; 16-bit tensors of odd sizes break 16-byte alignment."""
+    g = torch.Generator().manual_seed(1)
+    sizes = [1, 999, 3, 4097, 7, 1, 65536 + 5]
+    for dt in (torch.float32, torch.bfloat16):
+        ts = [(torch.randn(n, generator=g)).to(dt).cuda() for n in sizes]
+        flat = ss.fsdp_flatten_pad(ts, 8)
+        ref = oracle.flatten_pad([np_of(t) for t in ts], 8, "f32" if dt == torch.float32 else "bf16")
+        torch.cuda.synchronize()
+        assert_bitexact(np_of(flat), ref, "flatten")
+        back = ss.fsdp_unflatten_views(flat, [(n,) for n in sizes], materialize=True)
+        for a, b in zip(back, ts):
+            assert torch.equal(a.view(torch.int16) if dt != torch.float32 else a.view(torch.int32),
+                               b.view(torch.int16) if dt != torch.float32 else b.view(torch.int32))
+
+
+def test_nan_and_inf_gradients_propagate_like_the_oracle():
+    cfg = scaled(CONFIGS["gpt2-large-block"], gpt_block(32))
+    run = UnitRun(cfg)
+    for q, pos, val in ((0, 3, float("nan")), (1, 100, float("inf")), (0, 101, float("-inf")),
+                        (1, 5000, 65504.0), (0, 5000, 65504.0)):
+        run.grads[q][pos] = val
+    run.run_gpu()
+    run.run_oracle()
+    run.compare()
+    assert np.isnan(np_of(run.master)[3]) and np.isnan(np_of(run.master)[100])
+
+
+def test_empty_shard_is_a_no_op():
+    z = torch.empty(0, device="cuda")
+    ss.fsdp_sharded_adamw(z, z.clone(), z.clone(), [torch.empty(0, dtype=torch.bfloat16, device="cuda")],
+                          0, False, ss.AdamWHP())
+    torch.cuda.synchronize()
+
+
+def test_run_twice_is_bitwise_deterministic():
+    cfg = scaled(CONFIGS["llama70b-block"], llama_block(64, 80, 224))
+    a, b = UnitRun(cfg), UnitRun(cfg)
+    a.run_gpu()
+    b.run_gpu()
+    for x, y in ((a.master, b.master), (a.m, b.m), (a.v, b.v), (a.full, b.full)):
+        assert torch.equal(x.view(torch.int16) if x.dtype != torch.float32 else x.view(torch.int32),
+                           y.view(torch.int16) if y.dtype != torch.float32 else y.view(torch.int32))
+
+
+def test_fp16_16bit_reduce_and_fp32_compute_combinations():
+    """Dtype combinations beyond the five workloads: fp16 grads reduced in 16
+    bits, bf16 grads reduced in fp32, fp32 and bf16 compute copies."""
+    for gd, fp32r, cd in (("f16", False, "f32"), ("bf16", True, "f16"), ("f32", True, "bf16")):
+        cfg = scaled(CONFIGS["gpt2-large-block"], gpt_block(48), grad_dt=gd, fp32_reduce=fp32r,
+                     compute_dt=cd, world=4)
+        run = UnitRun(cfg)
+        run.run_gpu()
+        run.run_oracle()
+        run.compare()
