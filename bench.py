@@ -8,10 +8,21 @@ per FSDP unit.  One step = every unit slot of the workload, each through
 on synthetic inputs already resident in HBM.  Flatten + pad is an init-time
 step: it is timed separately and reported beside the line.
 
-Bytes are algorithmic: per shard element, N*g (read the N ranks' gradient
-blocks) + 12 (read master, m, v) + 12 (write them) + c (write the compute
-copy) + G * 2*N*c (each gather reads N shards and writes N), with g and c the
-gradient and compute element sizes.  A unit pool of distinct blocks larger than
+Two pipelines (--pipeline):
+  unit      (default) one launch per unit, fsdp_step_unit: the fused kernel
+            writes this rank's compute copy straight into its slot of the full
+            buffer and copies the N-1 peer shards into theirs in the same pass.
+            A second gather (reshard after forward, G = 2) reads all N shards
+            from persistent compute shards, so the step also keeps a persistent
+            copy of this rank's shard then.
+  separate  fsdp_sharded_adamw into a compute shard, then fsdp_unshard_gather.
+Bytes are algorithmic, per shard element, with g and c the gradient and
+compute element sizes:
+  separate: N*g (read N gradient blocks) + 12 (read master, m, v) + 12 (write
+            them) + c (write the compute shard) + G * 2*N*c (each gather reads
+            N shards and writes N);
+  unit:     N*g + 24 + c (own slot) + 2*(N-1)*c (peer copies)
+            [+ c persistent own copy + (G-1) * 2*N*c when G = 2].  A unit pool of distinct blocks larger than
 the 256 MB Infinity Cache is cycled over the slots so every step streams HBM.
 
 Prints one JSON line.  --gpus above 1 exits: this measures one GPU.
@@ -37,22 +48,29 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2-large-block",
                     help="gpt2-large-block (default), gpt2-xl-model, gpt3-13b-block, llama70b-block, tiny")
+    ap.add_argument("--pipeline", choices=["unit", "separate"], default="unit")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample (0 disables it)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="skip the per-launch HIP events (the roofline figure needs them)")
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="time every launch of the dominant kernel on one timed step in this many "
+                         "(timing a launch costs a few microseconds of stream time)")
     ap.add_argument("--probe", choices=["copy"], default=None,
                     help="copy: time a plain 1 GiB copy with the gather kernel (counter calibration)")
     return ap.parse_args()
 
 
-def sizes(cfg):
+def sizes(cfg, pipeline):
+    """(fused kernel bytes, whole-step bytes) per shard element."""
     g = 4 if cfg.grad_dt == "f32" else 2
     c = 4 if cfg.compute_dt == "f32" else 2
     N, G = cfg.world, cfg.gathers
-    fused = N * g + 24 + c
-    gather = 2 * N * c
-    return g, c, fused, gather, fused + G * gather
+    if pipeline == "separate":
+        fused = N * g + 24 + c
+        return fused, fused + G * 2 * N * c
+    fused = N * g + 24 + c + 2 * (N - 1) * c + (c if G > 1 else 0)
+    return fused, fused + (G - 1) * 2 * N * c
 
 
 class Unit:
@@ -96,7 +114,7 @@ def cpu_baseline(cfg, unit, budget_s, np_of_bytes):
     resident block, repeated until the budget is spent."""
     import numpy as np
     import oracle
-    g, c, fused, gather, per_elt = sizes(cfg)
+    _, per_elt = sizes(cfg, "separate")
     S = unit.S
     cap = min(S, 4 * 1024 * 1024)          # bounded sample: first `cap` shard elements
     # rank 0's block of each rank's gradient is its first S elements
@@ -141,6 +159,37 @@ def cpu_baseline(cfg, unit, budget_s, np_of_bytes):
                      os.cpu_count()),
         "elements_per_s": round(elems / dt, 1),
     }
+
+
+class HipEvents:
+    """Pre-created HIP events recorded with direct hipEventRecord calls on the
+    launch stream (no per-record allocation or wrapper work)."""
+
+    def __init__(self, count):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(count):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e)
+        self.record = self.hip.hipEventRecord
+
+    def elapsed_ms(self, i, j):
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
 
 
 def traffic_from_profiles(kernel_tag, src_hash):
@@ -209,7 +258,7 @@ def main():
         return
 
     cfg = workloads.CONFIGS[args.workload]
-    g, c, fused_b, gather_b, per_elt = sizes(cfg)
+    fused_b, per_elt = sizes(cfg, args.pipeline)
     pool = [Unit(cfg, b, ss, torch, workloads) for b in range(cfg.pool)]
     S = pool[0].S
     stream = torch.cuda.current_stream()
@@ -221,34 +270,46 @@ def main():
     views = (N.View * len(cfg.numels))()
 
     # prepared ctypes arguments: marshalling happens once, outside the timed region
+    unit_pipe = args.pipeline == "unit"
+    G = cfg.gathers
     plans = []
     for u in pool:
-        fused = (ctypes.c_void_p(u.master.data_ptr()), ctypes.c_void_p(u.m.data_ptr()),
-                 ctypes.c_void_p(u.v.data_ptr()), N.ptr_array([x.data_ptr() for x in u.grads]),
-                 cfg.world, 0, gcode, int(cfg.fp32_reduce), ctypes.c_void_p(u.compute.data_ptr()),
-                 ccode, S, hp_ref, st)
-        gather = (N.ptr_array([u.compute.data_ptr()] + [p.data_ptr() for p in u.peers]), cfg.world, S,
-                  ccode, ctypes.c_void_p(u.full.data_ptr()), st)
+        grads = N.ptr_array([x.data_ptr() for x in u.grads])
+        p, m, v = (ctypes.c_void_p(t.data_ptr()) for t in (u.master, u.m, u.v))
+        shards = N.ptr_array([u.compute.data_ptr()] + [q.data_ptr() for q in u.peers])
+        full = ctypes.c_void_p(u.full.data_ptr())
+        if unit_pipe:
+            persistent = ctypes.c_void_p(u.compute.data_ptr() if G > 1 else None)
+            first = (lib.fsdp_step_unit, (p, m, v, grads, cfg.world, 0, gcode, int(cfg.fp32_reduce), shards,
+                                          full, ccode, S, persistent, hp_ref, st))
+            gathers = [(lib.fsdp_unshard_gather, (shards, cfg.world, S, ccode, full, st))] * (G - 1)
+        else:
+            first = (lib.fsdp_sharded_adamw, (p, m, v, grads, cfg.world, 0, gcode, int(cfg.fp32_reduce),
+                                              ctypes.c_void_p(u.compute.data_ptr()), ccode, S, hp_ref, st))
+            gathers = [(lib.fsdp_unshard_gather, (shards, cfg.world, S, ccode, full, st))] * G
         unflat = (numels, len(cfg.numels), u.Pp, views, None, ccode, None, None)
-        plans.append((fused, gather, unflat))
-    f_adamw, f_gather, f_views = lib.fsdp_sharded_adamw, lib.fsdp_unshard_gather, lib.fsdp_unflatten_views
-    G = cfg.gathers
+        plans.append((first, gathers, unflat))
+    f_views = lib.fsdp_unflatten_views
     slots = [plans[s % len(plans)] for s in range(cfg.blocks)]
+    # Per-launch timing: the library attaches a start/stop event pair to the
+    # dominant kernel's own dispatch packet (fsdp_time_next_launch), so the
+    # timed region carries no extra stream packets.
     use_events = not args.no_kernel_events
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(cfg.blocks * args.steps)] if use_events else []
+    nslot = cfg.blocks
+    every = max(1, args.event_every)
+    ev_steps = [k for k in range(args.steps) if k % every == 0] if use_events else []
+    evs = HipEvents(2 * nslot * len(ev_steps)) if use_events else None
+    arm = lib.fsdp_time_next_launch
 
     def step(ev_base=None):
-        for i, (fa, ga, va) in enumerate(slots):
+        for i, ((f0, a0), gathers, va) in enumerate(slots):
             if ev_base is not None:
-                evs[ev_base + i][0].record(stream)
-            rc = f_adamw(*fa)
-            if ev_base is not None:
-                evs[ev_base + i][1].record(stream)
+                arm(evs.ev[2 * (ev_base + i)], evs.ev[2 * (ev_base + i) + 1])
+            rc = f0(*a0)
             if rc:
-                N.check("fsdp_sharded_adamw", rc)
-            for _ in range(G):
-                rc = f_gather(*ga)
+                N.check(f0.__name__, rc)
+            for fg, ag in gathers:
+                rc = fg(*ag)
                 if rc:
                     N.check("fsdp_unshard_gather", rc)
             rc = f_views(*va)
@@ -262,7 +323,7 @@ def main():
     wall0 = time.perf_counter()
     t0.record(stream)
     for k in range(args.steps):
-        step(k * cfg.blocks if use_events else None)
+        step((k // every) * nslot if (use_events and k % every == 0) else None)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -273,14 +334,17 @@ def main():
 
     roof = None
     if use_events:
-        durs = [a.elapsed_time(b) for a, b in evs]
+        durs = [evs.elapsed_ms(2 * k, 2 * k + 1) for k in range(nslot * len(ev_steps))]
+        evs.close()
         avg_ms = statistics.fmean(durs)
         achieved = fused_b * S / (avg_ms * 1e-3) / 1e9
-        traffic = traffic_from_profiles("fused_rs_adamw_%s" % cfg.name, kernel_source_hash())
+        traffic = traffic_from_profiles("%s_%s" % (args.pipeline, cfg.name), kernel_source_hash())
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "k_rs_adamw_cast (fused reduce-scatter + AdamW + cast)",
+                "kernel": ("k_rs_adamw_cast<GATHER> (fused reduce-scatter + AdamW + cast + all-gather)"
+                           if unit_pipe else "k_rs_adamw_cast (fused reduce-scatter + AdamW + cast)"),
                 "bytes_per_launch": fused_b * S, "avg_launch_ms": round(avg_ms, 5),
+                "timed_launches": len(durs),
                 "median_launch_ms": round(statistics.median(durs), 5)}
 
     cpu = None
@@ -299,7 +363,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-        "config": {"workload": "%s x%d" % (cfg.name, cfg.blocks), "world": cfg.world, "rank": 0,
+        "config": {"workload": "%s x%d" % (cfg.name, cfg.blocks), "pipeline": args.pipeline,
+                   "world": cfg.world, "rank": 0,
                    "shard_numel": S, "unit_numel": pool[0].P, "blocks_per_step": cfg.blocks,
                    "distinct_blocks": cfg.pool, "grad_dtype": cfg.grad_dt,
                    "fp32_reduce_scatter": cfg.fp32_reduce, "compute_dtype": cfg.compute_dt,

@@ -94,6 +94,14 @@ FSDP_API int fsdp_abi_version(void);
 /* Message for the last negative status returned on this thread ("" if none). */
 FSDP_API const char* fsdp_last_error(void);
 
+/* Profiling hook.  The next kernel that this thread enqueues through this
+ * library is launched with start_event / stop_event (hipEvent_t created by the
+ * caller, either may be NULL) attached to its own dispatch packet
+ * (hipExtLaunchKernel), so timing it adds nothing to the stream.  The pair is
+ * consumed by the next entry point that returns, whether it launched a kernel
+ * or not; an entry point that enqueues several kernels times its first. */
+FSDP_API int fsdp_time_next_launch(void* start_event, void* stop_event);
+
 /* Sizes of a flat unit (host only, no device work).
  * numels[n_tensors]: element counts of the unit's tensors, in flat order.
  * Outputs: total P = sum numels; padded P_pad = smallest multiple of world
@@ -168,6 +176,33 @@ FSDP_API int fsdp_sharded_adamw(float* master, float* exp_avg, float* exp_avg_sq
  * step when parameters are resharded after the forward ([TR] pseudo-code). */
 FSDP_API int fsdp_unshard_gather(const void* const* shards, int32_t world, int64_t shard_numel,
                                  fsdp_dtype dt, void* full_out, void* stream);
+
+/* One FSDP unit's step in one launch: the fused reduce-scatter + AdamW + cast
+ * of fsdp_sharded_adamw followed by the all-gather of fsdp_unshard_gather,
+ * with this rank's compute shard written straight into its slot of the full
+ * buffer (the all-gather then moves only the peers' shards).  Sources as for
+ * those two calls; [TR] "From all-reduce to sharded parameters": after the
+ * reduce-scatter each rank updates its own shard, and the full weights are
+ * gathered from every rank's shard before the next compute.
+ *   master, exp_avg, exp_avg_sq, rank_grads, world, rank, grad_dt, fp32_reduce,
+ *   hp, shard_numel   as in fsdp_sharded_adamw
+ *   peer_shards[world]  host array of device pointers: the other ranks'
+ *                       compute shards (shard_numel elements of compute_dt);
+ *                       entry `rank` is ignored and may be NULL
+ *   full_out            device, world * shard_numel elements of compute_dt:
+ *                       full_out[rank*S + i] = round(master_new[i]) and
+ *                       full_out[q*S + i] = peer_shards[q][i] for q != rank
+ *   compute_shard       device, shard_numel of compute_dt, or NULL: an extra
+ *                       persistent copy of this rank's compute shard (needed
+ *                       when the unit is gathered again, e.g. before backward
+ *                       with parameters resharded after the forward)
+ * No output may overlap an input or another output (FSDP_E_ALIAS). */
+FSDP_API int fsdp_step_unit(float* master, float* exp_avg, float* exp_avg_sq,
+                            const void* const* rank_grads, int32_t world, int32_t rank,
+                            fsdp_dtype grad_dt, int32_t fp32_reduce,
+                            const void* const* peer_shards, void* full_out, fsdp_dtype compute_dt,
+                            int64_t shard_numel, void* compute_shard, const fsdp_adamw_hp* hp,
+                            void* stream);
 
 /* Per-tensor views of the full buffer.  [P3] "The FSDP Unit" (use_orig_params):
  * tensor k is full[off_k : off_k + numel_k]; the padding belongs to no view.

@@ -15,13 +15,15 @@ from .api import (  # noqa: F401
     fsdp_layout,
     fsdp_reduce_scatter_local,
     fsdp_sharded_adamw,
+    fsdp_step_unit,
     fsdp_unflatten_views,
     fsdp_unshard_gather,
     view_table,
 )
+from .state import RankState  # noqa: F401
 
 __all__ = [
     "AdamWHP", "FsdpError", "MAX_WORLD", "lib", "dtype_code", "fsdp_layout", "fsdp_flatten_pad",
-    "fsdp_reduce_scatter_local", "fsdp_sharded_adamw", "fsdp_unshard_gather",
-    "fsdp_unflatten_views", "view_table",
+    "fsdp_reduce_scatter_local", "fsdp_sharded_adamw", "fsdp_step_unit", "fsdp_unshard_gather",
+    "fsdp_unflatten_views", "view_table", "RankState",
 ]

@@ -60,6 +60,8 @@ def lib():
     L.fsdp_abi_version.argtypes = []
     L.fsdp_last_error.restype = ctypes.c_char_p
     L.fsdp_last_error.argtypes = []
+    L.fsdp_time_next_launch.restype = ctypes.c_int
+    L.fsdp_time_next_launch.argtypes = [vp, vp]
     L.fsdp_layout.restype = ctypes.c_int
     L.fsdp_layout.argtypes = [i64p, i32, i32, i64p, i64p, i64p]
     L.fsdp_flatten_pad.restype = ctypes.c_int
@@ -69,6 +71,9 @@ def lib():
     L.fsdp_sharded_adamw.restype = ctypes.c_int
     L.fsdp_sharded_adamw.argtypes = [vp, vp, vp, vpp, i32, i32, ctypes.c_int, i32, vp, ctypes.c_int,
                                      i64, ctypes.POINTER(AdamWHP), vp]
+    L.fsdp_step_unit.restype = ctypes.c_int
+    L.fsdp_step_unit.argtypes = [vp, vp, vp, vpp, i32, i32, ctypes.c_int, i32, vpp, vp, ctypes.c_int,
+                                 i64, vp, ctypes.POINTER(AdamWHP), vp]
     L.fsdp_unshard_gather.restype = ctypes.c_int
     L.fsdp_unshard_gather.argtypes = [vpp, i32, i64, ctypes.c_int, vp, vp]
     L.fsdp_unflatten_views.restype = ctypes.c_int

@@ -156,6 +156,58 @@ def fsdp_sharded_adamw(master, exp_avg, exp_avg_sq, rank_grads, rank, fp32_reduc
     return compute_shard
 
 
+def fsdp_step_unit(master, exp_avg, exp_avg_sq, rank_grads, rank, fp32_reduce, hp, peer_shards,
+                   full, compute_shard=None, stream=None):
+    """One unit's step in one launch: fused reduce-scatter + AdamW + cast of rank
+    `rank`'s shard written into its slot of `full`, and the peers' compute
+    shards (peer_shards[q], q != rank; entry `rank` may be None) copied into
+    theirs.  compute_shard, if given, also receives this rank's compute copy."""
+    for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        _dev(t, name)
+        if t.dtype != torch.float32:
+            raise TypeError("%s must be float32" % name)
+        if t.numel() != master.numel():
+            raise ValueError("%s has %d elements, master %d" % (name, t.numel(), master.numel()))
+    S = master.numel()
+    rank_grads, world, gdt = _grads(rank_grads, S)
+    if len(peer_shards) != world:
+        raise ValueError("peer_shards needs one entry per rank (%d), got %d" % (world, len(peer_shards)))
+    _dev(full, "full")
+    cdt = full.dtype
+    if full.numel() != world * S:
+        raise ValueError("full must hold world*shard = %d elements" % (world * S))
+    tensors = rank_grads + [master, exp_avg, exp_avg_sq, full]
+    ptrs = []
+    for q, s in enumerate(peer_shards):
+        if q == rank:
+            ptrs.append(None)
+            continue
+        _dev(s, "peer_shards[%d]" % q)
+        if s.numel() != S or s.dtype != cdt:
+            raise ValueError("peer_shards[%d] must hold %d elements of %s" % (q, S, cdt))
+        ptrs.append(s.data_ptr())
+        tensors.append(s)
+    cptr = None
+    if compute_shard is not None:
+        _dev(compute_shard, "compute_shard")
+        if compute_shard.numel() != S or compute_shard.dtype != cdt:
+            raise ValueError("compute_shard must hold %d elements of %s" % (S, cdt))
+        cptr = compute_shard.data_ptr()
+        tensors.append(compute_shard)
+    _same_device(tensors)
+    if not isinstance(hp, AdamWHP):
+        hp = AdamWHP(**hp)
+    device = master.device
+    with torch.cuda.device(device):
+        check("fsdp_step_unit", N.lib().fsdp_step_unit(
+            ctypes.c_void_p(master.data_ptr()), ctypes.c_void_p(exp_avg.data_ptr()),
+            ctypes.c_void_p(exp_avg_sq.data_ptr()), ptr_array([g.data_ptr() for g in rank_grads]),
+            world, int(rank), dtype_code(gdt), int(bool(fp32_reduce)), ptr_array(ptrs),
+            ctypes.c_void_p(full.data_ptr()), dtype_code(cdt), S, ctypes.c_void_p(cptr),
+            ctypes.byref(hp), _stream(stream, device)))
+    return full
+
+
 def fsdp_unshard_gather(shards, full=None, stream=None):
     """Concatenate the N compute shards into the full flat buffer (a shard already
     at its slot of `full` is left in place)."""

@@ -20,6 +20,7 @@ namespace {
 thread_local char g_err[512] = "";
 
 int fail(int code, const char* fmt, ...) {
+    fsdp::set_launch_events(nullptr, nullptr);   // a failed call consumes pending timing events
     va_list ap;
     va_start(ap, fmt);
     vsnprintf(g_err, sizeof g_err, fmt, ap);
@@ -28,6 +29,7 @@ int fail(int code, const char* fmt, ...) {
 }
 
 int ok() {
+    fsdp::set_launch_events(nullptr, nullptr);   // consumed even when nothing was launched
     g_err[0] = 0;
     return FSDP_OK;
 }
@@ -122,7 +124,16 @@ int fsdp_abi_version(void) { return FSDP_ABI_VERSION; }
 
 const char* fsdp_last_error(void) { return g_err; }
 
-int fsdp_layout(const int64_t* numels, int32_t n_tensors, int32_t world, int64_t* numel_out,
+int fsdp_time_next_launch(void* start_event, void* stop_event) {
+    fsdp::set_launch_events(start_event, stop_event);
+    return FSDP_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int layout_impl(const int64_t* numels, int32_t n_tensors, int32_t world, int64_t* numel_out,
                 int64_t* padded_numel_out, int64_t* shard_numel_out) {
     if (world < 1) return fail(FSDP_E_INVAL, "world = %d < 1", world);
     if (n_tensors < 0) return fail(FSDP_E_INVAL, "n_tensors = %d < 0", n_tensors);
@@ -137,14 +148,24 @@ int fsdp_layout(const int64_t* numels, int32_t n_tensors, int32_t world, int64_t
     if (numel_out) *numel_out = total;
     if (padded_numel_out) *padded_numel_out = padded;
     if (shard_numel_out) *shard_numel_out = padded / world;
-    return ok();
+    return FSDP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fsdp_layout(const int64_t* numels, int32_t n_tensors, int32_t world, int64_t* numel_out,
+                int64_t* padded_numel_out, int64_t* shard_numel_out) {
+    int rc = layout_impl(numels, n_tensors, world, numel_out, padded_numel_out, shard_numel_out);
+    return rc ? rc : ok();
 }
 
 int fsdp_flatten_pad(const void* const* srcs, const int64_t* numels, int32_t n_tensors, fsdp_dtype dt,
                      int32_t world, void* flat, int64_t flat_capacity, int64_t* padded_numel_out,
                      void* stream) {
     int64_t total = 0, padded = 0;
-    int rc = fsdp_layout(numels, n_tensors, world, &total, &padded, nullptr);
+    int rc = layout_impl(numels, n_tensors, world, &total, &padded, nullptr);
     if (rc) return rc;
     if (!valid_dtype(dt)) return fail(FSDP_E_DTYPE, "dtype %d unsupported", (int)dt);
     if (flat_capacity < padded)
@@ -231,57 +252,113 @@ int fsdp_reduce_scatter_local(const void* const* rank_grads, int32_t world, int3
     return ok();
 }
 
-int fsdp_sharded_adamw(float* master, float* exp_avg, float* exp_avg_sq, const void* const* rank_grads,
-                       int32_t world, int32_t rank, fsdp_dtype grad_dt, int32_t fp32_reduce,
-                       void* compute_shard, fsdp_dtype compute_dt, int64_t shard_numel,
-                       const fsdp_adamw_hp* hp, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by fsdp_sharded_adamw and fsdp_step_unit.
+// own_out: this rank's compute destination (compute shard, or its slot of the
+// full buffer); out2: optional second destination; peers: the unit step's
+// (src, dst) copies.
+int adamw_common(const char* fn, float* master, float* exp_avg, float* exp_avg_sq,
+                 const void* const* rank_grads, int32_t world, int32_t rank, int grad_dt,
+                 int32_t fp32_reduce, int compute_dt, int64_t S, const fsdp_adamw_hp* hp,
+                 void* own_out, void* out2, const std::vector<const void*>& peer_src,
+                 const std::vector<void*>& peer_dst, void* stream) {
     std::vector<const void*> blocks;
     std::vector<Range> ins;
-    int rc = check_grads(rank_grads, world, rank, shard_numel, grad_dt, blocks, ins);
+    int rc = check_grads(rank_grads, world, rank, S, grad_dt, blocks, ins);
     if (rc) return rc;
-    if (!valid_dtype(compute_dt)) return fail(FSDP_E_DTYPE, "compute dtype %d unsupported", (int)compute_dt);
-    if (!hp) return fail(FSDP_E_INVAL, "hp is NULL");
-    if (hp->step < 1) return fail(FSDP_E_INVAL, "hp->step = %lld < 1", (long long)hp->step);
+    if (!valid_dtype(compute_dt)) return fail(FSDP_E_DTYPE, "%s: compute dtype %d unsupported", fn, compute_dt);
+    if (!hp) return fail(FSDP_E_INVAL, "%s: hp is NULL", fn);
+    if (hp->step < 1) return fail(FSDP_E_INVAL, "%s: hp->step = %lld < 1", fn, (long long)hp->step);
     if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
-        return fail(FSDP_E_INVAL, "betas must lie in [0, 1)");
-    if (shard_numel == 0) return ok();
+        return fail(FSDP_E_INVAL, "%s: betas must lie in [0, 1)", fn);
+    if (S == 0) return ok();
     if (!master || !exp_avg || !exp_avg_sq)
-        return fail(FSDP_E_INVAL, "master, exp_avg and exp_avg_sq must be non-NULL");
-    const Range outs[4] = {range(master, shard_numel, 4), range(exp_avg, shard_numel, 4),
-                           range(exp_avg_sq, shard_numel, 4),
-                           range(compute_shard, compute_shard ? shard_numel : 0, dt_size(compute_dt))};
-    const char* names[4] = {"master", "exp_avg", "exp_avg_sq", "compute_shard"};
-    for (int i = 0; i < 4; ++i) {
-        for (int j = i + 1; j < 4; ++j)
-            if (overlaps(outs[i], outs[j])) return fail(FSDP_E_ALIAS, "%s overlaps %s", names[i], names[j]);
-        for (int q = 0; q < world; ++q)
-            if (overlaps(outs[i], ins[q]))
-                return fail(FSDP_E_ALIAS, "%s overlaps the block of rank_grads[%d]", names[i], q);
+        return fail(FSDP_E_INVAL, "%s: master, exp_avg and exp_avg_sq must be non-NULL", fn);
+    const int64_t cs = dt_size(compute_dt);
+    for (size_t j = 0; j < peer_src.size(); ++j)
+        ins.push_back(range(peer_src[j], S, cs));
+    std::vector<Range> outs = {range(master, S, 4), range(exp_avg, S, 4), range(exp_avg_sq, S, 4),
+                               range(own_out, own_out ? S : 0, cs), range(out2, out2 ? S : 0, cs)};
+    for (size_t j = 0; j < peer_dst.size(); ++j) outs.push_back(range(peer_dst[j], S, cs));
+    for (size_t i = 0; i < outs.size(); ++i) {
+        for (size_t j = i + 1; j < outs.size(); ++j)
+            if (overlaps(outs[i], outs[j])) return fail(FSDP_E_ALIAS, "%s: output buffers overlap", fn);
+        for (size_t q = 0; q < ins.size(); ++q)
+            if (overlaps(outs[i], ins[q])) return fail(FSDP_E_ALIAS, "%s: an output overlaps an input", fn);
     }
 
     bool vec = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) &&
-               (!compute_shard || aligned16(compute_shard));
+               (!own_out || aligned16(own_out)) && (!out2 || aligned16(out2));
     for (int q = 0; q < world; ++q) vec = vec && aligned16(blocks[q]);
+    for (size_t j = 0; j < peer_src.size(); ++j) vec = vec && aligned16(peer_src[j]) && aligned16(peer_dst[j]);
     fsdp::FusedArgs a{};
     a.grads = blocks.data();
     a.world = world;
     a.grad_dt = grad_dt;
     a.fp32_reduce = fp32_reduce != 0;
     a.compute_dt = compute_dt;
-    a.S = shard_numel;
-    a.nvec = vec ? shard_numel / 8 : 0;
+    a.S = S;
+    a.nvec = vec ? S / 8 : 0;
     a.p = master;
     a.m = exp_avg;
     a.v = exp_avg_sq;
-    a.out = compute_shard;
+    a.out = own_out;
+    a.out2 = out2;
+    a.peer_src = peer_src.data();
+    a.peer_dst = peer_dst.data();
+    a.npeers = (int)peer_src.size();
     a.rs = reduce_scalars(world);
     a.as = adam_scalars(*hp);
     a.cus = cu_count();
     a.stream = stream;
     (void)hipGetLastError();
     hipError_t e = fsdp::launch_fused(a, true);
-    if (e != hipSuccess) return hip_fail(e, "sharded AdamW launch");
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int fsdp_sharded_adamw(float* master, float* exp_avg, float* exp_avg_sq, const void* const* rank_grads,
+                       int32_t world, int32_t rank, fsdp_dtype grad_dt, int32_t fp32_reduce,
+                       void* compute_shard, fsdp_dtype compute_dt, int64_t shard_numel,
+                       const fsdp_adamw_hp* hp, void* stream) {
+    static const std::vector<const void*> no_src;
+    static const std::vector<void*> no_dst;
+    return adamw_common("fsdp_sharded_adamw", master, exp_avg, exp_avg_sq, rank_grads, world, rank,
+                        grad_dt, fp32_reduce, compute_dt, shard_numel, hp, compute_shard, nullptr,
+                        no_src, no_dst, stream);
+}
+
+int fsdp_step_unit(float* master, float* exp_avg, float* exp_avg_sq, const void* const* rank_grads,
+                   int32_t world, int32_t rank, fsdp_dtype grad_dt, int32_t fp32_reduce,
+                   const void* const* peer_shards, void* full_out, fsdp_dtype compute_dt,
+                   int64_t shard_numel, void* compute_shard, const fsdp_adamw_hp* hp, void* stream) {
+    if (world < 1 || world > FSDP_MAX_WORLD)
+        return fail(FSDP_E_INVAL, "world = %d outside [1, %d]", world, FSDP_MAX_WORLD);
+    if (rank < 0 || rank >= world) return fail(FSDP_E_INVAL, "rank = %d outside [0, %d)", rank, world);
+    if (!valid_dtype(compute_dt)) return fail(FSDP_E_DTYPE, "compute dtype %d unsupported", (int)compute_dt);
+    std::vector<const void*> src;
+    std::vector<void*> dst;
+    if (shard_numel > 0) {
+        if (!full_out) return fail(FSDP_E_INVAL, "full_out is NULL");
+        if (world > 1 && !peer_shards) return fail(FSDP_E_INVAL, "peer_shards is NULL");
+        const int64_t bytes = shard_numel * dt_size(compute_dt);
+        for (int q = 0; q < world; ++q) {
+            if (q == rank) continue;
+            if (!peer_shards[q]) return fail(FSDP_E_INVAL, "peer_shards[%d] is NULL", q);
+            src.push_back(peer_shards[q]);
+            dst.push_back((char*)full_out + (int64_t)q * bytes);
+        }
+    }
+    void* own = shard_numel > 0 ? (char*)full_out + (int64_t)rank * shard_numel * dt_size(compute_dt) : nullptr;
+    return adamw_common("fsdp_step_unit", master, exp_avg, exp_avg_sq, rank_grads, world, rank, grad_dt,
+                        fp32_reduce, compute_dt, shard_numel, hp, own, compute_shard, src, dst, stream);
 }
 
 int fsdp_unshard_gather(const void* const* shards, int32_t world, int64_t shard_numel, fsdp_dtype dt,
@@ -317,7 +394,7 @@ int fsdp_unflatten_views(const int64_t* numels, int32_t n_tensors, int64_t padde
                          fsdp_view* views_out, const void* full, fsdp_dtype dt, void* const* dsts,
                          void* stream) {
     int64_t total = 0;
-    int rc = fsdp_layout(numels, n_tensors, 1, &total, nullptr, nullptr);
+    int rc = layout_impl(numels, n_tensors, 1, &total, nullptr, nullptr);
     if (rc) return rc;
     if (total > padded_numel)
         return fail(FSDP_E_SIZE, "tensors hold %lld elements, more than padded_numel %lld",

@@ -9,8 +9,11 @@
 
 namespace fsdp {
 
-constexpr int kThreads = 256;           // 4 wave64 per workgroup
-constexpr int kBlocksPerCU = 8;         // grid cap = CUs * kBlocksPerCU
+#ifndef FSDP_BLOCKS_PER_CU
+#define FSDP_BLOCKS_PER_CU 8
+#endif
+constexpr int kThreads = 256;                          // 4 wave64 per workgroup
+constexpr int kBlocksPerCU = FSDP_BLOCKS_PER_CU;       // grid cap = CUs * kBlocksPerCU
 constexpr int kSegMax = 64;             // segments per flatten/unflatten launch
 constexpr int64_t kSegChunkBytes = 32768;
 
@@ -27,6 +30,14 @@ struct ReduceScalars {
 template <int NW>
 struct GradPtrs {
     const void* p[NW > 0 ? NW : FSDP_MAX_WORLD];
+};
+
+// Peer compute shards copied into their slots of the full buffer by the
+// one-launch unit step: world - 1 (src, dst) pairs.
+template <int NW>
+struct PeerPtrs {
+    const char* src[NW > 1 ? NW - 1 : (NW == 1 ? 1 : FSDP_MAX_WORLD - 1)];
+    char* dst[NW > 1 ? NW - 1 : (NW == 1 ? 1 : FSDP_MAX_WORLD - 1)];
 };
 
 template <int MAXN>
@@ -55,6 +66,10 @@ struct FusedArgs {
     float* m;
     float* v;
     void* out;                 // compute shard (fused) or grad shard (reduce only)
+    void* out2;                // optional second copy of the compute shard, or null
+    const void* const* peer_src;  // world - 1 peer shards (unit step only)
+    void* const* peer_dst;        // their slots in the full buffer
+    int npeers;                // > 0 selects the unit-step kernel (fused + gather)
     ReduceScalars rs;
     AdamScalars as;
     int cus;
@@ -62,6 +77,7 @@ struct FusedArgs {
 };
 
 hipError_t launch_fused(const FusedArgs& a, bool fused);
+void set_launch_events(void* start, void* stop);
 hipError_t launch_gather(const void* const* srcs, void* const* dsts, int n, int64_t bytes, int cus,
                          void* stream);
 hipError_t launch_segments(const SegBatch& b, int64_t chunks, void* stream);

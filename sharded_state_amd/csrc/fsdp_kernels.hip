@@ -25,6 +25,7 @@
 
 #include "fsdp_kernels.h"
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #pragma clang fp contract(off)
@@ -32,6 +33,33 @@
 namespace fsdp {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#ifndef FSDP_NT_LOAD
+#define FSDP_NT_LOAD 0
+#endif
+#ifndef FSDP_NT_STORE
+#define FSDP_NT_STORE 0
+#endif
+#ifndef FSDP_UNROLL
+#define FSDP_UNROLL 1
+#endif
+constexpr int kUnroll = FSDP_UNROLL;   // 8-element vectors per lane per loop trip
+
+// 16-byte global accesses; the streamed buffers are touched once per launch.
+__device__ __forceinline__ u32x4 ld16(const u32x4* p) {
+#if FSDP_NT_LOAD
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+__device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
+#if FSDP_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
 
 // ----------------------------------------------------------------- formats
 template <int F> __device__ __forceinline__ float to_f32(uint32_t bits);
@@ -63,13 +91,13 @@ template <int F>
 __device__ __forceinline__ void load8(const void* __restrict__ base, int64_t vi, float (&x)[8]) {
     if constexpr (F == FSDP_F32) {
         const u32x4* q = reinterpret_cast<const u32x4*>(base) + 2 * vi;
-        u32x4 a = q[0], b = q[1];
+        u32x4 a = ld16(q), b = ld16(q + 1);
         x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
         x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
         x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
         x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
     } else {
-        u32x4 a = reinterpret_cast<const u32x4*>(base)[vi];
+        u32x4 a = ld16(reinterpret_cast<const u32x4*>(base) + vi);
         uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -88,15 +116,15 @@ __device__ __forceinline__ void store8(void* __restrict__ base, int64_t vi, cons
         a.z = __float_as_uint(x[2]); a.w = __float_as_uint(x[3]);
         b.x = __float_as_uint(x[4]); b.y = __float_as_uint(x[5]);
         b.z = __float_as_uint(x[6]); b.w = __float_as_uint(x[7]);
-        q[0] = a;
-        q[1] = b;
+        st16(q, a);
+        st16(q + 1, b);
     } else {
         uint32_t w[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) w[k] = from_f32<F>(x[2 * k]) | (from_f32<F>(x[2 * k + 1]) << 16);
         u32x4 a;
         a.x = w[0]; a.y = w[1]; a.z = w[2]; a.w = w[3];
-        reinterpret_cast<u32x4*>(base)[vi] = a;
+        st16(reinterpret_cast<u32x4*>(base) + vi, a);
     }
 }
 
@@ -189,17 +217,79 @@ __device__ __forceinline__ float reduce1(const GradPtrs<NW>& g, int world, int64
 }
 
 // ----------------------------------------------------------------- kernels
-// Fused reduce-scatter + AdamW + cast over one shard of S elements.
+// Copy vector vi (8 elements of CF) of every peer shard into its slot.
+template <int NW, int CF>
+__device__ __forceinline__ void copy_peers8(const PeerPtrs<NW>& pe, int npeers, int64_t vi) {
+    constexpr int kW = CF == FSDP_F32 ? 2 : 1;      // dwordx4 per 8 elements
+    if constexpr (NW > 1) {
+        u32x4 x[NW - 1][kW];
+#pragma unroll
+        for (int j = 0; j < NW - 1; ++j)
+#pragma unroll
+            for (int w = 0; w < kW; ++w) x[j][w] = ld16(reinterpret_cast<const u32x4*>(pe.src[j]) + kW * vi + w);
+#pragma unroll
+        for (int j = 0; j < NW - 1; ++j)
+#pragma unroll
+            for (int w = 0; w < kW; ++w) st16(reinterpret_cast<u32x4*>(pe.dst[j]) + kW * vi + w, x[j][w]);
+    } else if constexpr (NW == 0) {
+        for (int j = 0; j < npeers; ++j)
+#pragma unroll
+            for (int w = 0; w < kW; ++w)
+                st16(reinterpret_cast<u32x4*>(pe.dst[j]) + kW * vi + w,
+                     ld16(reinterpret_cast<const u32x4*>(pe.src[j]) + kW * vi + w));
+    }
+}
+
+template <int NW, int CF>
+__device__ __forceinline__ void copy_peers1(const PeerPtrs<NW>& pe, int npeers, int64_t i) {
+    const int n = NW > 0 ? NW - 1 : npeers;
+    for (int j = 0; j < n; ++j) {
+        if constexpr (CF == FSDP_F32)
+            reinterpret_cast<uint32_t*>(pe.dst[j])[i] = reinterpret_cast<const uint32_t*>(pe.src[j])[i];
+        else
+            reinterpret_cast<uint16_t*>(pe.dst[j])[i] = reinterpret_cast<const uint16_t*>(pe.src[j])[i];
+    }
+}
+
+// Fused reduce-scatter + AdamW + cast over one shard of S elements, and with
+// GATHER the all-gather of the unit in the same pass: `out` is then this
+// rank's slot of the full buffer and every trip also copies the same 8
+// elements of each peer's compute shard into its slot.
 // g.p[q] points at element 0 of rank q's block `rank` (shard-relative).
 // Elements [0, 8*nvec) take the vector path, [8*nvec, S) the scalar path.
-template <int NW, int GF, bool FP32R, int CF>
+template <int NW, int GF, bool FP32R, int CF, bool GATHER>
 __global__ __launch_bounds__(kThreads) void k_rs_adamw_cast(
-    GradPtrs<NW> g, int world, int64_t S, int64_t nvec, float* __restrict__ p,
-    float* __restrict__ m, float* __restrict__ v, void* __restrict__ out, ReduceScalars rs,
-    AdamScalars as) {
+    GradPtrs<NW> g, PeerPtrs<NW> pe, int world, int npeers, int64_t S, int64_t nvec,
+    float* __restrict__ p, float* __restrict__ m, float* __restrict__ v, void* __restrict__ out,
+    void* __restrict__ out2, ReduceScalars rs, AdamScalars as) {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (int64_t vi = t0; vi < nvec; vi += stride) {
+    int64_t vi = t0;
+    if constexpr (kUnroll > 1) {
+        for (; vi + (kUnroll - 1) * stride < nvec; vi += kUnroll * stride) {
+            float acc[kUnroll][8], pp[kUnroll][8], mm[kUnroll][8], vv[kUnroll][8];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                reduce8<NW, GF, FP32R>(g, world, vi + u * stride, acc[u]);
+                load8<FSDP_F32>(p, vi + u * stride, pp[u]);
+                load8<FSDP_F32>(m, vi + u * stride, mm[u]);
+                load8<FSDP_F32>(v, vi + u * stride, vv[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    adamw1(finish<NW, GF, FP32R>(acc[u][k], rs), pp[u][k], mm[u][k], vv[u][k], as);
+                store8<FSDP_F32>(p, vi + u * stride, pp[u]);
+                store8<FSDP_F32>(m, vi + u * stride, mm[u]);
+                store8<FSDP_F32>(v, vi + u * stride, vv[u]);
+                if (out) store8<CF>(out, vi + u * stride, pp[u]);
+                if (out2) store8<CF>(out2, vi + u * stride, pp[u]);
+                if constexpr (GATHER) copy_peers8<NW, CF>(pe, npeers, vi + u * stride);
+            }
+        }
+    }
+    for (; vi < nvec; vi += stride) {
         float acc[8], pp[8], mm[8], vv[8];
         reduce8<NW, GF, FP32R>(g, world, vi, acc);
         load8<FSDP_F32>(p, vi, pp);
@@ -211,6 +301,8 @@ __global__ __launch_bounds__(kThreads) void k_rs_adamw_cast(
         store8<FSDP_F32>(m, vi, mm);
         store8<FSDP_F32>(v, vi, vv);
         if (out) store8<CF>(out, vi, pp);
+        if (out2) store8<CF>(out2, vi, pp);
+        if constexpr (GATHER) copy_peers8<NW, CF>(pe, npeers, vi);
     }
     for (int64_t i = nvec * 8 + t0; i < S; i += stride) {
         float pp = p[i], mm = m[i], vv = v[i];
@@ -219,6 +311,8 @@ __global__ __launch_bounds__(kThreads) void k_rs_adamw_cast(
         m[i] = mm;
         v[i] = vv;
         if (out) store1<CF>(out, i, pp);
+        if (out2) store1<CF>(out2, i, pp);
+        if constexpr (GATHER) copy_peers1<NW, CF>(pe, npeers, i);
     }
 }
 
@@ -252,10 +346,10 @@ __device__ __forceinline__ void copy_range(char* __restrict__ dst, const char* _
         u32x4* d = reinterpret_cast<u32x4*>(dst);
         const u32x4* s = reinterpret_cast<const u32x4*>(src);
         if (src) {
-            for (int64_t i = lane; i < nv; i += nthreads) d[i] = s[i];
+            for (int64_t i = lane; i < nv; i += nthreads) st16(d + i, ld16(s + i));
         } else {
             const u32x4 z = {0u, 0u, 0u, 0u};
-            for (int64_t i = lane; i < nv; i += nthreads) d[i] = z;
+            for (int64_t i = lane; i < nv; i += nthreads) st16(d + i, z);
         }
         for (int64_t i = (nv << 4) + lane; i < bytes; i += nthreads) dst[i] = src ? src[i] : 0;
     } else if ((a & 3) == 0) {
@@ -303,6 +397,27 @@ __global__ __launch_bounds__(kThreads) void k_segments(SegBatch B) {
 }
 
 // ----------------------------------------------------------------- launchers
+// Optional timing of the next launch: the events ride on the kernel's own
+// dispatch (hipExtLaunchKernel), so no marker packets enter the stream.
+static thread_local hipEvent_t t_ev_start = nullptr;
+static thread_local hipEvent_t t_ev_stop = nullptr;
+
+void set_launch_events(void* start, void* stop) {
+    t_ev_start = (hipEvent_t)start;
+    t_ev_stop = (hipEvent_t)stop;
+}
+
+template <typename K, typename... Args>
+static void launch(K kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+    if (t_ev_start || t_ev_stop) {
+        hipEvent_t a = t_ev_start, b = t_ev_stop;
+        t_ev_start = t_ev_stop = nullptr;
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, a, b, 0, args...);
+    } else {
+        kernel<<<grid, block, 0, st>>>(args...);
+    }
+}
+
 static int64_t grid_for(int64_t work, int cus) {
     int64_t want = (work + kThreads - 1) / kThreads;
     int64_t cap = (int64_t)cus * kBlocksPerCU;
@@ -310,30 +425,40 @@ static int64_t grid_for(int64_t work, int cus) {
     return want < 1 ? 1 : want;
 }
 
+template <int NW, int GF, bool FP32R, int CF>
+static hipError_t fused_go(const FusedArgs& a, const GradPtrs<NW>& g, const PeerPtrs<NW>& pe, dim3 grid) {
+    hipStream_t st = (hipStream_t)a.stream;
+    if (a.npeers > 0)
+        launch(k_rs_adamw_cast<NW, GF, FP32R, CF, true>, grid, dim3(kThreads), st, g, pe, a.world,
+               a.npeers, a.S, a.nvec, a.p, a.m, a.v, a.out, a.out2, a.rs, a.as);
+    else
+        launch(k_rs_adamw_cast<NW, GF, FP32R, CF, false>, grid, dim3(kThreads), st, g, pe, a.world, 0,
+               a.S, a.nvec, a.p, a.m, a.v, a.out, a.out2, a.rs, a.as);
+    return hipGetLastError();
+}
+
 template <int NW, int GF, bool FP32R>
 static hipError_t fused_cf(const FusedArgs& a, const GradPtrs<NW>& g) {
     const int64_t work = a.nvec > 0 ? a.nvec : a.S;
     dim3 grid((unsigned)grid_for(work, a.cus));
-    hipStream_t st = (hipStream_t)a.stream;
-    switch (a.compute_dt) {
-    case FSDP_F32:
-        k_rs_adamw_cast<NW, GF, FP32R, FSDP_F32><<<grid, kThreads, 0, st>>>(g, a.world, a.S, a.nvec, a.p, a.m, a.v, a.out, a.rs, a.as);
-        break;
-    case FSDP_F16:
-        k_rs_adamw_cast<NW, GF, FP32R, FSDP_F16><<<grid, kThreads, 0, st>>>(g, a.world, a.S, a.nvec, a.p, a.m, a.v, a.out, a.rs, a.as);
-        break;
-    default:
-        k_rs_adamw_cast<NW, GF, FP32R, FSDP_BF16><<<grid, kThreads, 0, st>>>(g, a.world, a.S, a.nvec, a.p, a.m, a.v, a.out, a.rs, a.as);
-        break;
+    PeerPtrs<NW> pe{};
+    for (int j = 0; j < a.npeers; ++j) {
+        pe.src[j] = (const char*)a.peer_src[j];
+        pe.dst[j] = (char*)a.peer_dst[j];
     }
-    return hipGetLastError();
+    switch (a.compute_dt) {
+    case FSDP_F32: return fused_go<NW, GF, FP32R, FSDP_F32>(a, g, pe, grid);
+    case FSDP_F16: return fused_go<NW, GF, FP32R, FSDP_F16>(a, g, pe, grid);
+    default: return fused_go<NW, GF, FP32R, FSDP_BF16>(a, g, pe, grid);
+    }
 }
 
 template <int NW, int GF, bool FP32R>
 static hipError_t rs_only(const FusedArgs& a, const GradPtrs<NW>& g) {
     const int64_t work = a.nvec > 0 ? a.nvec : a.S;
     dim3 grid((unsigned)grid_for(work, a.cus));
-    k_reduce_scatter<NW, GF, FP32R><<<grid, kThreads, 0, (hipStream_t)a.stream>>>(g, a.world, a.S, a.nvec, a.out, a.rs);
+    launch(k_reduce_scatter<NW, GF, FP32R>, grid, dim3(kThreads), (hipStream_t)a.stream, g, a.world, a.S,
+           a.nvec, a.out, a.rs);
     return hipGetLastError();
 }
 
@@ -372,18 +497,18 @@ hipError_t launch_gather(const void* const* srcs, void* const* dsts, int n, int6
     if (n <= 8) {
         CopyList<8> L;
         for (int j = 0; j < n; ++j) { L.src[j] = (const char*)srcs[j]; L.dst[j] = (char*)dsts[j]; }
-        k_gather<8><<<grid, kThreads, 0, (hipStream_t)stream>>>(L, bytes);
+        launch(k_gather<8>, grid, dim3(kThreads), (hipStream_t)stream, L, bytes);
     } else {
         CopyList<FSDP_MAX_WORLD> L;
         for (int j = 0; j < n; ++j) { L.src[j] = (const char*)srcs[j]; L.dst[j] = (char*)dsts[j]; }
-        k_gather<FSDP_MAX_WORLD><<<grid, kThreads, 0, (hipStream_t)stream>>>(L, bytes);
+        launch(k_gather<FSDP_MAX_WORLD>, grid, dim3(kThreads), (hipStream_t)stream, L, bytes);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_segments(const SegBatch& b, int64_t chunks, void* stream) {
     if (chunks <= 0) return hipSuccess;
-    k_segments<<<dim3((unsigned)chunks), kThreads, 0, (hipStream_t)stream>>>(b);
+    launch(k_segments, dim3((unsigned)chunks), dim3(kThreads), (hipStream_t)stream, b);
     return hipGetLastError();
 }
 

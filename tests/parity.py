@@ -126,6 +126,40 @@ class UnitRun:
         self.mat = ss.fsdp_unflatten_views(self.full, self.cfg.shapes, materialize=True)
         torch.cuda.synchronize()
 
+    def run_gpu_step_unit(self, step=None, persistent=False):
+        """Every rank again from the same initial state, each through the
+        one-launch fsdp_step_unit with the peers' compute shards of run_gpu."""
+        c, S = self.cfg, self.S
+        self.su_master = self.flat0.clone()
+        self.su_m, self.su_v = self.m0.clone(), self.v0.clone()
+        self.su_full, self.su_compute = [], []
+        for r in range(c.world):
+            sl = slice(r * S, (r + 1) * S)
+            full = torch.empty(c.world * S, dtype=self.cdt_torch, device=self.device)
+            cs = torch.empty(S, dtype=self.cdt_torch, device=self.device) if persistent else None
+            peers = [None if q == r else self.compute[q] for q in range(c.world)]
+            ss.fsdp_step_unit(self.su_master[sl], self.su_m[sl], self.su_v[sl], self.grads, r,
+                              c.fp32_reduce, self.hp(step), peers, full, compute_shard=cs)
+            self.su_full.append(full)
+            self.su_compute.append(cs)
+        torch.cuda.synchronize()
+
+    def compare_step_unit(self):
+        c = self.cfg
+        for name, got, ref in (("master", self.su_master, self.o_master), ("exp_avg", self.su_m, self.o_m),
+                               ("exp_avg_sq", self.su_v, self.o_v)):
+            g = np_of(got)
+            assert_rel(g, ref, "step_unit " + name)
+            assert_bitexact(g, ref, "step_unit %s (bit-exact)" % name)
+        full_ref = np_of(self.full)
+        for r in range(c.world):
+            f = np_of(self.su_full[r])
+            assert_bitexact(f, full_ref, "step_unit full buffer, rank %d" % r)
+            compare_compute(f, self.o_full, c.compute_dt, "step_unit full vs oracle, rank %d" % r)
+            if self.su_compute[r] is not None:
+                assert_bitexact(np_of(self.su_compute[r]), np_of(self.compute[r]),
+                                "step_unit persistent compute shard, rank %d" % r)
+
     def run_oracle(self, step=None):
         c, S = self.cfg, self.S
         gd = self.gdt

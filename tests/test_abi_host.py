@@ -107,3 +107,24 @@ def test_python_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
         ss.fsdp_unshard_gather([torch.zeros(4)])
+
+
+def _step_unit(peers, full, world=2, rank=0, S=1000, cs=None):
+    hp = N.AdamWHP()
+    a, b, c = FAKE, FAKE + (1 << 30), FAKE + (2 << 30)
+    g = [FAKE + ((3 + q) << 30) for q in range(world)]
+    return N.lib().fsdp_step_unit(ctypes.c_void_p(a), ctypes.c_void_p(b), ctypes.c_void_p(c),
+                                  N.ptr_array(g), world, rank, N.BF16, 0, N.ptr_array(peers),
+                                  ctypes.c_void_p(full), N.BF16, S, ctypes.c_void_p(cs), ctypes.byref(hp),
+                                  None)
+
+
+def test_step_unit_validation():
+    full = FAKE + (20 << 30)
+    peer = FAKE + (21 << 30)
+    assert _step_unit([0, full + 2], full) == N.E_ALIAS             # peer inside the full buffer
+    assert _step_unit([0, peer], full, cs=full + 100) == N.E_ALIAS  # extra copy inside full
+    assert _step_unit([0, 0], full) == N.E_INVAL                     # missing peer shard
+    assert _step_unit([0, peer], 0) == N.E_INVAL                     # missing full buffer
+    assert _step_unit([0, peer], full, rank=2) == N.E_INVAL
+    assert _step_unit([0, peer], FAKE + 8) == N.E_ALIAS              # full overlaps master

@@ -39,6 +39,20 @@ def test_unit_matches_oracle(name):
     run.compare()
 
 
+@pytest.mark.parametrize("name", list(CASES))
+def test_step_unit_matches_oracle(name):
+    """The one-launch unit step (fused reduce-scatter + AdamW + cast + gather)
+    gives the oracle's results for every rank, and the same bytes as the
+    two-call pipeline."""
+    print("case", name, flush=True)
+    run = UnitRun(CASES[name])
+    run.run_gpu()
+    run.run_oracle()
+    run.compare()
+    run.run_gpu_step_unit(persistent=name.startswith("gpt3"))
+    run.compare_step_unit()
+
+
 @pytest.mark.parametrize("P,world", [(1, 8), (7, 2), (9, 8), (9, 3), (1_000_001, 2),
                                      (1_000_001, 3), (1_000_001, 7), (4099, 1), (12345, 16)])
 @pytest.mark.parametrize("base", ["gpt2-large-block", "llama70b-block"])
@@ -51,6 +65,8 @@ def test_padding_and_odd_world_sizes(P, world, base):
     run.run_gpu()
     run.run_oracle()
     run.compare()
+    run.run_gpu_step_unit(persistent=True)
+    run.compare_step_unit()
     pad = run.Pp - run.P
     assert not np.any(np_of(run.master)[run.P:].view(np.uint32))
     assert pad == oracle.padded_numel(P, world) - P
