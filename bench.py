@@ -53,7 +53,7 @@ def parse():
                     help="CPU time budget of the oracle baseline sample (0 disables it)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="skip the per-launch HIP events (the roofline figure needs them)")
-    ap.add_argument("--event-every", type=int, default=5,
+    ap.add_argument("--event-every", type=int, default=10,
                     help="time every launch of the dominant kernel on one timed step in this many "
                          "(timing a launch costs a few microseconds of stream time)")
     ap.add_argument("--probe", choices=["copy"], default=None,

@@ -10,7 +10,7 @@
 namespace fsdp {
 
 #ifndef FSDP_BLOCKS_PER_CU
-#define FSDP_BLOCKS_PER_CU 8
+#define FSDP_BLOCKS_PER_CU 256
 #endif
 constexpr int kThreads = 256;                          // 4 wave64 per workgroup
 constexpr int kBlocksPerCU = FSDP_BLOCKS_PER_CU;       // grid cap = CUs * kBlocksPerCU

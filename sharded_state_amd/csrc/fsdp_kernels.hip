@@ -40,11 +40,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #ifndef FSDP_NT_STORE
 #define FSDP_NT_STORE 0
 #endif
-#ifndef FSDP_UNROLL
-#define FSDP_UNROLL 1
-#endif
-constexpr int kUnroll = FSDP_UNROLL;   // 8-element vectors per lane per loop trip
-
 // 16-byte global accesses; the streamed buffers are touched once per launch.
 __device__ __forceinline__ u32x4 ld16(const u32x4* p) {
 #if FSDP_NT_LOAD
@@ -217,27 +212,46 @@ __device__ __forceinline__ float reduce1(const GradPtrs<NW>& g, int world, int64
 }
 
 // ----------------------------------------------------------------- kernels
-// Copy vector vi (8 elements of CF) of every peer shard into its slot.
+// Vector vi (8 elements of CF) of every peer shard: loaded with the unit's
+// other inputs at the top of a loop trip, stored into its slot at the end.
 template <int NW, int CF>
-__device__ __forceinline__ void copy_peers8(const PeerPtrs<NW>& pe, int npeers, int64_t vi) {
-    constexpr int kW = CF == FSDP_F32 ? 2 : 1;      // dwordx4 per 8 elements
+struct PeerVec {
+    static constexpr int kW = CF == FSDP_F32 ? 2 : 1;      // dwordx4 per 8 elements
+    static constexpr int kN = NW > 1 ? NW - 1 : 1;
+    u32x4 x[kN][kW];
+};
+
+template <int NW, int CF>
+__device__ __forceinline__ void load_peers8(const PeerPtrs<NW>& pe, int64_t vi, PeerVec<NW, CF>& r) {
+    constexpr int kW = PeerVec<NW, CF>::kW;
     if constexpr (NW > 1) {
-        u32x4 x[NW - 1][kW];
 #pragma unroll
         for (int j = 0; j < NW - 1; ++j)
 #pragma unroll
-            for (int w = 0; w < kW; ++w) x[j][w] = ld16(reinterpret_cast<const u32x4*>(pe.src[j]) + kW * vi + w);
-#pragma unroll
-        for (int j = 0; j < NW - 1; ++j)
-#pragma unroll
-            for (int w = 0; w < kW; ++w) st16(reinterpret_cast<u32x4*>(pe.dst[j]) + kW * vi + w, x[j][w]);
-    } else if constexpr (NW == 0) {
-        for (int j = 0; j < npeers; ++j)
-#pragma unroll
-            for (int w = 0; w < kW; ++w)
-                st16(reinterpret_cast<u32x4*>(pe.dst[j]) + kW * vi + w,
-                     ld16(reinterpret_cast<const u32x4*>(pe.src[j]) + kW * vi + w));
+            for (int w = 0; w < kW; ++w) r.x[j][w] = ld16(reinterpret_cast<const u32x4*>(pe.src[j]) + kW * vi + w);
     }
+}
+
+template <int NW, int CF>
+__device__ __forceinline__ void store_peers8(const PeerPtrs<NW>& pe, int64_t vi, const PeerVec<NW, CF>& r) {
+    constexpr int kW = PeerVec<NW, CF>::kW;
+    if constexpr (NW > 1) {
+#pragma unroll
+        for (int j = 0; j < NW - 1; ++j)
+#pragma unroll
+            for (int w = 0; w < kW; ++w) st16(reinterpret_cast<u32x4*>(pe.dst[j]) + kW * vi + w, r.x[j][w]);
+    }
+}
+
+// Generic world size: copy each peer vector directly.
+template <int NW, int CF>
+__device__ __forceinline__ void copy_peers8_generic(const PeerPtrs<NW>& pe, int npeers, int64_t vi) {
+    constexpr int kW = CF == FSDP_F32 ? 2 : 1;
+    for (int j = 0; j < npeers; ++j)
+#pragma unroll
+        for (int w = 0; w < kW; ++w)
+            st16(reinterpret_cast<u32x4*>(pe.dst[j]) + kW * vi + w,
+                 ld16(reinterpret_cast<const u32x4*>(pe.src[j]) + kW * vi + w));
 }
 
 template <int NW, int CF>
@@ -258,59 +272,59 @@ __device__ __forceinline__ void copy_peers1(const PeerPtrs<NW>& pe, int npeers, 
 // g.p[q] points at element 0 of rank q's block `rank` (shard-relative).
 // Elements [0, 8*nvec) take the vector path, [8*nvec, S) the scalar path.
 template <int NW, int GF, bool FP32R, int CF, bool GATHER>
+__device__ __forceinline__ void unit_vec(const GradPtrs<NW>& g, const PeerPtrs<NW>& pe, int world,
+                                         int npeers, int64_t vi, float* __restrict__ p,
+                                         float* __restrict__ m, float* __restrict__ v,
+                                         void* __restrict__ out, void* __restrict__ out2,
+                                         const ReduceScalars& rs, const AdamScalars& as) {
+    // every load of the trip first: gradient blocks, master/m/v, peer shards
+    float acc[8], pp[8], mm[8], vv[8];
+    PeerVec<NW, CF> peer;
+    if constexpr (GATHER && NW > 1) load_peers8<NW, CF>(pe, vi, peer);
+    load8<FSDP_F32>(p, vi, pp);
+    load8<FSDP_F32>(m, vi, mm);
+    load8<FSDP_F32>(v, vi, vv);
+    reduce8<NW, GF, FP32R>(g, world, vi, acc);
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the math
+#pragma unroll
+    for (int k = 0; k < 8; ++k) adamw1(finish<NW, GF, FP32R>(acc[k], rs), pp[k], mm[k], vv[k], as);
+    store8<FSDP_F32>(p, vi, pp);
+    store8<FSDP_F32>(m, vi, mm);
+    store8<FSDP_F32>(v, vi, vv);
+    if constexpr (GATHER) {
+        // the unit step always has its own slot; keep the peer stores in the
+        // same basic block as their loads so they are not sunk past the math
+        store8<CF>(out, vi, pp);
+        if constexpr (NW > 1) store_peers8<NW, CF>(pe, vi, peer);
+        if constexpr (NW == 0) copy_peers8_generic<NW, CF>(pe, npeers, vi);
+    } else {
+        if (out) store8<CF>(out, vi, pp);
+    }
+    if (out2) store8<CF>(out2, vi, pp);
+}
+
+// Fused reduce-scatter + AdamW + cast over one shard of S elements, and with
+// GATHER the all-gather of the unit in the same pass: `out` is then this
+// rank's slot of the full buffer and every trip also copies the same 8
+// elements of each peer's compute shard into its slot.
+// g.p[q] points at element 0 of rank q's block `rank` (shard-relative).
+// Elements [0, 8*nvec) take the vector path, [8*nvec, S) the scalar path.
+template <int NW, int GF, bool FP32R, int CF, bool GATHER>
 __global__ __launch_bounds__(kThreads) void k_rs_adamw_cast(
     GradPtrs<NW> g, PeerPtrs<NW> pe, int world, int npeers, int64_t S, int64_t nvec,
     float* __restrict__ p, float* __restrict__ m, float* __restrict__ v, void* __restrict__ out,
     void* __restrict__ out2, ReduceScalars rs, AdamScalars as) {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    int64_t vi = t0;
-    if constexpr (kUnroll > 1) {
-        for (; vi + (kUnroll - 1) * stride < nvec; vi += kUnroll * stride) {
-            float acc[kUnroll][8], pp[kUnroll][8], mm[kUnroll][8], vv[kUnroll][8];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                reduce8<NW, GF, FP32R>(g, world, vi + u * stride, acc[u]);
-                load8<FSDP_F32>(p, vi + u * stride, pp[u]);
-                load8<FSDP_F32>(m, vi + u * stride, mm[u]);
-                load8<FSDP_F32>(v, vi + u * stride, vv[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    adamw1(finish<NW, GF, FP32R>(acc[u][k], rs), pp[u][k], mm[u][k], vv[u][k], as);
-                store8<FSDP_F32>(p, vi + u * stride, pp[u]);
-                store8<FSDP_F32>(m, vi + u * stride, mm[u]);
-                store8<FSDP_F32>(v, vi + u * stride, vv[u]);
-                if (out) store8<CF>(out, vi + u * stride, pp[u]);
-                if (out2) store8<CF>(out2, vi + u * stride, pp[u]);
-                if constexpr (GATHER) copy_peers8<NW, CF>(pe, npeers, vi + u * stride);
-            }
-        }
-    }
-    for (; vi < nvec; vi += stride) {
-        float acc[8], pp[8], mm[8], vv[8];
-        reduce8<NW, GF, FP32R>(g, world, vi, acc);
-        load8<FSDP_F32>(p, vi, pp);
-        load8<FSDP_F32>(m, vi, mm);
-        load8<FSDP_F32>(v, vi, vv);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) adamw1(finish<NW, GF, FP32R>(acc[k], rs), pp[k], mm[k], vv[k], as);
-        store8<FSDP_F32>(p, vi, pp);
-        store8<FSDP_F32>(m, vi, mm);
-        store8<FSDP_F32>(v, vi, vv);
-        if (out) store8<CF>(out, vi, pp);
-        if (out2) store8<CF>(out2, vi, pp);
-        if constexpr (GATHER) copy_peers8<NW, CF>(pe, npeers, vi);
-    }
+    for (int64_t vi = t0; vi < nvec; vi += stride)
+        unit_vec<NW, GF, FP32R, CF, GATHER>(g, pe, world, npeers, vi, p, m, v, out, out2, rs, as);
     for (int64_t i = nvec * 8 + t0; i < S; i += stride) {
         float pp = p[i], mm = m[i], vv = v[i];
         adamw1(finish<NW, GF, FP32R>(reduce1<NW, GF, FP32R>(g, world, i), rs), pp, mm, vv, as);
         p[i] = pp;
         m[i] = mm;
         v[i] = vv;
-        if (out) store1<CF>(out, i, pp);
+        if (GATHER || out) store1<CF>(out, i, pp);
         if (out2) store1<CF>(out2, i, pp);
         if constexpr (GATHER) copy_peers1<NW, CF>(pe, npeers, i);
     }
