@@ -10,10 +10,10 @@
 namespace fsdp {
 
 #ifndef FSDP_BLOCKS_PER_CU
-#define FSDP_BLOCKS_PER_CU 256
+#define FSDP_BLOCKS_PER_CU 2048
 #endif
 constexpr int kThreads = 256;                          // 4 wave64 per workgroup
-constexpr int kBlocksPerCU = FSDP_BLOCKS_PER_CU;       // grid cap = CUs * kBlocksPerCU
+constexpr int kBlocksPerCU = FSDP_BLOCKS_PER_CU;       // grid cap = CUs * kBlocksPerCU (one trip per lane up to ~1e9 elements)
 constexpr int kSegMax = 64;             // segments per flatten/unflatten launch
 constexpr int64_t kSegChunkBytes = 32768;
 

@@ -38,9 +38,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define FSDP_NT_LOAD 0
 #endif
 #ifndef FSDP_NT_STORE
-#define FSDP_NT_STORE 0
+#define FSDP_NT_STORE 1   // streamed outputs: non-temporal (measured +1-9% on the unit step)
 #endif
-// 16-byte global accesses; the streamed buffers are touched once per launch.
+// 16-byte global accesses; the streamed buffers are touched once per launch,
+// so wide stores carry the non-temporal hint.
 __device__ __forceinline__ u32x4 ld16(const u32x4* p) {
 #if FSDP_NT_LOAD
     return __builtin_nontemporal_load(p);
