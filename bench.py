@@ -8,22 +8,28 @@ per FSDP unit.  One step = every unit slot of the workload, each through
 on synthetic inputs already resident in HBM.  Flatten + pad is an init-time
 step: it is timed separately and reported beside the line.
 
-Two pipelines (--pipeline):
-  unit      (default) one launch per unit, fsdp_step_unit: the fused kernel
-            writes this rank's compute copy straight into its slot of the full
-            buffer and copies the N-1 peer shards into theirs in the same pass.
-            A second gather (reshard after forward, G = 2) reads all N shards
-            from persistent compute shards, so the step also keeps a persistent
+Three pipelines (--pipeline):
+  units     (default) fsdp_step_units: the step of every unit of the workload
+            in as few launches as the kernel-argument table allows (up to 40
+            units at N <= 2, 16 at N = 8; a unit appears at most once per
+            launch), each unit as in `unit`.  One launch pays the grid's
+            ramp-up and drain once for all its units.
+  unit      one launch per unit, fsdp_step_unit: the fused kernel writes this
+            rank's compute copy straight into its slot of the full buffer and
+            copies the N-1 peer shards into theirs in the same pass.  A second
+            gather (reshard after forward, G = 2) reads all N shards from
+            persistent compute shards, so the step also keeps a persistent
             copy of this rank's shard then.
   separate  fsdp_sharded_adamw into a compute shard, then fsdp_unshard_gather.
 Bytes are algorithmic, per shard element, with g and c the gradient and
 compute element sizes:
-  separate: N*g (read N gradient blocks) + 12 (read master, m, v) + 12 (write
-            them) + c (write the compute shard) + G * 2*N*c (each gather reads
-            N shards and writes N);
-  unit:     N*g + 24 + c (own slot) + 2*(N-1)*c (peer copies)
-            [+ c persistent own copy + (G-1) * 2*N*c when G = 2].  A unit pool of distinct blocks larger than
-the 256 MB Infinity Cache is cycled over the slots so every step streams HBM.
+  separate:     N*g (read N gradient blocks) + 12 (read master, m, v) + 12
+                (write them) + c (write the compute shard) + G * 2*N*c (each
+                gather reads N shards and writes N);
+  unit, units:  N*g + 24 + c (own slot) + 2*(N-1)*c (peer copies)
+                [+ c persistent own copy + (G-1) * 2*N*c when G = 2].
+A unit pool of distinct blocks larger than the 256 MB Infinity Cache is cycled
+over the slots so every step streams HBM.
 
 Prints one JSON line.  --gpus above 1 exits: this measures one GPU.
 """
@@ -48,7 +54,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2-large-block",
                     help="gpt2-large-block (default), gpt2-xl-model, gpt3-13b-block, llama70b-block, tiny")
-    ap.add_argument("--pipeline", choices=["unit", "separate"], default="unit")
+    ap.add_argument("--pipeline", choices=["units", "unit", "separate"], default="units")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="alternate independent units over this many HIP streams (default priority), "
+                         "so one unit's tail overlaps the next unit's head")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample (0 disables it)")
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -258,11 +267,12 @@ def main():
         return
 
     cfg = workloads.CONFIGS[args.workload]
-    fused_b, per_elt = sizes(cfg, args.pipeline)
+    fused_b, per_elt = sizes(cfg, "separate" if args.pipeline == "separate" else "unit")
     pool = [Unit(cfg, b, ss, torch, workloads) for b in range(cfg.pool)]
     S = pool[0].S
     stream = torch.cuda.current_stream()
-    st = ctypes.c_void_p(stream.cuda_stream)
+    streams = [stream] + [torch.cuda.Stream() for _ in range(max(1, args.streams) - 1)]
+    st_handles = [ctypes.c_void_p(x.cuda_stream) for x in streams]
     hp = ss.AdamWHP(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.step)
     hp_ref = ctypes.byref(hp)
     gcode, ccode = ss.dtype_code(pool[0].grads[0].dtype), ss.dtype_code(pool[0].compute.dtype)
@@ -270,60 +280,98 @@ def main():
     views = (N.View * len(cfg.numels))()
 
     # prepared ctypes arguments: marshalling happens once, outside the timed region
-    unit_pipe = args.pipeline == "unit"
+    unit_pipe = args.pipeline in ("unit", "units")
     G = cfg.gathers
-    plans = []
-    for u in pool:
+    per_unit = []
+    for i, u in enumerate(pool):
         grads = N.ptr_array([x.data_ptr() for x in u.grads])
         p, m, v = (ctypes.c_void_p(t.data_ptr()) for t in (u.master, u.m, u.v))
         shards = N.ptr_array([u.compute.data_ptr()] + [q.data_ptr() for q in u.peers])
+        peer_tab = N.ptr_array([0] + [q.data_ptr() for q in u.peers])
         full = ctypes.c_void_p(u.full.data_ptr())
-        if unit_pipe:
-            persistent = ctypes.c_void_p(u.compute.data_ptr() if G > 1 else None)
-            first = (lib.fsdp_step_unit, (p, m, v, grads, cfg.world, 0, gcode, int(cfg.fp32_reduce), shards,
-                                          full, ccode, S, persistent, hp_ref, st))
-            gathers = [(lib.fsdp_unshard_gather, (shards, cfg.world, S, ccode, full, st))] * (G - 1)
-        else:
-            first = (lib.fsdp_sharded_adamw, (p, m, v, grads, cfg.world, 0, gcode, int(cfg.fp32_reduce),
-                                              ctypes.c_void_p(u.compute.data_ptr()), ccode, S, hp_ref, st))
-            gathers = [(lib.fsdp_unshard_gather, (shards, cfg.world, S, ccode, full, st))] * G
+        persistent = u.compute.data_ptr() if G > 1 else None
+        desc = N.Unit(u.master.data_ptr(), u.m.data_ptr(), u.v.data_ptr(), grads, peer_tab,
+                      u.full.data_ptr(), persistent, S)
         unflat = (numels, len(cfg.numels), u.Pp, views, None, ccode, None, None)
-        plans.append((first, gathers, unflat))
-    f_views = lib.fsdp_unflatten_views
-    slots = [plans[s % len(plans)] for s in range(cfg.blocks)]
+        per_unit.append(dict(grads=grads, p=p, m=m, v=v, shards=shards, peer_tab=peer_tab, full=full,
+                             persistent=ctypes.c_void_p(persistent), desc=desc, views=unflat))
+
+    # launch groups: (first call, units in it, trailing calls), in slot order
+    slots = [k % len(pool) for k in range(cfg.blocks)]
+    groups = []
+    if args.pipeline == "units":
+        kmax = {1: 40, 2: 40, 4: 24, 8: 16}.get(cfg.world, 1)
+        lim = min(kmax, len(pool))           # a unit appears at most once per launch
+        nb = -(-len(slots) // lim)
+        bounds = [round(j * len(slots) / nb) for j in range(nb + 1)]
+        for j in range(nb):
+            batch = slots[bounds[j]:bounds[j + 1]]
+            st = st_handles[j % len(st_handles)]
+            table = (N.Unit * len(batch))(*[per_unit[i]["desc"] for i in batch])
+            first = (lib.fsdp_step_units, (table, len(batch), cfg.world, 0, gcode, int(cfg.fp32_reduce), ccode,
+                                           hp_ref, st))
+            trail = [(lib.fsdp_unshard_gather, (per_unit[i]["shards"], cfg.world, S, ccode, per_unit[i]["full"], st))
+                     for i in batch for _ in range(G - 1)]
+            trail += [(lib.fsdp_unflatten_views, per_unit[i]["views"]) for i in batch]
+            groups.append((first, len(batch), trail, table))
+    else:
+        for j, i in enumerate(slots):
+            d = per_unit[i]
+            st = st_handles[j % len(st_handles)] if args.streams > 1 else st_handles[0]
+            if args.pipeline == "unit":
+                first = (lib.fsdp_step_unit, (d["p"], d["m"], d["v"], d["grads"], cfg.world, 0, gcode,
+                                              int(cfg.fp32_reduce), d["peer_tab"], d["full"], ccode, S,
+                                              d["persistent"], hp_ref, st))
+                trail = [(lib.fsdp_unshard_gather, (d["shards"], cfg.world, S, ccode, d["full"], st))] * (G - 1)
+            else:
+                first = (lib.fsdp_sharded_adamw, (d["p"], d["m"], d["v"], d["grads"], cfg.world, 0, gcode,
+                                                  int(cfg.fp32_reduce), ctypes.c_void_p(pool[i].compute.data_ptr()),
+                                                  ccode, S, hp_ref, st))
+                trail = [(lib.fsdp_unshard_gather, (d["shards"], cfg.world, S, ccode, d["full"], st))] * G
+            trail = trail + [(lib.fsdp_unflatten_views, d["views"])]
+            groups.append((first, 1, trail, None))
     # Per-launch timing: the library attaches a start/stop event pair to the
     # dominant kernel's own dispatch packet (fsdp_time_next_launch), so the
     # timed region carries no extra stream packets.
     use_events = not args.no_kernel_events
-    nslot = cfg.blocks
+    nslot = len(groups)
     every = max(1, args.event_every)
     ev_steps = [k for k in range(args.steps) if k % every == 0] if use_events else []
     evs = HipEvents(2 * nslot * len(ev_steps)) if use_events else None
     arm = lib.fsdp_time_next_launch
 
     def step(ev_base=None):
-        for i, ((f0, a0), gathers, va) in enumerate(slots):
+        for i, ((f0, a0), _, trail, _) in enumerate(groups):
             if ev_base is not None:
                 arm(evs.ev[2 * (ev_base + i)], evs.ev[2 * (ev_base + i) + 1])
             rc = f0(*a0)
             if rc:
                 N.check(f0.__name__, rc)
-            for fg, ag in gathers:
+            for fg, ag in trail:
                 rc = fg(*ag)
                 if rc:
-                    N.check("fsdp_unshard_gather", rc)
-            rc = f_views(*va)
-            if rc:
-                N.check("fsdp_unflatten_views", rc)
+                    N.check(fg.__name__, rc)
 
+    def fork():
+        for x in streams[1:]:
+            x.wait_stream(stream)
+
+    def join():
+        for x in streams[1:]:
+            stream.wait_stream(x)
+
+    fork()
     for _ in range(args.warmup):
         step()
+    join()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t0.record(stream)
+    fork()
     for k in range(args.steps):
         step((k // every) * nslot if (use_events and k % every == 0) else None)
+    join()
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -337,13 +385,16 @@ def main():
         durs = [evs.elapsed_ms(2 * k, 2 * k + 1) for k in range(nslot * len(ev_steps))]
         evs.close()
         avg_ms = statistics.fmean(durs)
-        achieved = fused_b * S / (avg_ms * 1e-3) / 1e9
+        units_per_launch = cfg.blocks / len(groups)
+        bytes_per_launch = fused_b * S * units_per_launch
+        achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
         traffic = traffic_from_profiles("%s_%s" % (args.pipeline, cfg.name), kernel_source_hash())
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": ("k_rs_adamw_cast<GATHER> (fused reduce-scatter + AdamW + cast + all-gather)"
-                           if unit_pipe else "k_rs_adamw_cast (fused reduce-scatter + AdamW + cast)"),
-                "bytes_per_launch": fused_b * S, "avg_launch_ms": round(avg_ms, 5),
+                "kernel": ("k_units<GATHER> (fused reduce-scatter + AdamW + cast + all-gather, %g units per "
+                           "launch)" % units_per_launch if unit_pipe else
+                           "k_units (fused reduce-scatter + AdamW + cast)"),
+                "bytes_per_launch": int(bytes_per_launch), "avg_launch_ms": round(avg_ms, 5),
                 "timed_launches": len(durs),
                 "median_launch_ms": round(statistics.median(durs), 5)}
 
@@ -364,6 +415,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "config": {"workload": "%s x%d" % (cfg.name, cfg.blocks), "pipeline": args.pipeline,
+                   "streams": len(streams),
                    "world": cfg.world, "rank": 0,
                    "shard_numel": S, "unit_numel": pool[0].P, "blocks_per_step": cfg.blocks,
                    "distinct_blocks": cfg.pool, "grad_dtype": cfg.grad_dt,

@@ -204,6 +204,35 @@ FSDP_API int fsdp_step_unit(float* master, float* exp_avg, float* exp_avg_sq,
                             int64_t shard_numel, void* compute_shard, const fsdp_adamw_hp* hp,
                             void* stream);
 
+/* One unit of a batched step (fsdp_step_units). */
+typedef struct fsdp_unit {
+    float* master;                   /* device fp32, shard_numel, updated in place */
+    float* exp_avg;                  /* device fp32, shard_numel, updated in place */
+    float* exp_avg_sq;               /* device fp32, shard_numel, updated in place */
+    const void* const* rank_grads;   /* host array [world] of device pointers, world*shard_numel each */
+    const void* const* peer_shards;  /* host array [world] (entry `rank` ignored), or NULL without full_out */
+    void* full_out;                  /* device, world*shard_numel of compute dtype, or NULL: no all-gather */
+    void* compute_shard;             /* device, shard_numel of compute dtype, or NULL */
+    int64_t shard_numel;
+} fsdp_unit;
+
+/* Several units' steps in as few launches as possible: the optimizer step of
+ * every flat unit of a model, as one fused multi-tensor update.  [P4]
+ * "工作原理": each rank updates the optimizer state of its own shards only;
+ * [TR] "Adoption paths for FSDP", concern 3: one hyper-parameter set per
+ * flattened unit (here one set for the whole call).  Unit k is stepped exactly
+ * as by fsdp_step_unit (when units[k].full_out is set: fused reduce-scatter,
+ * AdamW, cast, all-gather) or as by fsdp_sharded_adamw (when it is NULL, with
+ * compute_shard as the compute output); every unit of a call must take the
+ * same form.  All units share world, rank, dtypes and hp.  Units are packed
+ * into launches of up to 40 (world <= 2), 24 (world 4) or 16 (world 8) units;
+ * other world sizes take one launch per unit.  No output of any unit may
+ * overlap an input or an output of any unit (FSDP_E_ALIAS): a unit may appear
+ * only once per call. */
+FSDP_API int fsdp_step_units(const fsdp_unit* units, int32_t n_units, int32_t world, int32_t rank,
+                             fsdp_dtype grad_dt, int32_t fp32_reduce, fsdp_dtype compute_dt,
+                             const fsdp_adamw_hp* hp, void* stream);
+
 /* Per-tensor views of the full buffer.  [P3] "The FSDP Unit" (use_orig_params):
  * tensor k is full[off_k : off_k + numel_k]; the padding belongs to no view.
  *   views_out[n_tensors]  host, receives {off_k, numel_k}

@@ -16,6 +16,8 @@ from .api import (  # noqa: F401
     fsdp_reduce_scatter_local,
     fsdp_sharded_adamw,
     fsdp_step_unit,
+    fsdp_step_units,
+    prepare_step_units,
     fsdp_unflatten_views,
     fsdp_unshard_gather,
     view_table,
@@ -24,6 +26,6 @@ from .state import RankState  # noqa: F401
 
 __all__ = [
     "AdamWHP", "FsdpError", "MAX_WORLD", "lib", "dtype_code", "fsdp_layout", "fsdp_flatten_pad",
-    "fsdp_reduce_scatter_local", "fsdp_sharded_adamw", "fsdp_step_unit", "fsdp_unshard_gather",
+    "fsdp_reduce_scatter_local", "fsdp_sharded_adamw", "fsdp_step_unit", "fsdp_step_units", "prepare_step_units", "fsdp_unshard_gather",
     "fsdp_unflatten_views", "view_table", "RankState",
 ]

@@ -34,6 +34,14 @@ class View(ctypes.Structure):
     _fields_ = [("offset", ctypes.c_int64), ("numel", ctypes.c_int64)]
 
 
+class Unit(ctypes.Structure):
+    """fsdp_unit: one unit of a batched step."""
+    _fields_ = [("master", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("rank_grads", ctypes.POINTER(ctypes.c_void_p)),
+                ("peer_shards", ctypes.POINTER(ctypes.c_void_p)), ("full_out", ctypes.c_void_p),
+                ("compute_shard", ctypes.c_void_p), ("shard_numel", ctypes.c_int64)]
+
+
 class FsdpError(RuntimeError):
     def __init__(self, func, code, msg):
         super().__init__("%s failed (status %d): %s" % (func, code, msg))
@@ -74,6 +82,9 @@ def lib():
     L.fsdp_step_unit.restype = ctypes.c_int
     L.fsdp_step_unit.argtypes = [vp, vp, vp, vpp, i32, i32, ctypes.c_int, i32, vpp, vp, ctypes.c_int,
                                  i64, vp, ctypes.POINTER(AdamWHP), vp]
+    L.fsdp_step_units.restype = ctypes.c_int
+    L.fsdp_step_units.argtypes = [ctypes.POINTER(Unit), i32, i32, i32, ctypes.c_int, i32, ctypes.c_int,
+                                  ctypes.POINTER(AdamWHP), vp]
     L.fsdp_unshard_gather.restype = ctypes.c_int
     L.fsdp_unshard_gather.argtypes = [vpp, i32, i64, ctypes.c_int, vp, vp]
     L.fsdp_unflatten_views.restype = ctypes.c_int

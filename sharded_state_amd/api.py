@@ -11,7 +11,7 @@ import ctypes
 import torch
 
 from . import _native as N
-from ._native import AdamWHP, View, check, i64_array, ptr_array
+from ._native import AdamWHP, Unit, View, check, i64_array, ptr_array
 
 _DT = {torch.float32: N.F32, torch.float16: N.F16, torch.bfloat16: N.BF16}
 _TORCH = {v: k for k, v in _DT.items()}
@@ -206,6 +206,99 @@ def fsdp_step_unit(master, exp_avg, exp_avg_sq, rank_grads, rank, fp32_reduce, h
             ctypes.c_void_p(full.data_ptr()), dtype_code(cdt), S, ctypes.c_void_p(cptr),
             ctypes.byref(hp), _stream(stream, device)))
     return full
+
+
+def fsdp_step_units(units, rank, fp32_reduce, hp, stream=None):
+    """Step several units in as few launches as possible.  `units` is a list of
+    dicts with keys master, exp_avg, exp_avg_sq, rank_grads, and either
+    (peer_shards, full[, compute_shard]) for the fused step with all-gather or
+    compute_shard alone for the step without it.  All units share world (the
+    length of rank_grads), rank, dtypes and hp.  Returns the prepared call
+    (callable with no arguments) after running it once, so a training loop can
+    re-issue it without marshalling again."""
+    call = prepare_step_units(units, rank, fp32_reduce, hp, stream)
+    call()
+    return call
+
+
+def prepare_step_units(units, rank, fp32_reduce, hp, stream=None):
+    """Marshal a fsdp_step_units call once; the returned callable issues it."""
+    if not units:
+        raise ValueError("units is empty")
+    if not isinstance(hp, AdamWHP):
+        hp = AdamWHP(**hp)
+    world = len(units[0]["rank_grads"])
+    gather = units[0].get("full") is not None
+    table = (Unit * len(units))()
+    keep = []
+    gdt = cdt = None
+    device = units[0]["master"].device
+    tensors = []
+    for k, u in enumerate(units):
+        master, m, v = u["master"], u["exp_avg"], u["exp_avg_sq"]
+        for name, t in (("master", master), ("exp_avg", m), ("exp_avg_sq", v)):
+            _dev(t, "units[%d].%s" % (k, name))
+            if t.dtype != torch.float32 or t.numel() != master.numel():
+                raise ValueError("units[%d].%s must be float32 with master's size" % (k, name))
+        S = master.numel()
+        grads, w, g_dt = _grads(u["rank_grads"], S)
+        if w != world:
+            raise ValueError("units[%d] has %d ranks, units[0] %d" % (k, w, world))
+        gdt = gdt or g_dt
+        if g_dt != gdt:
+            raise TypeError("every unit's gradients must share one dtype")
+        full = u.get("full")
+        cs = u.get("compute_shard")
+        if (full is not None) != gather:
+            raise ValueError("either every unit has full or none")
+        out_dt = full.dtype if full is not None else (cs.dtype if cs is not None else None)
+        if out_dt is not None:
+            cdt = cdt or out_dt
+            if out_dt != cdt:
+                raise TypeError("every unit's compute dtype must be the same")
+        gptr = ptr_array([x.data_ptr() for x in grads])
+        keep.append(gptr)
+        tensors += grads + [master, m, v]
+        pptr = None
+        if gather:
+            _dev(full, "units[%d].full" % k)
+            if full.numel() != world * S:
+                raise ValueError("units[%d].full must hold world*shard = %d elements" % (k, world * S))
+            peers = u["peer_shards"]
+            if len(peers) != world:
+                raise ValueError("units[%d].peer_shards needs %d entries" % (k, world))
+            ptrs = []
+            for q, sh in enumerate(peers):
+                if q == rank:
+                    ptrs.append(None)
+                    continue
+                _dev(sh, "units[%d].peer_shards[%d]" % (k, q))
+                if sh.numel() != S or sh.dtype != full.dtype:
+                    raise ValueError("units[%d].peer_shards[%d] must hold %d elements of %s" % (k, q, S, full.dtype))
+                ptrs.append(sh.data_ptr())
+                tensors.append(sh)
+            pptr = ptr_array(ptrs)
+            keep.append(pptr)
+            tensors.append(full)
+        if cs is not None:
+            _dev(cs, "units[%d].compute_shard" % k)
+            if cs.numel() != S or (cdt is not None and cs.dtype != cdt):
+                raise ValueError("units[%d].compute_shard must hold %d elements of %s" % (k, S, cdt))
+            tensors.append(cs)
+        table[k] = Unit(master.data_ptr(), m.data_ptr(), v.data_ptr(), gptr, pptr,
+                        full.data_ptr() if full is not None else None,
+                        cs.data_ptr() if cs is not None else None, S)
+    _same_device(tensors)
+    args = (table, len(units), world, int(rank), dtype_code(gdt), int(bool(fp32_reduce)),
+            dtype_code(cdt or torch.float32), ctypes.byref(hp), _stream(stream, device))
+    fn = N.lib().fsdp_step_units
+
+    def call():
+        with torch.cuda.device(device):
+            check("fsdp_step_units", fn(*args))
+
+    call.keep = (keep, table, hp, tensors)   # the C side reads these host arrays at every call
+    return call
 
 
 def fsdp_unshard_gather(shards, full=None, stream=None):

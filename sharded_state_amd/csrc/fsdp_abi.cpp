@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -96,24 +97,145 @@ fsdp::AdamScalars adam_scalars(const fsdp_adamw_hp& hp) {
     return s;
 }
 
-// Shared validation of the N gradient inputs; fills the block pointers.
-int check_grads(const void* const* rank_grads, int32_t world, int32_t rank, int64_t S, int grad_dt,
-                std::vector<const void*>& blocks, std::vector<Range>& in_ranges) {
+// Shared validation of world / rank / shard size.
+int check_world(int32_t world, int32_t rank, int64_t S) {
     if (world < 1 || world > FSDP_MAX_WORLD)
         return fail(FSDP_E_INVAL, "world = %d outside [1, %d]", world, FSDP_MAX_WORLD);
     if (rank < 0 || rank >= world) return fail(FSDP_E_INVAL, "rank = %d outside [0, %d)", rank, world);
     if (S < 0) return fail(FSDP_E_INVAL, "shard_numel = %lld < 0", (long long)S);
+    return FSDP_OK;
+}
+
+// Rank `rank`'s block of each rank's gradient, recorded as inputs.
+int grad_blocks(const void* const* rank_grads, int32_t world, int32_t rank, int64_t S, int grad_dt,
+                std::vector<const void*>& blocks, std::vector<Range>& ins) {
     if (!valid_dtype(grad_dt)) return fail(FSDP_E_DTYPE, "grad dtype %d unsupported", grad_dt);
-    if (S > 0 && !rank_grads) return fail(FSDP_E_INVAL, "rank_grads is NULL");
+    blocks.assign(world, nullptr);
+    if (S == 0) return FSDP_OK;
+    if (!rank_grads) return fail(FSDP_E_INVAL, "rank_grads is NULL");
     const int64_t g = dt_size(grad_dt);
-    blocks.resize(world);
     for (int q = 0; q < world; ++q) {
-        const void* base = S > 0 ? rank_grads[q] : nullptr;
-        if (S > 0 && !base) return fail(FSDP_E_INVAL, "rank_grads[%d] is NULL", q);
-        blocks[q] = base ? (const char*)base + (int64_t)rank * S * g : nullptr;
-        in_ranges.push_back(range(blocks[q], S, g));
+        if (!rank_grads[q]) return fail(FSDP_E_INVAL, "rank_grads[%d] is NULL", q);
+        blocks[q] = (const char*)rank_grads[q] + (int64_t)rank * S * g;
+        ins.push_back(range(blocks[q], S, g));
     }
     return FSDP_OK;
+}
+
+// No two outputs overlap and no output overlaps an input (all non-empty).
+bool disjoint(std::vector<Range> outs, const std::vector<Range>& ins) {
+    outs.erase(std::remove_if(outs.begin(), outs.end(), [](const Range& r) { return r.n == 0; }), outs.end());
+    std::sort(outs.begin(), outs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < outs.size(); ++i)
+        if (outs[i].lo < outs[i - 1].lo + outs[i - 1].n) return false;
+    for (const Range& r : ins) {
+        if (r.n == 0) continue;
+        // the last output starting below r's end is the only one that can reach into r
+        auto it = std::lower_bound(outs.begin(), outs.end(), r.lo + r.n,
+                                   [](const Range& a, uintptr_t v) { return a.lo < v; });
+        if (it != outs.begin() && overlaps(*(it - 1), r)) return false;
+    }
+    return true;
+}
+
+// One unit of an AdamW launch: validated, with its pointer tables.
+struct UnitBuild {
+    std::vector<const void*> grads;
+    std::vector<const void*> psrc;
+    std::vector<void*> pdst;
+    fsdp::UnitArgs a{};
+};
+
+// Validate unit `idx` (fused step; with full_out the all-gather too) and fill ub.
+int build_unit(const char* fn, int idx, float* master, float* exp_avg, float* exp_avg_sq,
+               const void* const* rank_grads, int32_t world, int32_t rank, int grad_dt, int compute_dt,
+               int64_t S, void* compute_shard, const void* const* peer_shards, void* full_out, bool gather,
+               UnitBuild& ub, std::vector<Range>& ins, std::vector<Range>& outs) {
+    int rc = check_world(world, rank, S);
+    if (rc) return rc;
+    rc = grad_blocks(rank_grads, world, rank, S, grad_dt, ub.grads, ins);
+    if (rc) return rc;
+    ub.a.grads = ub.grads.data();
+    ub.a.S = S;
+    if (S == 0) return FSDP_OK;
+    if (!master || !exp_avg || !exp_avg_sq)
+        return fail(FSDP_E_INVAL, "%s: unit %d: master, exp_avg and exp_avg_sq must be non-NULL", fn, idx);
+    const int64_t cs = dt_size(compute_dt);
+    void* own = compute_shard;
+    void* out2 = nullptr;
+    if (gather) {
+        if (!full_out) return fail(FSDP_E_INVAL, "%s: unit %d: full_out is NULL", fn, idx);
+        if (world > 1 && !peer_shards) return fail(FSDP_E_INVAL, "%s: unit %d: peer_shards is NULL", fn, idx);
+        const int64_t bytes = S * cs;
+        for (int q = 0; q < world; ++q) {
+            char* slot = (char*)full_out + (int64_t)q * bytes;
+            outs.push_back(range(slot, S, cs));
+            if (q == rank) continue;
+            if (!peer_shards[q]) return fail(FSDP_E_INVAL, "%s: unit %d: peer_shards[%d] is NULL", fn, idx, q);
+            ub.psrc.push_back(peer_shards[q]);
+            ub.pdst.push_back(slot);
+            ins.push_back(range(peer_shards[q], S, cs));
+        }
+        own = (char*)full_out + (int64_t)rank * bytes;
+        out2 = compute_shard;
+        if (out2) outs.push_back(range(out2, S, cs));
+    } else if (own) {
+        outs.push_back(range(own, S, cs));
+    }
+    outs.push_back(range(master, S, 4));
+    outs.push_back(range(exp_avg, S, 4));
+    outs.push_back(range(exp_avg_sq, S, 4));
+
+    bool vec = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) && (!own || aligned16(own)) &&
+               (!out2 || aligned16(out2));
+    for (int q = 0; q < world; ++q) vec = vec && aligned16(ub.grads[q]);
+    for (size_t j = 0; j < ub.psrc.size(); ++j) vec = vec && aligned16(ub.psrc[j]) && aligned16(ub.pdst[j]);
+    ub.a.peer_src = ub.psrc.data();
+    ub.a.peer_dst = ub.pdst.data();
+    ub.a.p = master;
+    ub.a.m = exp_avg;
+    ub.a.v = exp_avg_sq;
+    ub.a.out = own;
+    ub.a.out2 = out2;
+    ub.a.nvec = vec ? S / 8 : 0;
+    return FSDP_OK;
+}
+
+int check_hp(const char* fn, const fsdp_adamw_hp* hp) {
+    if (!hp) return fail(FSDP_E_INVAL, "%s: hp is NULL", fn);
+    if (hp->step < 1) return fail(FSDP_E_INVAL, "%s: hp->step = %lld < 1", fn, (long long)hp->step);
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+        return fail(FSDP_E_INVAL, "%s: betas must lie in [0, 1)", fn);
+    return FSDP_OK;
+}
+
+// Launch the validated units (one grid per table of units).
+int launch_built(const char* fn, std::vector<UnitBuild>& units, int32_t world, int grad_dt,
+                 int32_t fp32_reduce, int compute_dt, bool gather, const fsdp_adamw_hp* hp,
+                 const std::vector<Range>& ins, const std::vector<Range>& outs, void* stream) {
+    if (!disjoint(outs, ins)) return fail(FSDP_E_ALIAS, "%s: an output overlaps an input or another output", fn);
+    std::vector<fsdp::UnitArgs> args;
+    args.reserve(units.size());
+    for (UnitBuild& u : units) {
+        u.a.grads = u.grads.data();
+        u.a.peer_src = u.psrc.data();
+        u.a.peer_dst = u.pdst.data();
+        if (u.a.S > 0) args.push_back(u.a);
+    }
+    if (args.empty()) return ok();
+    fsdp::UnitLaunch L;
+    L.world = world;
+    L.grad_dt = grad_dt;
+    L.fp32_reduce = fp32_reduce != 0;
+    L.compute_dt = compute_dt;
+    L.gather = gather;
+    L.rs = reduce_scalars(world);
+    L.as = adam_scalars(*hp);
+    L.stream = stream;
+    (void)hipGetLastError();
+    hipError_t e = fsdp::launch_units(args.data(), (int)args.size(), L);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    return ok();
 }
 
 }  // namespace
@@ -223,7 +345,9 @@ int fsdp_reduce_scatter_local(const void* const* rank_grads, int32_t world, int3
                               void* grad_shard_out, void* stream) {
     std::vector<const void*> blocks;
     std::vector<Range> ins;
-    int rc = check_grads(rank_grads, world, rank, shard_numel, grad_dt, blocks, ins);
+    int rc = check_world(world, rank, shard_numel);
+    if (rc) return rc;
+    rc = grad_blocks(rank_grads, world, rank, shard_numel, grad_dt, blocks, ins);
     if (rc) return rc;
     const int out_dt = (fp32_reduce || grad_dt == FSDP_F32) ? FSDP_F32 : grad_dt;
     if (shard_numel == 0) return ok();
@@ -234,12 +358,11 @@ int fsdp_reduce_scatter_local(const void* const* rank_grads, int32_t world, int3
 
     bool vec = aligned16(grad_shard_out);
     for (int q = 0; q < world; ++q) vec = vec && aligned16(blocks[q]);
-    fsdp::FusedArgs a{};
+    fsdp::ReduceArgs a{};
     a.grads = blocks.data();
     a.world = world;
     a.grad_dt = grad_dt;
     a.fp32_reduce = fp32_reduce != 0;
-    a.compute_dt = out_dt;
     a.S = shard_numel;
     a.nvec = vec ? shard_numel / 8 : 0;
     a.out = grad_shard_out;
@@ -247,118 +370,66 @@ int fsdp_reduce_scatter_local(const void* const* rank_grads, int32_t world, int3
     a.cus = cu_count();
     a.stream = stream;
     (void)hipGetLastError();
-    hipError_t e = fsdp::launch_fused(a, false);
+    hipError_t e = fsdp::launch_reduce_scatter(a);
     if (e != hipSuccess) return hip_fail(e, "reduce-scatter launch");
     return ok();
 }
-
-}  // extern "C"
-
-namespace {
-
-// Validation and launch shared by fsdp_sharded_adamw and fsdp_step_unit.
-// own_out: this rank's compute destination (compute shard, or its slot of the
-// full buffer); out2: optional second destination; peers: the unit step's
-// (src, dst) copies.
-int adamw_common(const char* fn, float* master, float* exp_avg, float* exp_avg_sq,
-                 const void* const* rank_grads, int32_t world, int32_t rank, int grad_dt,
-                 int32_t fp32_reduce, int compute_dt, int64_t S, const fsdp_adamw_hp* hp,
-                 void* own_out, void* out2, const std::vector<const void*>& peer_src,
-                 const std::vector<void*>& peer_dst, void* stream) {
-    std::vector<const void*> blocks;
-    std::vector<Range> ins;
-    int rc = check_grads(rank_grads, world, rank, S, grad_dt, blocks, ins);
-    if (rc) return rc;
-    if (!valid_dtype(compute_dt)) return fail(FSDP_E_DTYPE, "%s: compute dtype %d unsupported", fn, compute_dt);
-    if (!hp) return fail(FSDP_E_INVAL, "%s: hp is NULL", fn);
-    if (hp->step < 1) return fail(FSDP_E_INVAL, "%s: hp->step = %lld < 1", fn, (long long)hp->step);
-    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
-        return fail(FSDP_E_INVAL, "%s: betas must lie in [0, 1)", fn);
-    if (S == 0) return ok();
-    if (!master || !exp_avg || !exp_avg_sq)
-        return fail(FSDP_E_INVAL, "%s: master, exp_avg and exp_avg_sq must be non-NULL", fn);
-    const int64_t cs = dt_size(compute_dt);
-    for (size_t j = 0; j < peer_src.size(); ++j)
-        ins.push_back(range(peer_src[j], S, cs));
-    std::vector<Range> outs = {range(master, S, 4), range(exp_avg, S, 4), range(exp_avg_sq, S, 4),
-                               range(own_out, own_out ? S : 0, cs), range(out2, out2 ? S : 0, cs)};
-    for (size_t j = 0; j < peer_dst.size(); ++j) outs.push_back(range(peer_dst[j], S, cs));
-    for (size_t i = 0; i < outs.size(); ++i) {
-        for (size_t j = i + 1; j < outs.size(); ++j)
-            if (overlaps(outs[i], outs[j])) return fail(FSDP_E_ALIAS, "%s: output buffers overlap", fn);
-        for (size_t q = 0; q < ins.size(); ++q)
-            if (overlaps(outs[i], ins[q])) return fail(FSDP_E_ALIAS, "%s: an output overlaps an input", fn);
-    }
-
-    bool vec = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) &&
-               (!own_out || aligned16(own_out)) && (!out2 || aligned16(out2));
-    for (int q = 0; q < world; ++q) vec = vec && aligned16(blocks[q]);
-    for (size_t j = 0; j < peer_src.size(); ++j) vec = vec && aligned16(peer_src[j]) && aligned16(peer_dst[j]);
-    fsdp::FusedArgs a{};
-    a.grads = blocks.data();
-    a.world = world;
-    a.grad_dt = grad_dt;
-    a.fp32_reduce = fp32_reduce != 0;
-    a.compute_dt = compute_dt;
-    a.S = S;
-    a.nvec = vec ? S / 8 : 0;
-    a.p = master;
-    a.m = exp_avg;
-    a.v = exp_avg_sq;
-    a.out = own_out;
-    a.out2 = out2;
-    a.peer_src = peer_src.data();
-    a.peer_dst = peer_dst.data();
-    a.npeers = (int)peer_src.size();
-    a.rs = reduce_scalars(world);
-    a.as = adam_scalars(*hp);
-    a.cus = cu_count();
-    a.stream = stream;
-    (void)hipGetLastError();
-    hipError_t e = fsdp::launch_fused(a, true);
-    if (e != hipSuccess) return hip_fail(e, "kernel launch");
-    return ok();
-}
-
-}  // namespace
-
-extern "C" {
 
 int fsdp_sharded_adamw(float* master, float* exp_avg, float* exp_avg_sq, const void* const* rank_grads,
                        int32_t world, int32_t rank, fsdp_dtype grad_dt, int32_t fp32_reduce,
                        void* compute_shard, fsdp_dtype compute_dt, int64_t shard_numel,
                        const fsdp_adamw_hp* hp, void* stream) {
-    static const std::vector<const void*> no_src;
-    static const std::vector<void*> no_dst;
-    return adamw_common("fsdp_sharded_adamw", master, exp_avg, exp_avg_sq, rank_grads, world, rank,
-                        grad_dt, fp32_reduce, compute_dt, shard_numel, hp, compute_shard, nullptr,
-                        no_src, no_dst, stream);
+    const char* fn = "fsdp_sharded_adamw";
+    if (!valid_dtype(compute_dt)) return fail(FSDP_E_DTYPE, "%s: compute dtype %d unsupported", fn, (int)compute_dt);
+    int rc = check_hp(fn, hp);
+    if (rc) return rc;
+    std::vector<UnitBuild> units(1);
+    std::vector<Range> ins, outs;
+    rc = build_unit(fn, 0, master, exp_avg, exp_avg_sq, rank_grads, world, rank, grad_dt, compute_dt, shard_numel,
+                    compute_shard, nullptr, nullptr, false, units[0], ins, outs);
+    if (rc) return rc;
+    return launch_built(fn, units, world, grad_dt, fp32_reduce, compute_dt, false, hp, ins, outs, stream);
 }
 
 int fsdp_step_unit(float* master, float* exp_avg, float* exp_avg_sq, const void* const* rank_grads,
                    int32_t world, int32_t rank, fsdp_dtype grad_dt, int32_t fp32_reduce,
                    const void* const* peer_shards, void* full_out, fsdp_dtype compute_dt,
                    int64_t shard_numel, void* compute_shard, const fsdp_adamw_hp* hp, void* stream) {
-    if (world < 1 || world > FSDP_MAX_WORLD)
-        return fail(FSDP_E_INVAL, "world = %d outside [1, %d]", world, FSDP_MAX_WORLD);
-    if (rank < 0 || rank >= world) return fail(FSDP_E_INVAL, "rank = %d outside [0, %d)", rank, world);
-    if (!valid_dtype(compute_dt)) return fail(FSDP_E_DTYPE, "compute dtype %d unsupported", (int)compute_dt);
-    std::vector<const void*> src;
-    std::vector<void*> dst;
-    if (shard_numel > 0) {
-        if (!full_out) return fail(FSDP_E_INVAL, "full_out is NULL");
-        if (world > 1 && !peer_shards) return fail(FSDP_E_INVAL, "peer_shards is NULL");
-        const int64_t bytes = shard_numel * dt_size(compute_dt);
-        for (int q = 0; q < world; ++q) {
-            if (q == rank) continue;
-            if (!peer_shards[q]) return fail(FSDP_E_INVAL, "peer_shards[%d] is NULL", q);
-            src.push_back(peer_shards[q]);
-            dst.push_back((char*)full_out + (int64_t)q * bytes);
-        }
+    const char* fn = "fsdp_step_unit";
+    if (!valid_dtype(compute_dt)) return fail(FSDP_E_DTYPE, "%s: compute dtype %d unsupported", fn, (int)compute_dt);
+    int rc = check_hp(fn, hp);
+    if (rc) return rc;
+    std::vector<UnitBuild> units(1);
+    std::vector<Range> ins, outs;
+    rc = build_unit(fn, 0, master, exp_avg, exp_avg_sq, rank_grads, world, rank, grad_dt, compute_dt, shard_numel,
+                    compute_shard, peer_shards, full_out, true, units[0], ins, outs);
+    if (rc) return rc;
+    return launch_built(fn, units, world, grad_dt, fp32_reduce, compute_dt, true, hp, ins, outs, stream);
+}
+
+int fsdp_step_units(const fsdp_unit* units, int32_t n_units, int32_t world, int32_t rank, fsdp_dtype grad_dt,
+                    int32_t fp32_reduce, fsdp_dtype compute_dt, const fsdp_adamw_hp* hp, void* stream) {
+    const char* fn = "fsdp_step_units";
+    if (n_units < 0) return fail(FSDP_E_INVAL, "%s: n_units = %d < 0", fn, n_units);
+    if (n_units > 0 && !units) return fail(FSDP_E_INVAL, "%s: units is NULL", fn);
+    if (!valid_dtype(compute_dt)) return fail(FSDP_E_DTYPE, "%s: compute dtype %d unsupported", fn, (int)compute_dt);
+    int rc = check_world(world, rank, 0);
+    if (rc) return rc;
+    rc = check_hp(fn, hp);
+    if (rc) return rc;
+    if (n_units == 0) return ok();
+    const bool gather = units[0].full_out != nullptr;
+    std::vector<UnitBuild> built(n_units);
+    std::vector<Range> ins, outs;
+    for (int32_t k = 0; k < n_units; ++k) {
+        const fsdp_unit& u = units[k];
+        if ((u.full_out != nullptr) != gather)
+            return fail(FSDP_E_INVAL, "%s: unit %d: either every unit has full_out or none", fn, k);
+        rc = build_unit(fn, k, u.master, u.exp_avg, u.exp_avg_sq, u.rank_grads, world, rank, grad_dt, compute_dt,
+                        u.shard_numel, u.compute_shard, u.peer_shards, u.full_out, gather, built[k], ins, outs);
+        if (rc) return rc;
     }
-    void* own = shard_numel > 0 ? (char*)full_out + (int64_t)rank * shard_numel * dt_size(compute_dt) : nullptr;
-    return adamw_common("fsdp_step_unit", master, exp_avg, exp_avg_sq, rank_grads, world, rank, grad_dt,
-                        fp32_reduce, compute_dt, shard_numel, hp, own, compute_shard, src, dst, stream);
+    return launch_built(fn, built, world, grad_dt, fp32_reduce, compute_dt, gather, hp, ins, outs, stream);
 }
 
 int fsdp_unshard_gather(const void* const* shards, int32_t world, int64_t shard_numel, fsdp_dtype dt,

@@ -32,13 +32,33 @@ struct GradPtrs {
     const void* p[NW > 0 ? NW : FSDP_MAX_WORLD];
 };
 
-// Peer compute shards copied into their slots of the full buffer by the
-// one-launch unit step: world - 1 (src, dst) pairs.
+// Table of up to kMax units stepped by one launch of the unit kernel; it
+// travels in the kernel arguments, so each table stays under 4000 bytes.  Gradient pointers are already offset to block
+// `rank`; psrc/pdst are the peers' compute shards and their slots in the full
+// buffer (unit step only).
 template <int NW>
-struct PeerPtrs {
-    const char* src[NW > 1 ? NW - 1 : (NW == 1 ? 1 : FSDP_MAX_WORLD - 1)];
-    char* dst[NW > 1 ? NW - 1 : (NW == 1 ? 1 : FSDP_MAX_WORLD - 1)];
+struct UnitBatch {
+    static constexpr int kMax = NW == 0 ? 1 : (NW <= 2 ? 40 : (NW <= 4 ? 24 : 16));
+    static constexpr int kG = NW > 0 ? NW : FSDP_MAX_WORLD;
+    static constexpr int kP = NW > 1 ? NW - 1 : (NW == 1 ? 1 : FSDP_MAX_WORLD - 1);
+    int32_t count;
+    int32_t world;
+    int32_t npeers;
+    int64_t tile_begin[kMax + 1];
+    int64_t nvec[kMax];
+    int64_t S[kMax];
+    float* p[kMax];
+    float* m[kMax];
+    float* v[kMax];
+    void* out[kMax];
+    void* out2[kMax];
+    const void* g[kMax][kG];
+    const char* psrc[kMax][kP];
+    char* pdst[kMax][kP];
 };
+static_assert(sizeof(UnitBatch<1>) <= 4000 && sizeof(UnitBatch<2>) <= 4000 && sizeof(UnitBatch<4>) <= 4000 &&
+                  sizeof(UnitBatch<8>) <= 4000 && sizeof(UnitBatch<0>) <= 4000,
+              "unit tables travel in kernel arguments");
 
 template <int MAXN>
 struct CopyList {
@@ -54,29 +74,47 @@ struct SegBatch {
     int64_t bytes[kSegMax];
 };
 
-struct FusedArgs {
-    const void* const* grads;  // world pointers, already offset to block `rank`
+// One unit of a unit-kernel launch (host side).
+struct UnitArgs {
+    const void* const* grads;      // world pointers, already offset to block `rank`
+    const void* const* peer_src;   // world - 1 peer compute shards (gather only)
+    void* const* peer_dst;         // their slots in the full buffer
+    float* p;
+    float* m;
+    float* v;
+    void* out;                     // compute shard, or this rank's slot of the full buffer
+    void* out2;                    // optional extra copy of the compute shard
+    int64_t S;
+    int64_t nvec;                  // 8-element vectors on the wide path (0: every element scalar)
+};
+
+// What every unit of one launch shares.
+struct UnitLaunch {
     int world;
     int grad_dt;
     int fp32_reduce;
     int compute_dt;
-    int64_t S;
-    int64_t nvec;              // 8-element vectors taken by the wide path
-    float* p;
-    float* m;
-    float* v;
-    void* out;                 // compute shard (fused) or grad shard (reduce only)
-    void* out2;                // optional second copy of the compute shard, or null
-    const void* const* peer_src;  // world - 1 peer shards (unit step only)
-    void* const* peer_dst;        // their slots in the full buffer
-    int npeers;                // > 0 selects the unit-step kernel (fused + gather)
+    bool gather;
     ReduceScalars rs;
     AdamScalars as;
+    void* stream;
+};
+
+struct ReduceArgs {
+    const void* const* grads;      // world pointers, already offset to block `rank`
+    int world;
+    int grad_dt;
+    int fp32_reduce;
+    int64_t S;
+    int64_t nvec;
+    void* out;
+    ReduceScalars rs;
     int cus;
     void* stream;
 };
 
-hipError_t launch_fused(const FusedArgs& a, bool fused);
+hipError_t launch_units(const UnitArgs* units, int n, const UnitLaunch& L);
+hipError_t launch_reduce_scatter(const ReduceArgs& a);
 void set_launch_events(void* start, void* stop);
 hipError_t launch_gather(const void* const* srcs, void* const* dsts, int n, int64_t bytes, int cus,
                          void* stream);

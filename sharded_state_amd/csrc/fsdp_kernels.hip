@@ -169,13 +169,26 @@ __device__ __forceinline__ void adamw1(float g, float& p, float& m, float& v, co
     v = v1;
 }
 
+// Gradient pointer accessors: gp(q) is rank q's block (shard-relative).
+template <int NW>
+struct GradsOf {                       // single-unit kernels: pointers by value
+    const GradPtrs<NW>& g;
+    __device__ __forceinline__ const void* operator()(int q) const { return g.p[q]; }
+};
+template <int NW>
+struct UnitGrads {                     // batched kernel: unit u of the launch's table
+    const UnitBatch<NW>& B;
+    int u;
+    __device__ __forceinline__ const void* operator()(int q) const { return B.g[u][q]; }
+};
+
 // Accumulate the N rank blocks of 8 elements into acc (all loads first).
-template <int NW, int GF, bool FP32R>
-__device__ __forceinline__ void reduce8(const GradPtrs<NW>& g, int world, int64_t vi, float (&acc)[8]) {
+template <int NW, int GF, bool FP32R, typename GP>
+__device__ __forceinline__ void reduce8(const GP& gp, int world, int64_t vi, float (&acc)[8]) {
     if constexpr (NW > 0) {
         float x[NW][8];
 #pragma unroll
-        for (int q = 0; q < NW; ++q) load8<GF>(g.p[q], vi, x[q]);
+        for (int q = 0; q < NW; ++q) load8<GF>(gp(q), vi, x[q]);
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[k] = x[0][k];
 #pragma unroll
@@ -183,12 +196,12 @@ __device__ __forceinline__ void reduce8(const GradPtrs<NW>& g, int world, int64_
 #pragma unroll
             for (int k = 0; k < 8; ++k) acc[k] = fold<GF, FP32R>(acc[k], x[q][k]);
     } else {
-        load8<GF>(g.p[0], vi, acc);
+        load8<GF>(gp(0), vi, acc);
         int q = 1;
         for (; q + 4 <= world; q += 4) {
             float x[4][8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) load8<GF>(g.p[q + j], vi, x[j]);
+            for (int j = 0; j < 4; ++j) load8<GF>(gp(q + j), vi, x[j]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -196,138 +209,127 @@ __device__ __forceinline__ void reduce8(const GradPtrs<NW>& g, int world, int64_
         }
         for (; q < world; ++q) {
             float x[8];
-            load8<GF>(g.p[q], vi, x);
+            load8<GF>(gp(q), vi, x);
 #pragma unroll
             for (int k = 0; k < 8; ++k) acc[k] = fold<GF, FP32R>(acc[k], x[k]);
         }
     }
 }
 
-template <int NW, int GF, bool FP32R>
-__device__ __forceinline__ float reduce1(const GradPtrs<NW>& g, int world, int64_t i) {
-    constexpr int kN = NW > 0 ? NW : 1;
-    float acc = load1<GF>(g.p[0], i);
-    const int n = NW > 0 ? kN : world;
-    for (int q = 1; q < n; ++q) acc = fold<GF, FP32R>(acc, load1<GF>(g.p[q], i));
+template <int NW, int GF, bool FP32R, typename GP>
+__device__ __forceinline__ float reduce1(const GP& gp, int world, int64_t i) {
+    const int n = NW > 0 ? NW : world;
+    float acc = load1<GF>(gp(0), i);
+    for (int q = 1; q < n; ++q) acc = fold<GF, FP32R>(acc, load1<GF>(gp(q), i));
     return acc;
 }
 
 // ----------------------------------------------------------------- kernels
-// Vector vi (8 elements of CF) of every peer shard: loaded with the unit's
-// other inputs at the top of a loop trip, stored into its slot at the end.
-template <int NW, int CF>
-struct PeerVec {
-    static constexpr int kW = CF == FSDP_F32 ? 2 : 1;      // dwordx4 per 8 elements
-    static constexpr int kN = NW > 1 ? NW - 1 : 1;
-    u32x4 x[kN][kW];
-};
-
-template <int NW, int CF>
-__device__ __forceinline__ void load_peers8(const PeerPtrs<NW>& pe, int64_t vi, PeerVec<NW, CF>& r) {
-    constexpr int kW = PeerVec<NW, CF>::kW;
-    if constexpr (NW > 1) {
-#pragma unroll
-        for (int j = 0; j < NW - 1; ++j)
-#pragma unroll
-            for (int w = 0; w < kW; ++w) r.x[j][w] = ld16(reinterpret_cast<const u32x4*>(pe.src[j]) + kW * vi + w);
-    }
-}
-
-template <int NW, int CF>
-__device__ __forceinline__ void store_peers8(const PeerPtrs<NW>& pe, int64_t vi, const PeerVec<NW, CF>& r) {
-    constexpr int kW = PeerVec<NW, CF>::kW;
-    if constexpr (NW > 1) {
-#pragma unroll
-        for (int j = 0; j < NW - 1; ++j)
-#pragma unroll
-            for (int w = 0; w < kW; ++w) st16(reinterpret_cast<u32x4*>(pe.dst[j]) + kW * vi + w, r.x[j][w]);
-    }
-}
-
-// Generic world size: copy each peer vector directly.
-template <int NW, int CF>
-__device__ __forceinline__ void copy_peers8_generic(const PeerPtrs<NW>& pe, int npeers, int64_t vi) {
-    constexpr int kW = CF == FSDP_F32 ? 2 : 1;
-    for (int j = 0; j < npeers; ++j)
-#pragma unroll
-        for (int w = 0; w < kW; ++w)
-            st16(reinterpret_cast<u32x4*>(pe.dst[j]) + kW * vi + w,
-                 ld16(reinterpret_cast<const u32x4*>(pe.src[j]) + kW * vi + w));
-}
-
-template <int NW, int CF>
-__device__ __forceinline__ void copy_peers1(const PeerPtrs<NW>& pe, int npeers, int64_t i) {
-    const int n = NW > 0 ? NW - 1 : npeers;
-    for (int j = 0; j < n; ++j) {
-        if constexpr (CF == FSDP_F32)
-            reinterpret_cast<uint32_t*>(pe.dst[j])[i] = reinterpret_cast<const uint32_t*>(pe.src[j])[i];
-        else
-            reinterpret_cast<uint16_t*>(pe.dst[j])[i] = reinterpret_cast<const uint16_t*>(pe.src[j])[i];
-    }
-}
-
-// Fused reduce-scatter + AdamW + cast over one shard of S elements, and with
-// GATHER the all-gather of the unit in the same pass: `out` is then this
-// rank's slot of the full buffer and every trip also copies the same 8
-// elements of each peer's compute shard into its slot.
-// g.p[q] points at element 0 of rank q's block `rank` (shard-relative).
-// Elements [0, 8*nvec) take the vector path, [8*nvec, S) the scalar path.
+// One unit's step on vector vi (8 elements): every load first (the N gradient
+// blocks, master/m/v, the peers' compute vectors), then the math, then every
+// store.  With GATHER, `out` is this rank's slot of the full buffer and the
+// peers' vectors are copied into their slots.
 template <int NW, int GF, bool FP32R, int CF, bool GATHER>
-__device__ __forceinline__ void unit_vec(const GradPtrs<NW>& g, const PeerPtrs<NW>& pe, int world,
-                                         int npeers, int64_t vi, float* __restrict__ p,
-                                         float* __restrict__ m, float* __restrict__ v,
-                                         void* __restrict__ out, void* __restrict__ out2,
-                                         const ReduceScalars& rs, const AdamScalars& as) {
-    // every load of the trip first: gradient blocks, master/m/v, peer shards
+__device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t vi, const ReduceScalars& rs,
+                                         const AdamScalars& as) {
+    constexpr int kW = CF == FSDP_F32 ? 2 : 1;      // dwordx4 per 8 compute elements
+    constexpr int kP = NW > 1 ? NW - 1 : 1;
+    float* __restrict__ p = B.p[u];
+    float* __restrict__ m = B.m[u];
+    float* __restrict__ v = B.v[u];
     float acc[8], pp[8], mm[8], vv[8];
-    PeerVec<NW, CF> peer;
-    if constexpr (GATHER && NW > 1) load_peers8<NW, CF>(pe, vi, peer);
+    u32x4 peer[kP][kW];
+    if constexpr (GATHER && NW > 1) {
+#pragma unroll
+        for (int j = 0; j < NW - 1; ++j)
+#pragma unroll
+            for (int w = 0; w < kW; ++w) peer[j][w] = ld16(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + kW * vi + w);
+    }
     load8<FSDP_F32>(p, vi, pp);
     load8<FSDP_F32>(m, vi, mm);
     load8<FSDP_F32>(v, vi, vv);
-    reduce8<NW, GF, FP32R>(g, world, vi, acc);
+    reduce8<NW, GF, FP32R>(UnitGrads<NW>{B, u}, B.world, vi, acc);
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the math
 #pragma unroll
     for (int k = 0; k < 8; ++k) adamw1(finish<NW, GF, FP32R>(acc[k], rs), pp[k], mm[k], vv[k], as);
     store8<FSDP_F32>(p, vi, pp);
     store8<FSDP_F32>(m, vi, mm);
     store8<FSDP_F32>(v, vi, vv);
+    void* out = B.out[u];
+    void* out2 = B.out2[u];
     if constexpr (GATHER) {
         // the unit step always has its own slot; keep the peer stores in the
         // same basic block as their loads so they are not sunk past the math
         store8<CF>(out, vi, pp);
-        if constexpr (NW > 1) store_peers8<NW, CF>(pe, vi, peer);
-        if constexpr (NW == 0) copy_peers8_generic<NW, CF>(pe, npeers, vi);
+        if constexpr (NW > 1) {
+#pragma unroll
+            for (int j = 0; j < NW - 1; ++j)
+#pragma unroll
+                for (int w = 0; w < kW; ++w) st16(reinterpret_cast<u32x4*>(B.pdst[u][j]) + kW * vi + w, peer[j][w]);
+        } else if constexpr (NW == 0) {
+            for (int j = 0; j < B.npeers; ++j)
+#pragma unroll
+                for (int w = 0; w < kW; ++w)
+                    st16(reinterpret_cast<u32x4*>(B.pdst[u][j]) + kW * vi + w,
+                         ld16(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + kW * vi + w));
+        }
     } else {
         if (out) store8<CF>(out, vi, pp);
     }
     if (out2) store8<CF>(out2, vi, pp);
 }
 
-// Fused reduce-scatter + AdamW + cast over one shard of S elements, and with
-// GATHER the all-gather of the unit in the same pass: `out` is then this
-// rank's slot of the full buffer and every trip also copies the same 8
-// elements of each peer's compute shard into its slot.
-// g.p[q] points at element 0 of rank q's block `rank` (shard-relative).
-// Elements [0, 8*nvec) take the vector path, [8*nvec, S) the scalar path.
+// Element i of unit u, one lane (the tail past the last full vector, or every
+// element of a unit whose buffers are not 16-byte aligned).
 template <int NW, int GF, bool FP32R, int CF, bool GATHER>
-__global__ __launch_bounds__(kThreads) void k_rs_adamw_cast(
-    GradPtrs<NW> g, PeerPtrs<NW> pe, int world, int npeers, int64_t S, int64_t nvec,
-    float* __restrict__ p, float* __restrict__ m, float* __restrict__ v, void* __restrict__ out,
-    void* __restrict__ out2, ReduceScalars rs, AdamScalars as) {
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (int64_t vi = t0; vi < nvec; vi += stride)
-        unit_vec<NW, GF, FP32R, CF, GATHER>(g, pe, world, npeers, vi, p, m, v, out, out2, rs, as);
-    for (int64_t i = nvec * 8 + t0; i < S; i += stride) {
-        float pp = p[i], mm = m[i], vv = v[i];
-        adamw1(finish<NW, GF, FP32R>(reduce1<NW, GF, FP32R>(g, world, i), rs), pp, mm, vv, as);
-        p[i] = pp;
-        m[i] = mm;
-        v[i] = vv;
-        if (GATHER || out) store1<CF>(out, i, pp);
-        if (out2) store1<CF>(out2, i, pp);
-        if constexpr (GATHER) copy_peers1<NW, CF>(pe, npeers, i);
+__device__ __forceinline__ void unit_elem(const UnitBatch<NW>& B, int u, int64_t i, const ReduceScalars& rs,
+                                          const AdamScalars& as) {
+    float* __restrict__ p = B.p[u];
+    float* __restrict__ m = B.m[u];
+    float* __restrict__ v = B.v[u];
+    float pp = p[i], mm = m[i], vv = v[i];
+    adamw1(finish<NW, GF, FP32R>(reduce1<NW, GF, FP32R>(UnitGrads<NW>{B, u}, B.world, i), rs), pp, mm, vv, as);
+    p[i] = pp;
+    m[i] = mm;
+    v[i] = vv;
+    if (GATHER || B.out[u]) store1<CF>(B.out[u], i, pp);
+    if (B.out2[u]) store1<CF>(B.out2[u], i, pp);
+    if constexpr (GATHER) {
+        const int n = NW > 0 ? NW - 1 : B.npeers;
+        for (int j = 0; j < n; ++j) {
+            if constexpr (CF == FSDP_F32)
+                reinterpret_cast<uint32_t*>(B.pdst[u][j])[i] = reinterpret_cast<const uint32_t*>(B.psrc[u][j])[i];
+            else
+                reinterpret_cast<uint16_t*>(B.pdst[u][j])[i] = reinterpret_cast<const uint16_t*>(B.psrc[u][j])[i];
+        }
+    }
+}
+
+// Fused reduce-scatter + AdamW + cast (+ all-gather with GATHER) over the
+// shards of up to UnitBatch<NW>::kMax units in one launch.  Workgroup b owns
+// tile b: unit u holds tiles [tile_begin[u], tile_begin[u+1]); its first
+// ceil(nvec/256) tiles are 256 vectors of 8 elements each, the rest 256
+// single elements (the tail, or the whole unit when unaligned).  One launch
+// pays the ramp-up and drain of the grid once for all its units.
+template <int NW, int GF, bool FP32R, int CF, bool GATHER>
+__global__ __launch_bounds__(kThreads) void k_units(UnitBatch<NW> B, ReduceScalars rs, AdamScalars as) {
+    const int64_t tile = blockIdx.x;
+    int lo = 0, hi = B.count - 1;          // unit u with tile_begin[u] <= tile < tile_begin[u+1]
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (B.tile_begin[mid] <= tile) lo = mid;
+        else hi = mid - 1;
+    }
+    const int u = lo;
+    const int64_t j = tile - B.tile_begin[u];
+    const int64_t nvec = B.nvec[u];
+    const int64_t tv = (nvec + kThreads - 1) / kThreads;
+    if (j < tv) {
+        const int64_t vi = j * kThreads + threadIdx.x;
+        if (vi < nvec) unit_vec<NW, GF, FP32R, CF, GATHER>(B, u, vi, rs, as);
+    } else {
+        const int64_t i = nvec * 8 + (j - tv) * kThreads + threadIdx.x;
+        if (i < B.S[u]) unit_elem<NW, GF, FP32R, CF, GATHER>(B, u, i, rs, as);
     }
 }
 
@@ -339,15 +341,16 @@ __global__ __launch_bounds__(kThreads) void k_reduce_scatter(
     constexpr int OF = (FP32R || GF == FSDP_F32) ? FSDP_F32 : GF;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const GradsOf<NW> gp{g};
     for (int64_t vi = t0; vi < nvec; vi += stride) {
         float acc[8];
-        reduce8<NW, GF, FP32R>(g, world, vi, acc);
+        reduce8<NW, GF, FP32R>(gp, world, vi, acc);
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[k] = finish<NW, GF, FP32R>(acc[k], rs);
         store8<OF>(out, vi, acc);
     }
     for (int64_t i = nvec * 8 + t0; i < S; i += stride)
-        store1<OF>(out, i, finish<NW, GF, FP32R>(reduce1<NW, GF, FP32R>(g, world, i), rs));
+        store1<OF>(out, i, finish<NW, GF, FP32R>(reduce1<NW, GF, FP32R>(gp, world, i), rs));
 }
 
 // Copy `bytes` bytes from src to dst (or write zeros when src is null) with the
@@ -441,35 +444,88 @@ static int64_t grid_for(int64_t work, int cus) {
 }
 
 template <int NW, int GF, bool FP32R, int CF>
-static hipError_t fused_go(const FusedArgs& a, const GradPtrs<NW>& g, const PeerPtrs<NW>& pe, dim3 grid) {
-    hipStream_t st = (hipStream_t)a.stream;
-    if (a.npeers > 0)
-        launch(k_rs_adamw_cast<NW, GF, FP32R, CF, true>, grid, dim3(kThreads), st, g, pe, a.world,
-               a.npeers, a.S, a.nvec, a.p, a.m, a.v, a.out, a.out2, a.rs, a.as);
+static hipError_t units_go(const UnitBatch<NW>& B, int64_t tiles, bool gather, const ReduceScalars& rs,
+                           const AdamScalars& as, hipStream_t st) {
+    if (gather)
+        launch(k_units<NW, GF, FP32R, CF, true>, dim3((unsigned)tiles), dim3(kThreads), st, B, rs, as);
     else
-        launch(k_rs_adamw_cast<NW, GF, FP32R, CF, false>, grid, dim3(kThreads), st, g, pe, a.world, 0,
-               a.S, a.nvec, a.p, a.m, a.v, a.out, a.out2, a.rs, a.as);
+        launch(k_units<NW, GF, FP32R, CF, false>, dim3((unsigned)tiles), dim3(kThreads), st, B, rs, as);
     return hipGetLastError();
 }
 
 template <int NW, int GF, bool FP32R>
-static hipError_t fused_cf(const FusedArgs& a, const GradPtrs<NW>& g) {
-    const int64_t work = a.nvec > 0 ? a.nvec : a.S;
-    dim3 grid((unsigned)grid_for(work, a.cus));
-    PeerPtrs<NW> pe{};
-    for (int j = 0; j < a.npeers; ++j) {
-        pe.src[j] = (const char*)a.peer_src[j];
-        pe.dst[j] = (char*)a.peer_dst[j];
+static hipError_t units_cf(const UnitBatch<NW>& B, int64_t tiles, int compute_dt, bool gather,
+                           const ReduceScalars& rs, const AdamScalars& as, hipStream_t st) {
+    switch (compute_dt) {
+    case FSDP_F32: return units_go<NW, GF, FP32R, FSDP_F32>(B, tiles, gather, rs, as, st);
+    case FSDP_F16: return units_go<NW, GF, FP32R, FSDP_F16>(B, tiles, gather, rs, as, st);
+    default: return units_go<NW, GF, FP32R, FSDP_BF16>(B, tiles, gather, rs, as, st);
     }
-    switch (a.compute_dt) {
-    case FSDP_F32: return fused_go<NW, GF, FP32R, FSDP_F32>(a, g, pe, grid);
-    case FSDP_F16: return fused_go<NW, GF, FP32R, FSDP_F16>(a, g, pe, grid);
-    default: return fused_go<NW, GF, FP32R, FSDP_BF16>(a, g, pe, grid);
+}
+
+template <int NW>
+static hipError_t units_batch(const UnitBatch<NW>& B, int64_t tiles, const UnitLaunch& L) {
+    hipStream_t st = (hipStream_t)L.stream;
+    const bool f32r = L.fp32_reduce || L.grad_dt == FSDP_F32;
+    if (L.grad_dt == FSDP_F32) return units_cf<NW, FSDP_F32, true>(B, tiles, L.compute_dt, L.gather, L.rs, L.as, st);
+    if (L.grad_dt == FSDP_F16) {
+        if (f32r) return units_cf<NW, FSDP_F16, true>(B, tiles, L.compute_dt, L.gather, L.rs, L.as, st);
+        return units_cf<NW, FSDP_F16, false>(B, tiles, L.compute_dt, L.gather, L.rs, L.as, st);
+    }
+    if (f32r) return units_cf<NW, FSDP_BF16, true>(B, tiles, L.compute_dt, L.gather, L.rs, L.as, st);
+    return units_cf<NW, FSDP_BF16, false>(B, tiles, L.compute_dt, L.gather, L.rs, L.as, st);
+}
+
+// Pack the units into tables of at most kMax and launch one grid per table.
+template <int NW>
+static hipError_t units_all(const UnitArgs* units, int n, const UnitLaunch& L) {
+    constexpr int kMax = UnitBatch<NW>::kMax;
+    int done = 0;
+    while (done < n) {
+        UnitBatch<NW> B{};
+        B.world = L.world;
+        B.npeers = L.gather ? L.world - 1 : 0;
+        int64_t tiles = 0;
+        int c = 0;
+        for (; c < kMax && done + c < n; ++c) {
+            const UnitArgs& a = units[done + c];
+            B.tile_begin[c] = tiles;
+            B.nvec[c] = a.nvec;
+            B.S[c] = a.S;
+            B.p[c] = a.p;
+            B.m[c] = a.m;
+            B.v[c] = a.v;
+            B.out[c] = a.out;
+            B.out2[c] = a.out2;
+            for (int q = 0; q < L.world; ++q) B.g[c][q] = a.grads[q];
+            for (int q = 0; q < B.npeers; ++q) {
+                B.psrc[c][q] = (const char*)a.peer_src[q];
+                B.pdst[c][q] = (char*)a.peer_dst[q];
+            }
+            tiles += (a.nvec + kThreads - 1) / kThreads + (a.S - 8 * a.nvec + kThreads - 1) / kThreads;
+        }
+        B.count = c;
+        B.tile_begin[c] = tiles;
+        done += c;
+        if (tiles == 0) continue;
+        hipError_t e = units_batch<NW>(B, tiles, L);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_units(const UnitArgs* units, int n, const UnitLaunch& L) {
+    switch (L.world) {
+    case 1: return units_all<1>(units, n, L);
+    case 2: return units_all<2>(units, n, L);
+    case 4: return units_all<4>(units, n, L);
+    case 8: return units_all<8>(units, n, L);
+    default: return units_all<0>(units, n, L);
     }
 }
 
 template <int NW, int GF, bool FP32R>
-static hipError_t rs_only(const FusedArgs& a, const GradPtrs<NW>& g) {
+static hipError_t rs_only(const ReduceArgs& a, const GradPtrs<NW>& g) {
     const int64_t work = a.nvec > 0 ? a.nvec : a.S;
     dim3 grid((unsigned)grid_for(work, a.cus));
     launch(k_reduce_scatter<NW, GF, FP32R>, grid, dim3(kThreads), (hipStream_t)a.stream, g, a.world, a.S,
@@ -478,26 +534,23 @@ static hipError_t rs_only(const FusedArgs& a, const GradPtrs<NW>& g) {
 }
 
 template <int NW>
-static hipError_t dispatch_grad(const FusedArgs& a, bool fused) {
-    GradPtrs<NW> g;
+static hipError_t rs_grad(const ReduceArgs& a) {
+    GradPtrs<NW> g{};
     const int n = NW > 0 ? NW : a.world;
     for (int q = 0; q < n; ++q) g.p[q] = a.grads[q];
     const bool f32r = a.fp32_reduce || a.grad_dt == FSDP_F32;
-#define FSDP_GO(GF, R) return fused ? fused_cf<NW, GF, R>(a, g) : rs_only<NW, GF, R>(a, g)
-    if (a.grad_dt == FSDP_F32) FSDP_GO(FSDP_F32, true);
-    if (a.grad_dt == FSDP_F16) { if (f32r) FSDP_GO(FSDP_F16, true); FSDP_GO(FSDP_F16, false); }
-    if (f32r) FSDP_GO(FSDP_BF16, true);
-    FSDP_GO(FSDP_BF16, false);
-#undef FSDP_GO
+    if (a.grad_dt == FSDP_F32) return rs_only<NW, FSDP_F32, true>(a, g);
+    if (a.grad_dt == FSDP_F16) return f32r ? rs_only<NW, FSDP_F16, true>(a, g) : rs_only<NW, FSDP_F16, false>(a, g);
+    return f32r ? rs_only<NW, FSDP_BF16, true>(a, g) : rs_only<NW, FSDP_BF16, false>(a, g);
 }
 
-hipError_t launch_fused(const FusedArgs& a, bool fused) {
+hipError_t launch_reduce_scatter(const ReduceArgs& a) {
     switch (a.world) {
-    case 1: return dispatch_grad<1>(a, fused);
-    case 2: return dispatch_grad<2>(a, fused);
-    case 4: return dispatch_grad<4>(a, fused);
-    case 8: return dispatch_grad<8>(a, fused);
-    default: return dispatch_grad<0>(a, fused);
+    case 1: return rs_grad<1>(a);
+    case 2: return rs_grad<2>(a);
+    case 4: return rs_grad<4>(a);
+    case 8: return rs_grad<8>(a);
+    default: return rs_grad<0>(a);
     }
 }
 

@@ -128,3 +128,27 @@ def test_step_unit_validation():
     assert _step_unit([0, peer], 0) == N.E_INVAL                     # missing full buffer
     assert _step_unit([0, peer], full, rank=2) == N.E_INVAL
     assert _step_unit([0, peer], FAKE + 8) == N.E_ALIAS              # full overlaps master
+
+
+def test_step_units_validation():
+    L = N.lib()
+    hp = N.AdamWHP()
+    g = N.ptr_array([FAKE + (30 << 30), FAKE + (31 << 30)])
+    peers = N.ptr_array([0, FAKE + (32 << 30)])
+
+    def unit(base, full):
+        return N.Unit(base, base + (1 << 28), base + (2 << 28), g, peers, full, None, 1000)
+
+    a = unit(FAKE, FAKE + (40 << 30))
+    b = unit(FAKE + (1 << 30), FAKE + (41 << 30))
+    table = (N.Unit * 2)(a, b)
+    # distinct units would be launched; here only the error paths are exercised
+    dup = (N.Unit * 2)(a, a)
+    assert L.fsdp_step_units(dup, 2, 2, 0, N.BF16, 0, N.BF16, ctypes.byref(hp), None) == N.E_ALIAS
+    mixed = (N.Unit * 2)(a, unit(FAKE + (2 << 30), 0))
+    assert L.fsdp_step_units(mixed, 2, 2, 0, N.BF16, 0, N.BF16, ctypes.byref(hp), None) == N.E_INVAL
+    cross = (N.Unit * 2)(a, unit(FAKE + (3 << 30), FAKE + (1 << 28)))   # b's full overlaps a's exp_avg
+    assert L.fsdp_step_units(cross, 2, 2, 0, N.BF16, 0, N.BF16, ctypes.byref(hp), None) == N.E_ALIAS
+    assert L.fsdp_step_units(table, -1, 2, 0, N.BF16, 0, N.BF16, ctypes.byref(hp), None) == N.E_INVAL
+    assert L.fsdp_step_units(table, 2, 2, 0, N.BF16, 0, 5, ctypes.byref(hp), None) == N.E_DTYPE
+    assert L.fsdp_step_units(table, 0, 2, 0, N.BF16, 0, N.BF16, ctypes.byref(hp), None) == N.OK

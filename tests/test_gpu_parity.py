@@ -160,3 +160,74 @@ def test_fp16_16bit_reduce_and_fp32_compute_combinations():
         run.run_gpu()
         run.run_oracle()
         run.compare()
+
+
+def _batch_units(runs, rank, gather=True):
+    units = []
+    for r in runs:
+        world, S = r.cfg.world, r.S
+        sl = slice(rank * S, (rank + 1) * S)
+        u = dict(master=r.flat0[sl].clone(), exp_avg=r.m0[sl].clone(), exp_avg_sq=r.v0[sl].clone(),
+                 rank_grads=r.grads)
+        if gather:
+            u["peer_shards"] = [None if q == rank else r.compute[q] for q in range(world)]
+            u["full"] = torch.empty(world * S, dtype=r.cdt_torch, device="cuda")
+        else:
+            u["compute_shard"] = torch.empty(S, dtype=r.cdt_torch, device="cuda")
+        units.append(u)
+    return units
+
+
+@pytest.mark.parametrize("base", ["tiny", "gpt2-large-block", "gpt2-xl-model", "gpt3-13b-block",
+                                  "llama70b-block"])
+def test_step_units_batch_matches_oracle(base):
+    """Units of different sizes -- whole vectors, ragged tails, a single element,
+    blocks that are not 16-byte aligned -- stepped together in one call give the
+    oracle's bytes for every unit."""
+    print("case", base, flush=True)
+    shapes = [gpt_block(24), gpt_block(40), [("t", (1,))], [("t", (7,))], [("t", (1001,))], gpt_block(64)]
+    runs = [UnitRun(scaled(CONFIGS[base], t, name="b%d" % i), block=i) for i, t in enumerate(shapes)]
+    for r in runs:
+        r.run_gpu()
+        r.run_oracle()
+        r.compare()
+    world = runs[0].cfg.world
+    for gather in (True, False):
+        for rank in sorted({0, world - 1}):
+            units = _batch_units(runs, rank, gather)
+            ss.fsdp_step_units(units, rank, runs[0].cfg.fp32_reduce, runs[0].hp())
+            torch.cuda.synchronize()
+            for r, u in zip(runs, units):
+                sl = slice(rank * r.S, (rank + 1) * r.S)
+                assert_bitexact(np_of(u["master"]), r.o_master[sl], "master %s rank %d" % (r.cfg.name, rank))
+                assert_bitexact(np_of(u["exp_avg"]), r.o_m[sl], "exp_avg %s" % r.cfg.name)
+                assert_bitexact(np_of(u["exp_avg_sq"]), r.o_v[sl], "exp_avg_sq %s" % r.cfg.name)
+                if gather:
+                    assert_bitexact(np_of(u["full"]), np_of(r.full), "full %s rank %d" % (r.cfg.name, rank))
+                else:
+                    assert_bitexact(np_of(u["compute_shard"]), np_of(r.compute[rank]), "compute %s" % r.cfg.name)
+
+
+def test_step_units_more_units_than_one_launch_holds():
+    """70 units at N = 2 take two launches (40 + 30) and still match."""
+    runs = [UnitRun(scaled(CONFIGS["gpt2-large-block"], [("t", (97 + 13 * i,))], name="u%d" % i), block=i)
+            for i in range(70)]
+    for r in runs:
+        r.run_gpu()
+        r.run_oracle()
+    units = _batch_units(runs, 1)
+    ss.fsdp_step_units(units, 1, True, runs[0].hp())
+    torch.cuda.synchronize()
+    for r, u in zip(runs, units):
+        sl = slice(r.S, 2 * r.S)
+        assert_bitexact(np_of(u["master"]), r.o_master[sl], "master %s" % r.cfg.name)
+        assert_bitexact(np_of(u["full"]), np_of(r.full), "full %s" % r.cfg.name)
+
+
+def test_step_units_rejects_a_unit_twice():
+    run = UnitRun(scaled(CONFIGS["gpt2-large-block"], gpt_block(16)))
+    run.run_gpu()
+    u = _batch_units([run], 0)[0]
+    with pytest.raises(ss.FsdpError) as e:
+        ss.fsdp_step_units([u, u], 0, True, run.hp())
+    assert e.value.code == -4
