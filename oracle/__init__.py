@@ -61,6 +61,7 @@ def lib():
         L.orc_reduce_scatter.argtypes = [vpp, i32, i32, i64, ci, ci, vp]
         L.orc_adamw_scalars.argtypes = [ctypes.POINTER(_HP), vp]
         L.orc_adamw.argtypes = [vp, vp, vp, vp, i64, ctypes.POINTER(_HP)]
+        L.orc_adamw16.argtypes = [vp, vp, vp, ci, vp, i64, ctypes.POINTER(_HP)]
         L.orc_cast.argtypes = [vp, ci, vp, i64]
         L.orc_gather.argtypes = [vpp, i32, i64, i64, vp]
         L.orc_memory_per_worker.argtypes = [i64, i32, ci, ci, ci, ctypes.c_double,
@@ -190,6 +191,27 @@ def adamw(p, m, v, g, h):
     if not (m.size == n and v.size == n and g.size == n):
         raise ValueError("size mismatch")
     lib().orc_adamw(_ptr(p), _ptr(m), _ptr(v), _ptr(g), n, ctypes.byref(h))
+
+
+def adamw16(p, m, v, g, h, state_dt):
+    """In-place AdamW on 16-bit state (uint16 patterns of state_dt) with fp32 grad g."""
+    for a in (p, m, v):
+        if not (a.dtype == np.uint16 and a.flags.c_contiguous and a.flags.writeable):
+            raise TypeError("p, m, v must be writeable contiguous uint16 patterns")
+    g = _c(g, np.float32)
+    n = p.size
+    if not (m.size == n and v.size == n and g.size == n):
+        raise ValueError("size mismatch")
+    lib().orc_adamw16(_ptr(p), _ptr(m), _ptr(v), DTYPES[state_dt], _ptr(g), n, ctypes.byref(h))
+
+
+def rank_step16(grads, rank, p_shard, m_shard, v_shard, h, grad_dt, fp32_reduce, state_dt):
+    """One rank's step with 16-bit state: reduce-scatter, then AdamW on the
+    16-bit parameter / m / v shard in place (the parameter is the compute copy)."""
+    gshard = reduce_scatter(grads, rank, grad_dt, fp32_reduce)
+    g32 = gshard if gshard.dtype == np.float32 else to_f32(gshard, grad_dt)
+    adamw16(p_shard, m_shard, v_shard, g32, h, state_dt)
+    return gshard
 
 
 def cast(master, dt):

@@ -298,6 +298,36 @@ void orc_adamw(float* p, float* m, float* v, const float* g, int64_t n, const or
 }
 
 /* ------------------------------------------------------------------------ */
+/* AdamW with 16-bit state.  [P3] "Mixed Precision and FSDP": without an fp32 */
+/* master copy the parameters and the Adam state are kept in bf16; [TR]      */
+/* "Adoption paths for FSDP", concern 4: FP16 master weights.  Reading: the  */
+/* update is the fp32 AdamW above applied to the widened 16-bit values, and  */
+/* each new value is rounded once to the state format; the rounded parameter */
+/* is also the compute copy.  p, m, v are 16-bit patterns of format state_dt.*/
+/* ------------------------------------------------------------------------ */
+
+void orc_adamw16(uint16_t* p, uint16_t* m, uint16_t* v, int state_dt, const float* g, int64_t n,
+                 const orc_hp* hp)
+{
+    float s[8];
+    orc_adamw_scalars(hp, s);
+    const float decay = s[0], b1 = s[1], omb1 = s[2], b2 = s[3], omb2 = s[4];
+    const float step_size = s[5], bc2_sqrt = s[6], eps = s[7];
+    for (int64_t i = 0; i < n; ++i) {
+        float pi = load_as_f32(p, state_dt, i), mi = load_as_f32(m, state_dt, i), vi = load_as_f32(v, state_dt, i);
+        float gi = g[i];
+        float p1 = pi * decay;
+        float m1 = (b1 * mi) + (omb1 * gi);
+        float v1 = (b2 * vi) + (omb2 * (gi * gi));
+        float den = (sqrtf(v1) / bc2_sqrt) + eps;
+        float p2 = p1 - (step_size * (m1 / den));
+        store_from_f32(p, state_dt, i, p2);
+        store_from_f32(m, state_dt, i, m1);
+        store_from_f32(v, state_dt, i, v1);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Cast to the compute dtype.  [P3] "Mixed Precision and FSDP": fp32 master  */
 /* weights with a 16-bit compute copy; [P4] fsdp_config mapping:             */
 /* compute_dtype is fp16 under --fp16 and fp32 otherwise.                    */

@@ -229,3 +229,45 @@ def test_elementwise_sample_equals_full_shard(orc):
     sm, sv = np.zeros(200, np.float32), np.zeros(200, np.float32)
     _, sc = orc.elementwise_step([g[pos] for g in grads], sp, sm, sv, h, "bf16", False, "bf16")
     assert sp.tobytes() == ps[idx].tobytes() and sc.tobytes() == c[idx].tobytes()
+
+
+@pytest.mark.parametrize("state_dt", ["bf16", "f16"])
+def test_16bit_state_is_the_fp32_update_rounded_once(orc, state_dt):
+    """AdamW on 16-bit state = the fp32 AdamW on the widened values, each result
+    rounded once to the state format (both pinned above)."""
+    rng = np.random.default_rng(12)
+    n = 50000
+    p16 = orc.f32_to((rng.standard_normal(n) * 0.02).astype(np.float32), state_dt)
+    m16 = orc.f32_to((rng.standard_normal(n) * 1e-3).astype(np.float32), state_dt)
+    v16 = orc.f32_to(np.abs(rng.standard_normal(n) * 1e-4).astype(np.float32), state_dt)
+    g = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    h = orc.hp(step=5)
+    p, m, v = p16.copy(), m16.copy(), v16.copy()
+    orc.adamw16(p, m, v, g, h, state_dt)
+    P, M, V = (orc.to_f32(x, state_dt) for x in (p16, m16, v16))
+    orc.adamw(P, M, V, g, h)
+    assert np.array_equal(p, orc.f32_to(P, state_dt))
+    assert np.array_equal(m, orc.f32_to(M, state_dt))
+    assert np.array_equal(v, orc.f32_to(V, state_dt))
+
+
+def test_16bit_state_against_torch_adamw_in_fp32(orc):
+    """torch.optim.AdamW in fp32 on the widened bf16 state, rounded to bf16,
+    agrees within one bf16 ulp (the fp32 sequences differ by a few fp32 ulps)."""
+    rng = np.random.default_rng(13)
+    n = 20000
+    p16 = orc.f32_to((rng.standard_normal(n) * 0.02).astype(np.float32), "bf16")
+    m16 = orc.f32_to((rng.standard_normal(n) * 1e-3).astype(np.float32), "bf16")
+    v16 = orc.f32_to(np.abs(rng.standard_normal(n) * 1e-4).astype(np.float32), "bf16")
+    g = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    h = orc.hp(step=3)
+    p, m, v = p16.copy(), m16.copy(), v16.copy()
+    orc.adamw16(p, m, v, g, h, "bf16")
+    tp, tm, tv = _torch_adamw(orc.to_f32(p16, "bf16"), [g], h, orc.to_f32(m16, "bf16"),
+                              orc.to_f32(v16, "bf16"), t0=2)
+    for got, ref in ((p, tp), (m, tm), (v, tv)):
+        r = orc.f32_to(ref, "bf16").astype(np.int32)
+        d = np.abs(np.where(r & 0x8000, -(r & 0x7FFF), r & 0x7FFF)
+                   - np.where(got.astype(np.int32) & 0x8000, -(got.astype(np.int32) & 0x7FFF),
+                              got.astype(np.int32) & 0x7FFF))
+        assert d.max() <= 1

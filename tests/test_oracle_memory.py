@@ -15,17 +15,26 @@ def _rows():
         line = line.strip()
         if not line or line.startswith("#"):
             continue
-        f = line.split(None, 6)
-        yield f[0], int(f[1]), int(f[2]), int(f[3]), float(f[4]), float(f[5])
+        f = line.split(None, 9)
+        yield (f[0], int(f[1]), int(f[2]), int(f[3]), float(f[4]), float(f[5]), float(f[6]), float(f[7]),
+               float(f[8]))
 
 
 @pytest.mark.parametrize("row", list(_rows()), ids=lambda r: r[0])
 def test_pages_70b_numbers(orc, row):
-    case, sp, sg, so, printed, exact = row
-    out = orc.memory_per_worker(70_000_000_000, 8, sp, sg, so, 2.0, 2.0, 8.0)
+    case, sp, sg, so, pb, gb, ob, printed, exact = row
+    out = orc.memory_per_worker(70_000_000_000, 8, sp, sg, so, pb, gb, ob)
     total_gb = out.sum() / 1e9
     assert total_gb == pytest.approx(exact, rel=1e-12)
     assert total_gb == pytest.approx(printed, rel=0.015)
+
+
+def test_pure_16bit_state_is_half_of_the_fp32_optimizer_classes(orc):
+    """Dropping the fp32 master and keeping m, v in 16 bits: per shard element
+    2 (parameter) + 4 (m, v) bytes against 2 + 12 with fp32 master, m, v."""
+    pure = orc.memory_per_worker(855_638_016, 8, 1, 1, 1, 2, 0, 4).sum()
+    mixed = orc.memory_per_worker(855_638_016, 8, 1, 1, 1, 2, 0, 12).sum()
+    assert pure * 14 == mixed * 6
 
 
 @pytest.mark.parametrize("numel,world", [(1_000_000, 2), (19_677_440, 2), (7, 3), (1, 8), (855_638_016, 8)])
