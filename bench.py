@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--workload", default="gpt2-large-block",
                     help="gpt2-large-block (default), gpt2-xl-model, gpt3-13b-block, llama70b-block, tiny")
     ap.add_argument("--pipeline", choices=["units", "unit", "separate"], default="units")
+    ap.add_argument("--state", choices=["f32", "bf16", "f16"], default="f32",
+                    help="optimizer state: fp32 master/m/v (default) or 16-bit parameter/m/v with no fp32 "
+                         "master (the parameter shard is the compute shard)")
     ap.add_argument("--streams", type=int, default=1,
                     help="alternate independent units over this many HIP streams (default priority), "
                          "so one unit's tail overlaps the next unit's head")
@@ -70,11 +73,14 @@ def parse():
     return ap.parse_args()
 
 
-def sizes(cfg, pipeline):
+def sizes(cfg, pipeline, state="f32"):
     """(fused kernel bytes, whole-step bytes) per shard element."""
     g = 4 if cfg.grad_dt == "f32" else 2
     c = 4 if cfg.compute_dt == "f32" else 2
     N, G = cfg.world, cfg.gathers
+    if state != "f32":               # 16-bit parameter, m, v; the parameter is the compute copy
+        fused = N * g + 12 + c + 2 * (N - 1) * c
+        return fused, fused + (G - 1) * 2 * N * c
     if pipeline == "separate":
         fused = N * g + 24 + c
         return fused, fused + G * 2 * N * c
@@ -85,45 +91,54 @@ def sizes(cfg, pipeline):
 class Unit:
     """Rank 0's resident buffers for one distinct block of the pool."""
 
-    def __init__(self, cfg, block, ss, torch, workloads):
+    def __init__(self, cfg, block, ss, torch, workloads, state="f32"):
         dev = "cuda"
         P, Pp, S = ss.fsdp_layout(cfg.numels, cfg.world)
         self.P, self.Pp, self.S = P, Pp, S
+        sd = workloads.TORCH_DTYPE[state]
         params = workloads.param_tensors(cfg, block, dev)
+        if state != "f32":
+            params = [t.to(sd) for t in params]
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record()
         flat = ss.fsdp_flatten_pad(params, cfg.world)
         ev1.record()
         torch.cuda.synchronize()
+        es = 4 if state == "f32" else 2
         self.flatten_ms = ev0.elapsed_time(ev1)
-        self.flatten_bytes = 2 * P * 4 + (Pp - P) * 4
+        self.flatten_bytes = 2 * P * es + (Pp - P) * es
         del params
         self.grads = [workloads.rank_grad(cfg, block, q, Pp, dev) for q in range(cfg.world)]
-        cdt = workloads.TORCH_DTYPE[cfg.compute_dt]
+        cdt = workloads.TORCH_DTYPE[cfg.compute_dt] if state == "f32" else sd
         hp = ss.AdamWHP(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.step)
         # peers' compute shards: the other ranks' own steps on the same unit
         self.peers = []
         for q in range(1, cfg.world):
-            mq, vq = workloads.moments(cfg, block, q * S, S, P, dev)
+            mq, vq = (x.to(sd) for x in workloads.moments(cfg, block, q * S, S, P, dev))
             pq = flat[q * S:(q + 1) * S].clone()
-            cq = torch.empty(S, dtype=cdt, device=dev)
-            ss.fsdp_sharded_adamw(pq, mq, vq, self.grads, q, cfg.fp32_reduce, hp, compute_shard=cq)
+            if state == "f32":
+                cq = torch.empty(S, dtype=cdt, device=dev)
+                ss.fsdp_sharded_adamw(pq, mq, vq, self.grads, q, cfg.fp32_reduce, hp, compute_shard=cq)
+            else:
+                ss.fsdp_step_units([dict(master=pq, exp_avg=mq, exp_avg_sq=vq, rank_grads=self.grads)], q,
+                                   cfg.fp32_reduce, hp)
+                cq = pq
             self.peers.append(cq)
-            del mq, vq, pq
+            del mq, vq
         self.master = flat[:S].clone()
         del flat
-        self.m, self.v = workloads.moments(cfg, block, 0, S, P, dev)
-        self.compute = torch.empty(S, dtype=cdt, device=dev)
+        self.m, self.v = (x.to(sd) for x in workloads.moments(cfg, block, 0, S, P, dev))
+        self.compute = torch.empty(S, dtype=cdt, device=dev) if state == "f32" else self.master
         self.full = torch.empty(Pp, dtype=cdt, device=dev)
         torch.cuda.synchronize()
 
 
-def cpu_baseline(cfg, unit, budget_s, np_of_bytes):
+def cpu_baseline(cfg, unit, budget_s, np_of_bytes, state="f32"):
     """The oracle, single-threaded on one host core, on rank 0's step of one
     resident block, repeated until the budget is spent."""
     import numpy as np
     import oracle
-    _, per_elt = sizes(cfg, "separate")
+    _, per_elt = sizes(cfg, "separate", state)
     S = unit.S
     cap = min(S, 4 * 1024 * 1024)          # bounded sample: first `cap` shard elements
     # rank 0's block of each rank's gradient is its first S elements
@@ -142,10 +157,14 @@ def cpu_baseline(cfg, unit, budget_s, np_of_bytes):
         p, m, v = p0.copy(), m0.copy(), v0.copy()
         avg = oracle.grad_average(grads, 0, cap, cfg.grad_dt, cfg.fp32_reduce)
         g32 = avg if avg.dtype == np.float32 else oracle.to_f32(avg, cfg.grad_dt)
-        oracle.adamw(p, m, v, g32, h)
-        comp = oracle.cast(p, cfg.compute_dt)
+        if state == "f32":
+            oracle.adamw(p, m, v, g32, h)
+            comp = oracle.cast(p, cfg.compute_dt)
+        else:
+            oracle.adamw16(p, m, v, g32, h, state)
+            comp = p
         for _ in range(cfg.gathers):
-            oracle.gather([comp] + peers, cfg.compute_dt)
+            oracle.gather([comp] + peers, cfg.compute_dt if state == "f32" else state)
         elems += cap
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -267,8 +286,11 @@ def main():
         return
 
     cfg = workloads.CONFIGS[args.workload]
-    fused_b, per_elt = sizes(cfg, "separate" if args.pipeline == "separate" else "unit")
-    pool = [Unit(cfg, b, ss, torch, workloads) for b in range(cfg.pool)]
+    if args.state != "f32" and args.pipeline == "separate":
+        print("--state %s needs --pipeline units or unit" % args.state, file=sys.stderr)
+        sys.exit(2)
+    fused_b, per_elt = sizes(cfg, "separate" if args.pipeline == "separate" else "unit", args.state)
+    pool = [Unit(cfg, b, ss, torch, workloads, args.state) for b in range(cfg.pool)]
     S = pool[0].S
     stream = torch.cuda.current_stream()
     streams = [stream] + [torch.cuda.Stream() for _ in range(max(1, args.streams) - 1)]
@@ -276,6 +298,8 @@ def main():
     hp = ss.AdamWHP(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.step)
     hp_ref = ctypes.byref(hp)
     gcode, ccode = ss.dtype_code(pool[0].grads[0].dtype), ss.dtype_code(pool[0].compute.dtype)
+    scode = ss.dtype_code(pool[0].master.dtype)
+    state16 = args.state != "f32"
     numels = N.i64_array(cfg.numels)
     views = (N.View * len(cfg.numels))()
 
@@ -289,7 +313,7 @@ def main():
         shards = N.ptr_array([u.compute.data_ptr()] + [q.data_ptr() for q in u.peers])
         peer_tab = N.ptr_array([0] + [q.data_ptr() for q in u.peers])
         full = ctypes.c_void_p(u.full.data_ptr())
-        persistent = u.compute.data_ptr() if G > 1 else None
+        persistent = u.compute.data_ptr() if (G > 1 and not state16) else None
         desc = N.Unit(u.master.data_ptr(), u.m.data_ptr(), u.v.data_ptr(), grads, peer_tab,
                       u.full.data_ptr(), persistent, S)
         unflat = (numels, len(cfg.numels), u.Pp, views, None, ccode, None, None)
@@ -308,8 +332,8 @@ def main():
             batch = slots[bounds[j]:bounds[j + 1]]
             st = st_handles[j % len(st_handles)]
             table = (N.Unit * len(batch))(*[per_unit[i]["desc"] for i in batch])
-            first = (lib.fsdp_step_units, (table, len(batch), cfg.world, 0, gcode, int(cfg.fp32_reduce), ccode,
-                                           hp_ref, st))
+            first = (lib.fsdp_step_units, (table, len(batch), cfg.world, 0, gcode, int(cfg.fp32_reduce), scode,
+                                           ccode, hp_ref, st))
             trail = [(lib.fsdp_unshard_gather, (per_unit[i]["shards"], cfg.world, S, ccode, per_unit[i]["full"], st))
                      for i in batch for _ in range(G - 1)]
             trail += [(lib.fsdp_unflatten_views, per_unit[i]["views"]) for i in batch]
@@ -318,7 +342,13 @@ def main():
         for j, i in enumerate(slots):
             d = per_unit[i]
             st = st_handles[j % len(st_handles)] if args.streams > 1 else st_handles[0]
-            if args.pipeline == "unit":
+            if args.pipeline == "unit" and state16:
+                table = (N.Unit * 1)(d["desc"])
+                first = (lib.fsdp_step_units, (table, 1, cfg.world, 0, gcode, int(cfg.fp32_reduce), scode, ccode,
+                                               hp_ref, st))
+                d["table"] = table
+                trail = [(lib.fsdp_unshard_gather, (d["shards"], cfg.world, S, ccode, d["full"], st))] * (G - 1)
+            elif args.pipeline == "unit":
                 first = (lib.fsdp_step_unit, (d["p"], d["m"], d["v"], d["grads"], cfg.world, 0, gcode,
                                               int(cfg.fp32_reduce), d["peer_tab"], d["full"], ccode, S,
                                               d["persistent"], hp_ref, st))
@@ -406,7 +436,7 @@ def main():
             if t.dtype in (torch.float16, torch.bfloat16):
                 return t.view(torch.int16).numpy().view(np.uint16)
             return t.numpy()
-        cpu = cpu_baseline(cfg, pool[0], args.cpu_seconds, np_of_bytes)
+        cpu = cpu_baseline(cfg, pool[0], args.cpu_seconds, np_of_bytes, args.state)
 
     flat_ms = statistics.fmean(u.flatten_ms for u in pool)
     out = {
@@ -415,6 +445,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "config": {"workload": "%s x%d" % (cfg.name, cfg.blocks), "pipeline": args.pipeline,
+                   "state_dtype": args.state,
                    "streams": len(streams),
                    "world": cfg.world, "rank": 0,
                    "shard_numel": S, "unit_numel": pool[0].P, "blocks_per_step": cfg.blocks,

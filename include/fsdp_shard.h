@@ -51,7 +51,7 @@ extern "C" {
 
 #define FSDP_API __attribute__((visibility("default")))
 
-#define FSDP_ABI_VERSION 1
+#define FSDP_ABI_VERSION 2
 #define FSDP_MAX_WORLD 128
 
 typedef enum fsdp_dtype {
@@ -204,15 +204,18 @@ FSDP_API int fsdp_step_unit(float* master, float* exp_avg, float* exp_avg_sq,
                             int64_t shard_numel, void* compute_shard, const fsdp_adamw_hp* hp,
                             void* stream);
 
-/* One unit of a batched step (fsdp_step_units). */
+/* One unit of a batched step (fsdp_step_units).  The state buffers have the
+ * call's state dtype: fp32 master / m / v, or with 16-bit state the 16-bit
+ * parameter shard (also the compute shard) and 16-bit m / v. */
 typedef struct fsdp_unit {
-    float* master;                   /* device fp32, shard_numel, updated in place */
-    float* exp_avg;                  /* device fp32, shard_numel, updated in place */
-    float* exp_avg_sq;               /* device fp32, shard_numel, updated in place */
+    void* master;                    /* device, shard_numel of state_dt, updated in place */
+    void* exp_avg;                   /* device, shard_numel of state_dt, updated in place */
+    void* exp_avg_sq;                /* device, shard_numel of state_dt, updated in place */
     const void* const* rank_grads;   /* host array [world] of device pointers, world*shard_numel each */
     const void* const* peer_shards;  /* host array [world] (entry `rank` ignored), or NULL without full_out */
     void* full_out;                  /* device, world*shard_numel of compute dtype, or NULL: no all-gather */
-    void* compute_shard;             /* device, shard_numel of compute dtype, or NULL */
+    void* compute_shard;             /* device, shard_numel of compute dtype, or NULL (must be NULL with
+                                        16-bit state) */
     int64_t shard_numel;
 } fsdp_unit;
 
@@ -224,14 +227,21 @@ typedef struct fsdp_unit {
  * as by fsdp_step_unit (when units[k].full_out is set: fused reduce-scatter,
  * AdamW, cast, all-gather) or as by fsdp_sharded_adamw (when it is NULL, with
  * compute_shard as the compute output); every unit of a call must take the
- * same form.  All units share world, rank, dtypes and hp.  Units are packed
- * into launches of up to 40 (world <= 2), 24 (world 4) or 16 (world 8) units;
- * other world sizes take one launch per unit.  No output of any unit may
- * overlap an input or an output of any unit (FSDP_E_ALIAS): a unit may appear
- * only once per call. */
+ * same form.  All units share world, rank, dtypes and hp.
+ * state_dt: FSDP_F32 for an fp32 master with fp32 m / v (as above), or
+ * FSDP_BF16 / FSDP_F16 for 16-bit parameters and m / v with no fp32 master
+ * ([P3] "Mixed Precision and FSDP", pure bf16, 3P/N per worker; [TR] concern 4,
+ * FP16 master weights): the update is the fp32 sequence above on the widened
+ * values, and the new parameter, m and v are each rounded once to state_dt;
+ * compute_dt must equal state_dt, the parameter shard is the compute shard
+ * (compute_shard NULL), and with full_out the gather copies it.
+ * Units are packed into launches of up to 40 (world <= 2), 24 (world 4) or
+ * 16 (world 8) units; other world sizes take one launch per unit.  No output
+ * of any unit may overlap an input or an output of any unit (FSDP_E_ALIAS): a
+ * unit may appear only once per call. */
 FSDP_API int fsdp_step_units(const fsdp_unit* units, int32_t n_units, int32_t world, int32_t rank,
-                             fsdp_dtype grad_dt, int32_t fp32_reduce, fsdp_dtype compute_dt,
-                             const fsdp_adamw_hp* hp, void* stream);
+                             fsdp_dtype grad_dt, int32_t fp32_reduce, fsdp_dtype state_dt,
+                             fsdp_dtype compute_dt, const fsdp_adamw_hp* hp, void* stream);
 
 /* Per-tensor views of the full buffer.  [P3] "The FSDP Unit" (use_orig_params):
  * tensor k is full[off_k : off_k + numel_k]; the padding belongs to no view.

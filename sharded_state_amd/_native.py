@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libfsdp_shard.so")
 F32, F16, BF16 = 0, 1, 2
 OK, E_INVAL, E_DTYPE, E_SIZE, E_ALIAS, E_HIP = 0, -1, -2, -3, -4, -5
 MAX_WORLD = 128
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class AdamWHP(ctypes.Structure):
@@ -84,7 +84,7 @@ def lib():
                                  i64, vp, ctypes.POINTER(AdamWHP), vp]
     L.fsdp_step_units.restype = ctypes.c_int
     L.fsdp_step_units.argtypes = [ctypes.POINTER(Unit), i32, i32, i32, ctypes.c_int, i32, ctypes.c_int,
-                                  ctypes.POINTER(AdamWHP), vp]
+                                  ctypes.c_int, ctypes.POINTER(AdamWHP), vp]
     L.fsdp_unshard_gather.restype = ctypes.c_int
     L.fsdp_unshard_gather.argtypes = [vpp, i32, i64, ctypes.c_int, vp, vp]
     L.fsdp_unflatten_views.restype = ctypes.c_int

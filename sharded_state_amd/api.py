@@ -222,24 +222,30 @@ def fsdp_step_units(units, rank, fp32_reduce, hp, stream=None):
 
 
 def prepare_step_units(units, rank, fp32_reduce, hp, stream=None):
-    """Marshal a fsdp_step_units call once; the returned callable issues it."""
+    """Marshal a fsdp_step_units call once; the returned callable issues it.
+    The state dtype is the dtype of the units' master tensors: float32 (fp32
+    master, m, v) or bfloat16 / float16 (16-bit parameter, m, v; the parameter
+    shard is the compute shard, so no compute_shard is given)."""
     if not units:
         raise ValueError("units is empty")
     if not isinstance(hp, AdamWHP):
         hp = AdamWHP(**hp)
     world = len(units[0]["rank_grads"])
     gather = units[0].get("full") is not None
+    sdt = units[0]["master"].dtype
+    dtype_code(sdt)
     table = (Unit * len(units))()
     keep = []
-    gdt = cdt = None
+    gdt = None
+    cdt = None if sdt == torch.float32 else sdt
     device = units[0]["master"].device
     tensors = []
     for k, u in enumerate(units):
         master, m, v = u["master"], u["exp_avg"], u["exp_avg_sq"]
         for name, t in (("master", master), ("exp_avg", m), ("exp_avg_sq", v)):
             _dev(t, "units[%d].%s" % (k, name))
-            if t.dtype != torch.float32 or t.numel() != master.numel():
-                raise ValueError("units[%d].%s must be float32 with master's size" % (k, name))
+            if t.dtype != sdt or t.numel() != master.numel():
+                raise ValueError("units[%d].%s must be %s with master's size" % (k, name, sdt))
         S = master.numel()
         grads, w, g_dt = _grads(u["rank_grads"], S)
         if w != world:
@@ -251,11 +257,13 @@ def prepare_step_units(units, rank, fp32_reduce, hp, stream=None):
         cs = u.get("compute_shard")
         if (full is not None) != gather:
             raise ValueError("either every unit has full or none")
+        if sdt != torch.float32 and cs is not None:
+            raise ValueError("with 16-bit state the parameter shard is the compute shard: no compute_shard")
         out_dt = full.dtype if full is not None else (cs.dtype if cs is not None else None)
         if out_dt is not None:
             cdt = cdt or out_dt
             if out_dt != cdt:
-                raise TypeError("every unit's compute dtype must be the same")
+                raise TypeError("every unit's compute dtype must be the same (and equal a 16-bit state dtype)")
         gptr = ptr_array([x.data_ptr() for x in grads])
         keep.append(gptr)
         tensors += grads + [master, m, v]
@@ -289,7 +297,7 @@ def prepare_step_units(units, rank, fp32_reduce, hp, stream=None):
                         full.data_ptr() if full is not None else None,
                         cs.data_ptr() if cs is not None else None, S)
     _same_device(tensors)
-    args = (table, len(units), world, int(rank), dtype_code(gdt), int(bool(fp32_reduce)),
+    args = (table, len(units), world, int(rank), dtype_code(gdt), int(bool(fp32_reduce)), dtype_code(sdt),
             dtype_code(cdt or torch.float32), ctypes.byref(hp), _stream(stream, device))
     fn = N.lib().fsdp_step_units
 

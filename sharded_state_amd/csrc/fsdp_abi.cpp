@@ -147,7 +147,7 @@ struct UnitBuild {
 };
 
 // Validate unit `idx` (fused step; with full_out the all-gather too) and fill ub.
-int build_unit(const char* fn, int idx, float* master, float* exp_avg, float* exp_avg_sq,
+int build_unit(const char* fn, int idx, void* master, void* exp_avg, void* exp_avg_sq, int state_dt,
                const void* const* rank_grads, int32_t world, int32_t rank, int grad_dt, int compute_dt,
                int64_t S, void* compute_shard, const void* const* peer_shards, void* full_out, bool gather,
                UnitBuild& ub, std::vector<Range>& ins, std::vector<Range>& outs) {
@@ -182,9 +182,10 @@ int build_unit(const char* fn, int idx, float* master, float* exp_avg, float* ex
     } else if (own) {
         outs.push_back(range(own, S, cs));
     }
-    outs.push_back(range(master, S, 4));
-    outs.push_back(range(exp_avg, S, 4));
-    outs.push_back(range(exp_avg_sq, S, 4));
+    const int64_t ss = dt_size(state_dt);
+    outs.push_back(range(master, S, ss));
+    outs.push_back(range(exp_avg, S, ss));
+    outs.push_back(range(exp_avg_sq, S, ss));
 
     bool vec = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) && (!own || aligned16(own)) &&
                (!out2 || aligned16(out2));
@@ -211,7 +212,7 @@ int check_hp(const char* fn, const fsdp_adamw_hp* hp) {
 
 // Launch the validated units (one grid per table of units).
 int launch_built(const char* fn, std::vector<UnitBuild>& units, int32_t world, int grad_dt,
-                 int32_t fp32_reduce, int compute_dt, bool gather, const fsdp_adamw_hp* hp,
+                 int32_t fp32_reduce, int state_dt, int compute_dt, bool gather, const fsdp_adamw_hp* hp,
                  const std::vector<Range>& ins, const std::vector<Range>& outs, void* stream) {
     if (!disjoint(outs, ins)) return fail(FSDP_E_ALIAS, "%s: an output overlaps an input or another output", fn);
     std::vector<fsdp::UnitArgs> args;
@@ -228,6 +229,7 @@ int launch_built(const char* fn, std::vector<UnitBuild>& units, int32_t world, i
     L.grad_dt = grad_dt;
     L.fp32_reduce = fp32_reduce != 0;
     L.compute_dt = compute_dt;
+    L.state_dt = state_dt;
     L.gather = gather;
     L.rs = reduce_scalars(world);
     L.as = adam_scalars(*hp);
@@ -385,10 +387,10 @@ int fsdp_sharded_adamw(float* master, float* exp_avg, float* exp_avg_sq, const v
     if (rc) return rc;
     std::vector<UnitBuild> units(1);
     std::vector<Range> ins, outs;
-    rc = build_unit(fn, 0, master, exp_avg, exp_avg_sq, rank_grads, world, rank, grad_dt, compute_dt, shard_numel,
-                    compute_shard, nullptr, nullptr, false, units[0], ins, outs);
+    rc = build_unit(fn, 0, master, exp_avg, exp_avg_sq, FSDP_F32, rank_grads, world, rank, grad_dt, compute_dt,
+                    shard_numel, compute_shard, nullptr, nullptr, false, units[0], ins, outs);
     if (rc) return rc;
-    return launch_built(fn, units, world, grad_dt, fp32_reduce, compute_dt, false, hp, ins, outs, stream);
+    return launch_built(fn, units, world, grad_dt, fp32_reduce, FSDP_F32, compute_dt, false, hp, ins, outs, stream);
 }
 
 int fsdp_step_unit(float* master, float* exp_avg, float* exp_avg_sq, const void* const* rank_grads,
@@ -401,18 +403,23 @@ int fsdp_step_unit(float* master, float* exp_avg, float* exp_avg_sq, const void*
     if (rc) return rc;
     std::vector<UnitBuild> units(1);
     std::vector<Range> ins, outs;
-    rc = build_unit(fn, 0, master, exp_avg, exp_avg_sq, rank_grads, world, rank, grad_dt, compute_dt, shard_numel,
-                    compute_shard, peer_shards, full_out, true, units[0], ins, outs);
+    rc = build_unit(fn, 0, master, exp_avg, exp_avg_sq, FSDP_F32, rank_grads, world, rank, grad_dt, compute_dt,
+                    shard_numel, compute_shard, peer_shards, full_out, true, units[0], ins, outs);
     if (rc) return rc;
-    return launch_built(fn, units, world, grad_dt, fp32_reduce, compute_dt, true, hp, ins, outs, stream);
+    return launch_built(fn, units, world, grad_dt, fp32_reduce, FSDP_F32, compute_dt, true, hp, ins, outs, stream);
 }
 
 int fsdp_step_units(const fsdp_unit* units, int32_t n_units, int32_t world, int32_t rank, fsdp_dtype grad_dt,
-                    int32_t fp32_reduce, fsdp_dtype compute_dt, const fsdp_adamw_hp* hp, void* stream) {
+                    int32_t fp32_reduce, fsdp_dtype state_dt, fsdp_dtype compute_dt, const fsdp_adamw_hp* hp,
+                    void* stream) {
     const char* fn = "fsdp_step_units";
     if (n_units < 0) return fail(FSDP_E_INVAL, "%s: n_units = %d < 0", fn, n_units);
     if (n_units > 0 && !units) return fail(FSDP_E_INVAL, "%s: units is NULL", fn);
+    if (!valid_dtype(state_dt)) return fail(FSDP_E_DTYPE, "%s: state dtype %d unsupported", fn, (int)state_dt);
     if (!valid_dtype(compute_dt)) return fail(FSDP_E_DTYPE, "%s: compute dtype %d unsupported", fn, (int)compute_dt);
+    if (state_dt != FSDP_F32 && compute_dt != state_dt)
+        return fail(FSDP_E_DTYPE, "%s: with 16-bit state the parameter is the compute copy: compute dtype "
+                                  "must equal the state dtype", fn);
     int rc = check_world(world, rank, 0);
     if (rc) return rc;
     rc = check_hp(fn, hp);
@@ -425,11 +432,16 @@ int fsdp_step_units(const fsdp_unit* units, int32_t n_units, int32_t world, int3
         const fsdp_unit& u = units[k];
         if ((u.full_out != nullptr) != gather)
             return fail(FSDP_E_INVAL, "%s: unit %d: either every unit has full_out or none", fn, k);
-        rc = build_unit(fn, k, u.master, u.exp_avg, u.exp_avg_sq, u.rank_grads, world, rank, grad_dt, compute_dt,
-                        u.shard_numel, u.compute_shard, u.peer_shards, u.full_out, gather, built[k], ins, outs);
+        if (state_dt != FSDP_F32 && u.compute_shard)
+            return fail(FSDP_E_INVAL, "%s: unit %d: with 16-bit state the parameter shard is the compute shard; "
+                                      "compute_shard must be NULL", fn, k);
+        rc = build_unit(fn, k, u.master, u.exp_avg, u.exp_avg_sq, state_dt, u.rank_grads, world, rank, grad_dt,
+                        compute_dt, u.shard_numel, u.compute_shard, u.peer_shards, u.full_out, gather, built[k],
+                        ins, outs);
         if (rc) return rc;
     }
-    return launch_built(fn, built, world, grad_dt, fp32_reduce, compute_dt, gather, hp, ins, outs, stream);
+    return launch_built(fn, built, world, grad_dt, fp32_reduce, state_dt, compute_dt, gather, hp, ins, outs,
+                        stream);
 }
 
 int fsdp_unshard_gather(const void* const* shards, int32_t world, int64_t shard_numel, fsdp_dtype dt,

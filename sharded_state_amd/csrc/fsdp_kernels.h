@@ -47,9 +47,9 @@ struct UnitBatch {
     int64_t tile_begin[kMax + 1];
     int64_t nvec[kMax];
     int64_t S[kMax];
-    float* p[kMax];
-    float* m[kMax];
-    float* v[kMax];
+    void* p[kMax];                 // state: fp32 master/m/v, or 16-bit parameter/m/v
+    void* m[kMax];
+    void* v[kMax];
     void* out[kMax];
     void* out2[kMax];
     const void* g[kMax][kG];
@@ -79,9 +79,9 @@ struct UnitArgs {
     const void* const* grads;      // world pointers, already offset to block `rank`
     const void* const* peer_src;   // world - 1 peer compute shards (gather only)
     void* const* peer_dst;         // their slots in the full buffer
-    float* p;
-    float* m;
-    float* v;
+    void* p;                       // state of format state_dt (UnitLaunch)
+    void* m;
+    void* v;
     void* out;                     // compute shard, or this rank's slot of the full buffer
     void* out2;                    // optional extra copy of the compute shard
     int64_t S;
@@ -94,6 +94,7 @@ struct UnitLaunch {
     int grad_dt;
     int fp32_reduce;
     int compute_dt;
+    int state_dt;                  // FSDP_F32, or the 16-bit format shared with compute_dt
     bool gather;
     ReduceScalars rs;
     AdamScalars as;

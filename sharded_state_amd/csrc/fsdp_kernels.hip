@@ -229,14 +229,14 @@ __device__ __forceinline__ float reduce1(const GP& gp, int world, int64_t i) {
 // blocks, master/m/v, the peers' compute vectors), then the math, then every
 // store.  With GATHER, `out` is this rank's slot of the full buffer and the
 // peers' vectors are copied into their slots.
-template <int NW, int GF, bool FP32R, int CF, bool GATHER>
+template <int NW, int GF, bool FP32R, int CF, bool GATHER, int SF>
 __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t vi, const ReduceScalars& rs,
                                          const AdamScalars& as) {
     constexpr int kW = CF == FSDP_F32 ? 2 : 1;      // dwordx4 per 8 compute elements
     constexpr int kP = NW > 1 ? NW - 1 : 1;
-    float* __restrict__ p = B.p[u];
-    float* __restrict__ m = B.m[u];
-    float* __restrict__ v = B.v[u];
+    void* __restrict__ p = B.p[u];
+    void* __restrict__ m = B.m[u];
+    void* __restrict__ v = B.v[u];
     float acc[8], pp[8], mm[8], vv[8];
     u32x4 peer[kP][kW];
     if constexpr (GATHER && NW > 1) {
@@ -245,16 +245,16 @@ __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t 
 #pragma unroll
             for (int w = 0; w < kW; ++w) peer[j][w] = ld16(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + kW * vi + w);
     }
-    load8<FSDP_F32>(p, vi, pp);
-    load8<FSDP_F32>(m, vi, mm);
-    load8<FSDP_F32>(v, vi, vv);
+    load8<SF>(p, vi, pp);
+    load8<SF>(m, vi, mm);
+    load8<SF>(v, vi, vv);
     reduce8<NW, GF, FP32R>(UnitGrads<NW>{B, u}, B.world, vi, acc);
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the math
 #pragma unroll
     for (int k = 0; k < 8; ++k) adamw1(finish<NW, GF, FP32R>(acc[k], rs), pp[k], mm[k], vv[k], as);
-    store8<FSDP_F32>(p, vi, pp);
-    store8<FSDP_F32>(m, vi, mm);
-    store8<FSDP_F32>(v, vi, vv);
+    store8<SF>(p, vi, pp);
+    store8<SF>(m, vi, mm);
+    store8<SF>(v, vi, vv);
     void* out = B.out[u];
     void* out2 = B.out2[u];
     if constexpr (GATHER) {
@@ -281,17 +281,17 @@ __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t 
 
 // Element i of unit u, one lane (the tail past the last full vector, or every
 // element of a unit whose buffers are not 16-byte aligned).
-template <int NW, int GF, bool FP32R, int CF, bool GATHER>
+template <int NW, int GF, bool FP32R, int CF, bool GATHER, int SF>
 __device__ __forceinline__ void unit_elem(const UnitBatch<NW>& B, int u, int64_t i, const ReduceScalars& rs,
                                           const AdamScalars& as) {
-    float* __restrict__ p = B.p[u];
-    float* __restrict__ m = B.m[u];
-    float* __restrict__ v = B.v[u];
-    float pp = p[i], mm = m[i], vv = v[i];
+    void* __restrict__ p = B.p[u];
+    void* __restrict__ m = B.m[u];
+    void* __restrict__ v = B.v[u];
+    float pp = load1<SF>(p, i), mm = load1<SF>(m, i), vv = load1<SF>(v, i);
     adamw1(finish<NW, GF, FP32R>(reduce1<NW, GF, FP32R>(UnitGrads<NW>{B, u}, B.world, i), rs), pp, mm, vv, as);
-    p[i] = pp;
-    m[i] = mm;
-    v[i] = vv;
+    store1<SF>(p, i, pp);
+    store1<SF>(m, i, mm);
+    store1<SF>(v, i, vv);
     if (GATHER || B.out[u]) store1<CF>(B.out[u], i, pp);
     if (B.out2[u]) store1<CF>(B.out2[u], i, pp);
     if constexpr (GATHER) {
@@ -311,7 +311,10 @@ __device__ __forceinline__ void unit_elem(const UnitBatch<NW>& B, int u, int64_t
 // ceil(nvec/256) tiles are 256 vectors of 8 elements each, the rest 256
 // single elements (the tail, or the whole unit when unaligned).  One launch
 // pays the ramp-up and drain of the grid once for all its units.
-template <int NW, int GF, bool FP32R, int CF, bool GATHER>
+// SF is the state format: FSDP_F32 for fp32 master/m/v with a separate compute
+// copy of format CF, or a 16-bit format (CF == SF) where the parameter shard is
+// itself the compute copy.
+template <int NW, int GF, bool FP32R, int CF, bool GATHER, int SF>
 __global__ __launch_bounds__(kThreads) void k_units(UnitBatch<NW> B, ReduceScalars rs, AdamScalars as) {
     const int64_t tile = blockIdx.x;
     int lo = 0, hi = B.count - 1;          // unit u with tile_begin[u] <= tile < tile_begin[u+1]
@@ -326,10 +329,10 @@ __global__ __launch_bounds__(kThreads) void k_units(UnitBatch<NW> B, ReduceScala
     const int64_t tv = (nvec + kThreads - 1) / kThreads;
     if (j < tv) {
         const int64_t vi = j * kThreads + threadIdx.x;
-        if (vi < nvec) unit_vec<NW, GF, FP32R, CF, GATHER>(B, u, vi, rs, as);
+        if (vi < nvec) unit_vec<NW, GF, FP32R, CF, GATHER, SF>(B, u, vi, rs, as);
     } else {
         const int64_t i = nvec * 8 + (j - tv) * kThreads + threadIdx.x;
-        if (i < B.S[u]) unit_elem<NW, GF, FP32R, CF, GATHER>(B, u, i, rs, as);
+        if (i < B.S[u]) unit_elem<NW, GF, FP32R, CF, GATHER, SF>(B, u, i, rs, as);
     }
 }
 
@@ -443,23 +446,24 @@ static int64_t grid_for(int64_t work, int cus) {
     return want < 1 ? 1 : want;
 }
 
-template <int NW, int GF, bool FP32R, int CF>
+template <int NW, int GF, bool FP32R, int CF, int SF>
 static hipError_t units_go(const UnitBatch<NW>& B, int64_t tiles, bool gather, const ReduceScalars& rs,
                            const AdamScalars& as, hipStream_t st) {
     if (gather)
-        launch(k_units<NW, GF, FP32R, CF, true>, dim3((unsigned)tiles), dim3(kThreads), st, B, rs, as);
+        launch(k_units<NW, GF, FP32R, CF, true, SF>, dim3((unsigned)tiles), dim3(kThreads), st, B, rs, as);
     else
-        launch(k_units<NW, GF, FP32R, CF, false>, dim3((unsigned)tiles), dim3(kThreads), st, B, rs, as);
+        launch(k_units<NW, GF, FP32R, CF, false, SF>, dim3((unsigned)tiles), dim3(kThreads), st, B, rs, as);
     return hipGetLastError();
 }
 
 template <int NW, int GF, bool FP32R>
-static hipError_t units_cf(const UnitBatch<NW>& B, int64_t tiles, int compute_dt, bool gather,
-                           const ReduceScalars& rs, const AdamScalars& as, hipStream_t st) {
-    switch (compute_dt) {
-    case FSDP_F32: return units_go<NW, GF, FP32R, FSDP_F32>(B, tiles, gather, rs, as, st);
-    case FSDP_F16: return units_go<NW, GF, FP32R, FSDP_F16>(B, tiles, gather, rs, as, st);
-    default: return units_go<NW, GF, FP32R, FSDP_BF16>(B, tiles, gather, rs, as, st);
+static hipError_t units_cf(const UnitBatch<NW>& B, int64_t tiles, const UnitLaunch& L, hipStream_t st) {
+    if (L.state_dt == FSDP_F16) return units_go<NW, GF, FP32R, FSDP_F16, FSDP_F16>(B, tiles, L.gather, L.rs, L.as, st);
+    if (L.state_dt == FSDP_BF16) return units_go<NW, GF, FP32R, FSDP_BF16, FSDP_BF16>(B, tiles, L.gather, L.rs, L.as, st);
+    switch (L.compute_dt) {
+    case FSDP_F32: return units_go<NW, GF, FP32R, FSDP_F32, FSDP_F32>(B, tiles, L.gather, L.rs, L.as, st);
+    case FSDP_F16: return units_go<NW, GF, FP32R, FSDP_F16, FSDP_F32>(B, tiles, L.gather, L.rs, L.as, st);
+    default: return units_go<NW, GF, FP32R, FSDP_BF16, FSDP_F32>(B, tiles, L.gather, L.rs, L.as, st);
     }
 }
 
@@ -467,13 +471,13 @@ template <int NW>
 static hipError_t units_batch(const UnitBatch<NW>& B, int64_t tiles, const UnitLaunch& L) {
     hipStream_t st = (hipStream_t)L.stream;
     const bool f32r = L.fp32_reduce || L.grad_dt == FSDP_F32;
-    if (L.grad_dt == FSDP_F32) return units_cf<NW, FSDP_F32, true>(B, tiles, L.compute_dt, L.gather, L.rs, L.as, st);
+    if (L.grad_dt == FSDP_F32) return units_cf<NW, FSDP_F32, true>(B, tiles, L, st);
     if (L.grad_dt == FSDP_F16) {
-        if (f32r) return units_cf<NW, FSDP_F16, true>(B, tiles, L.compute_dt, L.gather, L.rs, L.as, st);
-        return units_cf<NW, FSDP_F16, false>(B, tiles, L.compute_dt, L.gather, L.rs, L.as, st);
+        if (f32r) return units_cf<NW, FSDP_F16, true>(B, tiles, L, st);
+        return units_cf<NW, FSDP_F16, false>(B, tiles, L, st);
     }
-    if (f32r) return units_cf<NW, FSDP_BF16, true>(B, tiles, L.compute_dt, L.gather, L.rs, L.as, st);
-    return units_cf<NW, FSDP_BF16, false>(B, tiles, L.compute_dt, L.gather, L.rs, L.as, st);
+    if (f32r) return units_cf<NW, FSDP_BF16, true>(B, tiles, L, st);
+    return units_cf<NW, FSDP_BF16, false>(B, tiles, L, st);
 }
 
 // Pack the units into tables of at most kMax and launch one grid per table.

@@ -144,11 +144,16 @@ def test_step_units_validation():
     table = (N.Unit * 2)(a, b)
     # distinct units would be launched; here only the error paths are exercised
     dup = (N.Unit * 2)(a, a)
-    assert L.fsdp_step_units(dup, 2, 2, 0, N.BF16, 0, N.BF16, ctypes.byref(hp), None) == N.E_ALIAS
+    assert L.fsdp_step_units(dup, 2, 2, 0, N.BF16, 0, N.F32, N.BF16, ctypes.byref(hp), None) == N.E_ALIAS
     mixed = (N.Unit * 2)(a, unit(FAKE + (2 << 30), 0))
-    assert L.fsdp_step_units(mixed, 2, 2, 0, N.BF16, 0, N.BF16, ctypes.byref(hp), None) == N.E_INVAL
+    assert L.fsdp_step_units(mixed, 2, 2, 0, N.BF16, 0, N.F32, N.BF16, ctypes.byref(hp), None) == N.E_INVAL
     cross = (N.Unit * 2)(a, unit(FAKE + (3 << 30), FAKE + (1 << 28)))   # b's full overlaps a's exp_avg
-    assert L.fsdp_step_units(cross, 2, 2, 0, N.BF16, 0, N.BF16, ctypes.byref(hp), None) == N.E_ALIAS
-    assert L.fsdp_step_units(table, -1, 2, 0, N.BF16, 0, N.BF16, ctypes.byref(hp), None) == N.E_INVAL
-    assert L.fsdp_step_units(table, 2, 2, 0, N.BF16, 0, 5, ctypes.byref(hp), None) == N.E_DTYPE
-    assert L.fsdp_step_units(table, 0, 2, 0, N.BF16, 0, N.BF16, ctypes.byref(hp), None) == N.OK
+    assert L.fsdp_step_units(cross, 2, 2, 0, N.BF16, 0, N.F32, N.BF16, ctypes.byref(hp), None) == N.E_ALIAS
+    assert L.fsdp_step_units(table, -1, 2, 0, N.BF16, 0, N.F32, N.BF16, ctypes.byref(hp), None) == N.E_INVAL
+    assert L.fsdp_step_units(table, 2, 2, 0, N.BF16, 0, N.F32, 5, ctypes.byref(hp), None) == N.E_DTYPE
+    assert L.fsdp_step_units(table, 0, 2, 0, N.BF16, 0, N.F32, N.BF16, ctypes.byref(hp), None) == N.OK
+    # 16-bit state: the parameter is the compute copy
+    assert L.fsdp_step_units(table, 2, 2, 0, N.BF16, 0, N.BF16, N.F16, ctypes.byref(hp), None) == N.E_DTYPE
+    with_cs = (N.Unit * 1)(N.Unit(FAKE, FAKE + (1 << 28), FAKE + (2 << 28), g, peers, FAKE + (40 << 30),
+                                  FAKE + (50 << 30), 1000))
+    assert L.fsdp_step_units(with_cs, 1, 2, 0, N.BF16, 0, N.BF16, N.BF16, ctypes.byref(hp), None) == N.E_INVAL
