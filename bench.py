@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--streams", type=int, default=1,
                     help="alternate independent units over this many HIP streams (default priority), "
                          "so one unit's tail overlaps the next unit's head")
+    ap.add_argument("--checkpoint", default=None, metavar="DIR",
+                    help="also time saving and loading rank 0's shard state of every resident unit as "
+                         "shard files in DIR (sharded-state checkpoint), reported beside the line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample (0 disables it)")
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -438,6 +441,30 @@ def main():
             return t.numpy()
         cpu = cpu_baseline(cfg, pool[0], args.cpu_seconds, np_of_bytes, args.state)
 
+    ckpt = None
+    if args.checkpoint:
+        os.makedirs(args.checkpoint, exist_ok=True)
+        nbytes = sum(3 * u.S * u.master.element_size() for u in pool)
+        torch.cuda.synchronize()
+        t_s = time.perf_counter()
+        paths = []
+        for b, u in enumerate(pool):
+            path = ss.shard_path(os.path.join(args.checkpoint, "%s-unit%d" % (cfg.name, b)), 0)
+            ss.save_shard(path, cfg.numels, cfg.world, 0, u.master, u.m, u.v, step=args.warmup + args.steps,
+                          hp=hp, compute_dtype=u.compute.dtype)
+            paths.append(path)
+        save_s = time.perf_counter() - t_s
+        t_l = time.perf_counter()
+        for path, u in zip(paths, pool):
+            ss.load_shard(path, u.master, u.m, u.v)
+        load_s = time.perf_counter() - t_l
+        for path in paths:
+            os.remove(path)
+        ckpt = {"units": len(pool), "bytes": nbytes, "save_s": round(save_s, 4), "load_s": round(load_s, 4),
+                "save_gbps": round(nbytes / save_s / 1e9, 3), "load_gbps": round(nbytes / load_s / 1e9, 3),
+                "note": "blocking calls: device-to-host through pinned staging, CRC32C, file write + fsync "
+                        "(load: read, CRC32C, host-to-device)"}
+
     flat_ms = statistics.fmean(u.flatten_ms for u in pool)
     out = {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -459,6 +486,7 @@ def main():
                     "gbps": round(pool[0].flatten_bytes / (flat_ms * 1e-3) / 1e9, 1)},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "checkpoint": ckpt,
     }
     print(json.dumps(out))
 

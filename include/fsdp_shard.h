@@ -51,7 +51,7 @@ extern "C" {
 
 #define FSDP_API __attribute__((visibility("default")))
 
-#define FSDP_ABI_VERSION 2
+#define FSDP_ABI_VERSION 3
 #define FSDP_MAX_WORLD 128
 
 typedef enum fsdp_dtype {
@@ -66,7 +66,9 @@ enum {
     FSDP_E_DTYPE = -2,  /* unsupported dtype or dtype combination */
     FSDP_E_SIZE = -3,   /* output capacity too small or inconsistent sizes */
     FSDP_E_ALIAS = -4,  /* an output overlaps an input or another output */
-    FSDP_E_HIP = -5     /* HIP runtime error while enqueueing */
+    FSDP_E_HIP = -5,    /* HIP runtime error while enqueueing */
+    FSDP_E_IO = -6,     /* a file could not be opened, written or renamed */
+    FSDP_E_FORMAT = -7  /* a file is not a shard file, is truncated or fails its checksum */
 };
 
 /* AdamW hyper-parameters of one flat unit.  Flattening puts the whole unit in
@@ -253,6 +255,57 @@ FSDP_API int fsdp_step_units(const fsdp_unit* units, int32_t n_units, int32_t wo
 FSDP_API int fsdp_unflatten_views(const int64_t* numels, int32_t n_tensors, int64_t padded_numel,
                                   fsdp_view* views_out, const void* full, fsdp_dtype dt,
                                   void* const* dsts, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Sharded-state checkpoints.  [P4] "工作原理", checkpoint paragraph: with
+ * --use-sharded-state every rank saves its own local state to a file named
+ * with the suffix -shard{rank} and loads it back the same way (all ranks save);
+ * the default mode consolidates the full state instead, which is a gather of
+ * the shards followed by the per-tensor views.  [P3] "FSDP Checkpointing".
+ *
+ * A shard file holds: a 256-byte header (the fields of fsdp_ckpt_info, the
+ * hyper-parameters at save time, CRC32C checksums), the unit's tensor sizes,
+ * and at a 4096-aligned offset the master, exp_avg and exp_avg_sq shards
+ * (shard_numel elements each, state dtype).  Files are written to
+ * "<path>.tmp", synced and renamed, so the final name never holds a partial
+ * file.  Buffers live in host memory (on_device = 0) or device memory
+ * (on_device = 1, copied through pinned staging on `stream`; the call returns
+ * after the copies completed).  The calls block the calling thread.
+ * ------------------------------------------------------------------------ */
+typedef struct fsdp_ckpt_info {
+    int32_t world;           /* N */
+    int32_t rank;            /* r, 0 <= r < N */
+    int64_t numel;           /* P: elements of the unit's tensors */
+    int64_t padded_numel;    /* P_pad */
+    int64_t shard_numel;     /* S = P_pad / N */
+    fsdp_dtype state_dt;     /* FSDP_F32 master/m/v, or 16-bit parameter/m/v */
+    fsdp_dtype compute_dt;
+    int64_t step;            /* optimizer steps taken so far */
+    fsdp_adamw_hp hp;        /* hyper-parameters (hp.step is not stored; read back as `step`) */
+    int32_t n_tensors;
+} fsdp_ckpt_info;
+
+/* CRC32C (Castagnoli) of n bytes of host memory, as stored in shard files. */
+FSDP_API uint32_t fsdp_crc32c(const void* data, int64_t n);
+
+/* Save one rank's shard state.  numels[info->n_tensors]: the unit's tensor
+ * sizes (host), summing to info->numel.  master/exp_avg/exp_avg_sq:
+ * info->shard_numel elements of info->state_dt each. */
+FSDP_API int fsdp_save_shard(const char* path, const fsdp_ckpt_info* info, const int64_t* numels,
+                             const void* master, const void* exp_avg, const void* exp_avg_sq,
+                             int32_t on_device, void* stream);
+
+/* Read a shard file's header and size table (no payload).  numels_out may be
+ * NULL; otherwise it must hold info_out->n_tensors entries (FSDP_E_SIZE). */
+FSDP_API int fsdp_shard_info(const char* path, fsdp_ckpt_info* info_out, int64_t* numels_out,
+                             int32_t numels_capacity);
+
+/* Load a shard file into master/exp_avg/exp_avg_sq (shard_capacity elements
+ * each at least).  FSDP_E_FORMAT on a bad header, truncation or checksum
+ * mismatch; after a payload mismatch the destinations' contents are
+ * unspecified.  info_out (may be NULL) receives the header. */
+FSDP_API int fsdp_load_shard(const char* path, fsdp_ckpt_info* info_out, void* master, void* exp_avg,
+                             void* exp_avg_sq, int64_t shard_capacity, int32_t on_device, void* stream);
 
 #ifdef __cplusplus
 }

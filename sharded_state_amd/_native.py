@@ -11,9 +11,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfsdp_shard.so")
 
 F32, F16, BF16 = 0, 1, 2
-OK, E_INVAL, E_DTYPE, E_SIZE, E_ALIAS, E_HIP = 0, -1, -2, -3, -4, -5
+OK, E_INVAL, E_DTYPE, E_SIZE, E_ALIAS, E_HIP, E_IO, E_FORMAT = 0, -1, -2, -3, -4, -5, -6, -7
 MAX_WORLD = 128
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class AdamWHP(ctypes.Structure):
@@ -40,6 +40,14 @@ class Unit(ctypes.Structure):
                 ("rank_grads", ctypes.POINTER(ctypes.c_void_p)),
                 ("peer_shards", ctypes.POINTER(ctypes.c_void_p)), ("full_out", ctypes.c_void_p),
                 ("compute_shard", ctypes.c_void_p), ("shard_numel", ctypes.c_int64)]
+
+
+class CkptInfo(ctypes.Structure):
+    """fsdp_ckpt_info: header of a shard file."""
+    _fields_ = [("world", ctypes.c_int32), ("rank", ctypes.c_int32), ("numel", ctypes.c_int64),
+                ("padded_numel", ctypes.c_int64), ("shard_numel", ctypes.c_int64), ("state_dt", ctypes.c_int),
+                ("compute_dt", ctypes.c_int), ("step", ctypes.c_int64), ("hp", AdamWHP),
+                ("n_tensors", ctypes.c_int32)]
 
 
 class FsdpError(RuntimeError):
@@ -89,6 +97,14 @@ def lib():
     L.fsdp_unshard_gather.argtypes = [vpp, i32, i64, ctypes.c_int, vp, vp]
     L.fsdp_unflatten_views.restype = ctypes.c_int
     L.fsdp_unflatten_views.argtypes = [i64p, i32, i64, ctypes.POINTER(View), vp, ctypes.c_int, vpp, vp]
+    L.fsdp_crc32c.restype = ctypes.c_uint32
+    L.fsdp_crc32c.argtypes = [vp, i64]
+    L.fsdp_save_shard.restype = ctypes.c_int
+    L.fsdp_save_shard.argtypes = [ctypes.c_char_p, ctypes.POINTER(CkptInfo), i64p, vp, vp, vp, i32, vp]
+    L.fsdp_shard_info.restype = ctypes.c_int
+    L.fsdp_shard_info.argtypes = [ctypes.c_char_p, ctypes.POINTER(CkptInfo), i64p, i32]
+    L.fsdp_load_shard.restype = ctypes.c_int
+    L.fsdp_load_shard.argtypes = [ctypes.c_char_p, ctypes.POINTER(CkptInfo), vp, vp, vp, i64, i32, vp]
     v = L.fsdp_abi_version()
     if v != ABI_VERSION:
         raise ImportError("libfsdp_shard.so ABI version %d, binding expects %d" % (v, ABI_VERSION))

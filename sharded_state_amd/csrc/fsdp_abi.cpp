@@ -13,15 +13,16 @@
 #include <cstring>
 #include <vector>
 
+#include "fsdp_internal.h"
 #include "fsdp_kernels.h"
 #include "fsdp_shard.h"
 
-namespace {
+namespace fsdp {
 
-thread_local char g_err[512] = "";
+static thread_local char g_err[512] = "";
 
 int fail(int code, const char* fmt, ...) {
-    fsdp::set_launch_events(nullptr, nullptr);   // a failed call consumes pending timing events
+    set_launch_events(nullptr, nullptr);   // a failed call consumes pending timing events
     va_list ap;
     va_start(ap, fmt);
     vsnprintf(g_err, sizeof g_err, fmt, ap);
@@ -30,7 +31,7 @@ int fail(int code, const char* fmt, ...) {
 }
 
 int ok() {
-    fsdp::set_launch_events(nullptr, nullptr);   // consumed even when nothing was launched
+    set_launch_events(nullptr, nullptr);   // consumed even when nothing was launched
     g_err[0] = 0;
     return FSDP_OK;
 }
@@ -41,6 +42,18 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool valid_dtype(int dt) { return dt == FSDP_F32 || dt == FSDP_F16 || dt == FSDP_BF16; }
 int64_t dt_size(int dt) { return dt == FSDP_F32 ? 4 : 2; }
+
+const char* last_error() { return g_err; }
+
+}  // namespace fsdp
+
+namespace {
+
+using fsdp::dt_size;
+using fsdp::fail;
+using fsdp::hip_fail;
+using fsdp::ok;
+using fsdp::valid_dtype;
 
 // Byte range [lo, lo + n) of device memory.
 struct Range {
@@ -246,7 +259,7 @@ extern "C" {
 
 int fsdp_abi_version(void) { return FSDP_ABI_VERSION; }
 
-const char* fsdp_last_error(void) { return g_err; }
+const char* fsdp_last_error(void) { return fsdp::last_error(); }
 
 int fsdp_time_next_launch(void* start_event, void* stop_event) {
     fsdp::set_launch_events(start_event, stop_event);

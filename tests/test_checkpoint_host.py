@@ -1,0 +1,125 @@
+"""Sharded-state checkpoint files on the host (no GPU): CRC32C pinned to the
+published iSCSI test vectors (RFC 3720, appendix B.4) and to a bit-at-a-time
+reference, and save / load of host-resident shard state with every error path
+(truncation, corruption, bad magic, capacity, inconsistent sizes)."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import sharded_state_amd as ss
+from sharded_state_amd import _native as N
+
+
+def _crc(b):
+    buf = ctypes.create_string_buffer(bytes(b), len(b))
+    return N.lib().fsdp_crc32c(buf, len(b))
+
+
+def _crc_bitwise(data):
+    crc = 0xFFFFFFFF
+    for byte in data:
+        crc ^= byte
+        for _ in range(8):
+            crc = (crc >> 1) ^ (0x82F63B78 if crc & 1 else 0)
+    return crc ^ 0xFFFFFFFF
+
+
+def test_crc32c_published_vectors():
+    assert _crc(b"123456789") == 0xE3069283
+    assert _crc(bytes(32)) == 0x8A9136AA
+    assert _crc(bytes([0xFF] * 32)) == 0x62A8AB43
+    assert _crc(bytes(range(32))) == 0x46DD794E
+    assert _crc(bytes(range(31, -1, -1))) == 0x113FDB5C
+
+
+def test_crc32c_matches_bitwise_reference_on_every_length():
+    rng = np.random.default_rng(0)
+    for n in list(range(0, 40)) + [63, 64, 65, 1000, 4099]:
+        data = rng.integers(0, 256, size=n, dtype=np.uint8).tobytes()
+        want = _crc_bitwise(data) if n else 0
+        assert _crc(data) == want, n
+
+
+def _state(S, seed):
+    rng = np.random.default_rng(seed)
+    return [(rng.standard_normal(S) * s).astype(np.float32) for s in (0.02, 1e-3, 1e-6)]
+
+
+def test_host_round_trip(tmp_path):
+    numels = [1000 * 999, 999, 1]
+    P, Pp, S = ss.fsdp_layout(numels, 2)
+    p, m, v = _state(S, 1)
+    path = ss.shard_path(str(tmp_path / "unit"), 1)
+    ss.save_shard(path, numels, 2, 1, p, m, v, step=7, hp=ss.AdamWHP(lr=3e-4, weight_decay=0.1))
+    assert os.path.exists(path) and not os.path.exists(path + ".tmp")
+    info, sizes = ss.shard_info(path)
+    assert sizes == numels
+    assert (info["world"], info["rank"], info["numel"], info["padded_numel"], info["shard_numel"]) == (2, 1, P, Pp, S)
+    assert info["step"] == 7 and abs(info["hp"].lr - np.float32(3e-4)) == 0 and info["hp"].weight_decay == np.float32(0.1)
+    q = [np.empty(S, np.float32) for _ in range(3)]
+    ss.load_shard(path, *q)
+    for a, b in zip((p, m, v), q):
+        assert a.tobytes() == b.tobytes()
+    # payload starts at a 4096-aligned offset after the header and size table
+    raw = open(path, "rb").read()
+    assert len(raw) == 4096 + 3 * 4 * S
+
+
+def _save(tmp_path, S=5003):
+    numels = [S * 2 - 1]
+    p, m, v = _state(S, 2)
+    path = str(tmp_path / "u-shard0")
+    ss.save_shard(path, numels, 2, 0, p, m, v, step=1, hp=ss.AdamWHP())
+    return path, S
+
+
+def _load_code(path, S):
+    q = [np.empty(S, np.float32) for _ in range(3)]
+    try:
+        ss.load_shard(path, *q)
+        return 0
+    except ss.FsdpError as e:
+        return e.code
+
+
+def test_corruption_is_detected(tmp_path):
+    path, S = _save(tmp_path)
+    raw = bytearray(open(path, "rb").read())
+    for where in (4096 + 5, len(raw) - 1, 256 + 3):          # payload, last byte, size table
+        bad = bytearray(raw)
+        bad[where] ^= 0x10
+        open(path, "wb").write(bad)
+        assert _load_code(path, S) == N.E_FORMAT, where
+    open(path, "wb").write(raw[:-100])                          # truncated payload
+    assert _load_code(path, S) == N.E_FORMAT
+    open(path, "wb").write(raw[:100])                           # truncated header
+    assert _load_code(path, S) == N.E_FORMAT
+    bad = bytearray(raw)
+    bad[0:8] = b"NOTSHARD"
+    open(path, "wb").write(bad)
+    assert _load_code(path, S) == N.E_FORMAT
+    open(path, "wb").write(raw)
+    assert _load_code(path, S) == 0
+    assert _load_code(str(tmp_path / "missing"), S) == N.E_IO
+
+
+def test_argument_errors(tmp_path):
+    path, S = _save(tmp_path)
+    small = [np.empty(S - 1, np.float32) for _ in range(3)]
+    with pytest.raises(ss.FsdpError) as e:
+        ss.load_shard(path, *small)
+    assert e.value.code == N.E_SIZE
+    L = N.lib()
+    info = N.CkptInfo(2, 2, 10, 10, 5, N.F32, N.F32, 1, N.AdamWHP(), 1)        # rank out of range
+    assert L.fsdp_save_shard(str(tmp_path / "x").encode(), ctypes.byref(info), N.i64_array([10]),
+                             None, None, None, 0, None) == N.E_INVAL
+    info = N.CkptInfo(2, 0, 10, 12, 5, N.F32, N.F32, 1, N.AdamWHP(), 1)        # padded / shard inconsistent
+    assert L.fsdp_save_shard(str(tmp_path / "x").encode(), ctypes.byref(info), N.i64_array([10]),
+                             None, None, None, 0, None) == N.E_SIZE
+    info = N.CkptInfo(2, 0, 10, 10, 5, N.F32, N.F32, 1, N.AdamWHP(), 1)
+    assert L.fsdp_save_shard(str(tmp_path / "x").encode(), ctypes.byref(info), N.i64_array([9]),
+                             None, None, None, 0, None) == N.E_SIZE                # sizes do not sum to numel
+    assert L.fsdp_save_shard(str(tmp_path / "no" / "dir" / "x").encode(), ctypes.byref(info),
+                             N.i64_array([10]), None, None, None, 0, None) in (N.E_INVAL, N.E_IO)
