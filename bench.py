@@ -8,7 +8,7 @@ per FSDP unit.  One step = every unit slot of the workload, each through
 on synthetic inputs already resident in HBM.  Flatten + pad is an init-time
 step: it is timed separately and reported beside the line.
 
-Three pipelines (--pipeline):
+Four pipelines (--pipeline):
   units     (default) fsdp_step_units: the step of every unit of the workload
             in as few launches as the kernel-argument table allows (up to 40
             units at N <= 2, 16 at N = 8; a unit appears at most once per
@@ -21,6 +21,13 @@ Three pipelines (--pipeline):
             persistent compute shards, so the step also keeps a persistent
             copy of this rank's shard then.
   separate  fsdp_sharded_adamw into a compute shard, then fsdp_unshard_gather.
+  offload   CPU offload of the optimizer step (fsdp_offload_step): the fp32
+            master, m and v of every unit live in pinned host memory; per unit
+            the device reduce-scatter, the copy of the gradient shard to the
+            host, AdamW on the host cores, the copy of the compute shard back,
+            then the G gathers and the views on the device.  `value` uses the
+            bytes per element of `separate`, so it compares the same work;
+            the "offload" object gives the host and PCIe rates it runs at.
 Bytes are algorithmic, per shard element, with g and c the gradient and
 compute element sizes:
   separate:     N*g (read N gradient blocks) + 12 (read master, m, v) + 12
@@ -54,7 +61,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2-large-block",
                     help="gpt2-large-block (default), gpt2-xl-model, gpt3-13b-block, llama70b-block, tiny")
-    ap.add_argument("--pipeline", choices=["units", "unit", "separate"], default="units")
+    ap.add_argument("--pipeline", choices=["units", "unit", "separate", "offload"], default="units")
+    ap.add_argument("--offload-threads", type=int, default=16,
+                    help="host threads of the offloaded AdamW (--pipeline offload)")
+    ap.add_argument("--offload-chunk", type=int, default=0,
+                    help="elements per copy/update chunk of the offloaded step (0: the library's 4 Mi)")
     ap.add_argument("--state", choices=["f32", "bf16", "f16"], default="f32",
                     help="optimizer state: fp32 master/m/v (default) or 16-bit parameter/m/v with no fp32 "
                          "master (the parameter shard is the compute shard)")
@@ -250,6 +261,139 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+def bench_offload(args, cfg, torch, ss, N, workloads):
+    """--pipeline offload: the step of every unit slot with its optimizer state
+    in pinned host memory (fsdp_offload_step_units over batches of distinct
+    units), then the device gathers."""
+    _, per_elt = sizes(cfg, "separate")
+    pool = [Unit(cfg, b, ss, torch, workloads) for b in range(cfg.pool)]
+    S = pool[0].S
+    cdt = pool[0].compute.dtype
+    threads = max(1, args.offload_threads)
+    states = []
+    for u in pool:
+        states.append(ss.OffloadState(u.master, u.grads[0].dtype, cfg.fp32_reduce, cdt, "cuda",
+                                      exp_avg=u.m, exp_avg_sq=u.v))
+        del u.master, u.m, u.v                  # the fp32 state lives on the host only
+    torch.cuda.empty_cache()
+    hp = ss.AdamWHP(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.step)
+    G = cfg.gathers
+    slots = [k % len(pool) for k in range(cfg.blocks)]
+    shard_lists = [[u.compute] + u.peers for u in pool]
+    # batches of distinct units; the copies back and the gathers of a batch run
+    # on a second stream, so the next batch's reduce-scatter and copies to the
+    # host do not queue behind them
+    copy_stream = torch.cuda.Stream()
+    nb = -(-len(slots) // len(pool))
+    bounds = [round(j * len(slots) / nb) for j in range(nb + 1)]
+    batches = []
+    for j in range(nb):
+        ids = slots[bounds[j]:bounds[j + 1]]
+        call = ss.prepare_offload_step_units([(states[i], pool[i].grads, pool[i].compute) for i in ids], 0,
+                                             cfg.fp32_reduce, hp, chunk_numel=args.offload_chunk,
+                                             n_threads=threads, copy_stream=copy_stream)
+        batches.append((call, ids))
+
+    def step():
+        for call, ids in batches:
+            call()
+            with torch.cuda.stream(copy_stream):
+                for i in ids:
+                    for _ in range(G):
+                        ss.fsdp_unshard_gather(shard_lists[i], full=pool[i].full)
+                    ss.fsdp_unflatten_views(pool[i].full, cfg.shapes)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    gbps = per_elt * S * cfg.blocks / (ms_step * 1e-3) / 1e9
+
+    # the parts alone, on unit 0: host AdamW, device-to-host and host-to-device copies
+    st, u = states[0], pool[0]
+    gsz, csz = st.grad_host.element_size(), st.compute_host.element_size()
+    host_b = S * (12 + gsz + 12 + csz)            # read master, m, v, grad; write master, m, v, compute
+    reps = 5
+    t = time.perf_counter()
+    for _ in range(reps):
+        ss.fsdp_host_adamw(st.master, st.exp_avg, st.exp_avg_sq, st.grad_host, hp, compute=st.compute_host,
+                           n_threads=threads)
+    host_s = (time.perf_counter() - t) / reps
+    t = time.perf_counter()
+    ss.fsdp_host_adamw(st.master, st.exp_avg, st.exp_avg_sq, st.grad_host, hp, compute=st.compute_host,
+                       n_threads=1)
+    host1_s = time.perf_counter() - t
+
+    def copy_rate(dst, src):
+        dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        return src.numel() * src.element_size() * reps / (time.perf_counter() - t) / 1e9
+
+    # host memory rates on the same cores: a threaded read-only pass (sum) and
+    # a threaded copy of 1 GiB
+    a = torch.ones(1 << 28, dtype=torch.float32)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    t = time.perf_counter()
+    for _ in range(reps):
+        b.copy_(a)
+    host_copy = 2 * a.numel() * 4 * reps / (time.perf_counter() - t) / 1e9
+    a.sum()
+    t = time.perf_counter()
+    for _ in range(reps):
+        a.sum()
+    host_read = a.numel() * 4 * reps / (time.perf_counter() - t) / 1e9
+    del a, b
+    d2h = copy_rate(st.grad_host, st.grad_dev)
+    h2d = copy_rate(u.compute, st.compute_host)
+    pcie_b = S * (gsz + csz)
+    off = {
+        "threads": threads, "chunk_numel": args.offload_chunk or 4 << 20, "units_per_call": len(batches[0][1]),
+        "host_copy_gbps": round(host_copy, 2), "host_read_gbps": round(host_read, 2),
+        "torch_cpu_threads": torch.get_num_threads(),
+        "host_state_bytes_per_unit": 12 * S, "device_state_bytes_per_unit": 0,
+        "host_adamw_bytes_per_element": 12 + gsz + 12 + csz,
+        "host_adamw_gbps": round(host_b / host_s / 1e9, 2),
+        "host_adamw_ms_per_unit": round(host_s * 1e3, 3),
+        "host_adamw_1thread_gbps": round(host_b / host1_s / 1e9, 2),
+        "pcie_bytes_per_element": gsz + csz,
+        "d2h_copy_gbps": round(d2h, 2), "h2d_copy_gbps": round(h2d, 2),
+        "step_host_gbps": round(host_b * cfg.blocks / (ms_step * 1e-3) / 1e9, 2),
+        "step_host_gbps_with_dma": round((host_b + pcie_b) * cfg.blocks / (ms_step * 1e-3) / 1e9, 2),
+        "step_pcie_gbps": round(pcie_b * cfg.blocks / (ms_step * 1e-3) / 1e9, 2),
+    }
+    # the bound of the offloaded step is host DRAM: the host AdamW's own bytes
+    # plus the copies' DMA into and out of host memory, against the measured
+    # read-only rate of the same cores (no published figure for this host)
+    ach = off["step_host_gbps_with_dma"]
+    roof = {"bound": "host", "achieved": ach, "peak": off["host_read_gbps"], "unit": "GB/s",
+            "frac": round(ach / off["host_read_gbps"], 4), "traffic": None,
+            "kernel": "fsdp_host_adamw (%d threads) + PCIe DMA; peak = threaded host read rate measured in "
+                      "this run" % threads}
+    out = {
+        "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "%s x%d" % (cfg.name, cfg.blocks), "pipeline": "offload", "state_dtype": "f32",
+                   "world": cfg.world, "rank": 0, "shard_numel": S, "blocks_per_step": cfg.blocks,
+                   "distinct_blocks": cfg.pool, "grad_dtype": cfg.grad_dt,
+                   "fp32_reduce_scatter": cfg.fp32_reduce, "compute_dtype": cfg.compute_dt,
+                   "gathers_per_step": G, "bytes_per_shard_element": per_elt},
+        "shard_elements_per_s": round(S * cfg.blocks / (ms_step * 1e-3), 1),
+        "roofline": roof, "offload": off, "cpu_baseline": None,
+    }
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -289,9 +433,12 @@ def main():
         return
 
     cfg = workloads.CONFIGS[args.workload]
-    if args.state != "f32" and args.pipeline == "separate":
+    if args.state != "f32" and args.pipeline in ("separate", "offload"):
         print("--state %s needs --pipeline units or unit" % args.state, file=sys.stderr)
         sys.exit(2)
+    if args.pipeline == "offload":
+        bench_offload(args, cfg, torch, ss, N, workloads)
+        return
     fused_b, per_elt = sizes(cfg, "separate" if args.pipeline == "separate" else "unit", args.state)
     pool = [Unit(cfg, b, ss, torch, workloads, args.state) for b in range(cfg.pool)]
     S = pool[0].S

@@ -51,7 +51,7 @@ extern "C" {
 
 #define FSDP_API __attribute__((visibility("default")))
 
-#define FSDP_ABI_VERSION 3
+#define FSDP_ABI_VERSION 4
 #define FSDP_MAX_WORLD 128
 
 typedef enum fsdp_dtype {
@@ -255,6 +255,82 @@ FSDP_API int fsdp_step_units(const fsdp_unit* units, int32_t n_units, int32_t wo
 FSDP_API int fsdp_unflatten_views(const int64_t* numels, int32_t n_tensors, int64_t padded_numel,
                                   fsdp_view* views_out, const void* full, fsdp_dtype dt,
                                   void* const* dsts, void* stream);
+
+/* ------------------------------------------------------------------------
+ * CPU offload of the optimizer step.  [TR] "Adoption paths for FSDP"
+ * (fairseq, --cpu-offload): the fp32 master copy and the optimizer state move
+ * to host memory and the Adam update runs on the CPU; [P3] "CPU Offloading":
+ * the cost is the PCIe transfer of every step; [P4] flag table and the
+ * single-GPU example (--cpu-offload with the Adam step on the CPU).
+ * The update is the one of fsdp_sharded_adamw, bit for bit.
+ * ------------------------------------------------------------------------ */
+
+/* AdamW on a host shard, on the calling thread plus up to n_threads - 1 worker
+ * threads of the library (AVX2 + F16C when the CPU has them, same IEEE fp32
+ * operation sequence either way; the caller's MXCSR is left as it was).
+ *   master, exp_avg, exp_avg_sq  host fp32, n elements each, updated in place
+ *   grad                         host, n elements of grad_dt (already averaged)
+ *   compute                      host, n elements of compute_dt, or NULL (no cast)
+ * Blocks until done.  FSDP_E_ALIAS if two buffers overlap. */
+FSDP_API int fsdp_host_adamw(float* master, float* exp_avg, float* exp_avg_sq, const void* grad,
+                             fsdp_dtype grad_dt, void* compute, fsdp_dtype compute_dt, int64_t n,
+                             const fsdp_adamw_hp* hp, int32_t n_threads);
+
+/* One unit of an offloaded step (fsdp_offload_step_units).
+ *   master, exp_avg, exp_avg_sq  host fp32, shard_numel each, updated in place
+ *   rank_grads                   host array of `world` device pointers, as in
+ *                                fsdp_reduce_scatter_local
+ *   grad_shard_dev               device, shard_numel of the reduce-scatter output
+ *                                dtype (fp32 when fp32_reduce or fp32 grads)
+ *   grad_shard_host              host, same size and dtype
+ *   compute_host                 host, shard_numel of compute_dt
+ *   compute_dev                  device, shard_numel of compute_dt (e.g. the rank's
+ *                                slot of the full buffer, or the shard that
+ *                                fsdp_unshard_gather reads)
+ * Host buffers should be pinned (hipHostMalloc) for the copies to be
+ * asynchronous; pageable memory works, with copies that block. */
+typedef struct fsdp_offload_unit {
+    float* master;
+    float* exp_avg;
+    float* exp_avg_sq;
+    const void* const* rank_grads;
+    void* grad_shard_dev;
+    void* grad_shard_host;
+    void* compute_host;
+    void* compute_dev;
+    int64_t shard_numel;
+} fsdp_offload_unit;
+
+/* Offloaded step of n_units units of rank `rank`.  Enqueued on `stream`, in
+ * unit order: each unit's device reduce-scatter of block `rank` (as
+ * fsdp_reduce_scatter_local) into grad_shard_dev, then its device-to-host
+ * copies into grad_shard_host in chunks of chunk_numel elements (<= 0: 4 Mi;
+ * rounded up to a multiple of 8).  Then up to n_threads host threads run
+ * fsdp_host_adamw over the chunks in order, each chunk once its copy has
+ * landed; the thread that completes a chunk enqueues the copy of its compute
+ * values to compute_dev, on copy_stream if it is not NULL (copy_stream first
+ * waits for the work already on `stream`, and `stream` waits for copy_stream's
+ * copies before the call returns, so later work on `stream` sees compute_dev),
+ * else on `stream`.
+ * Blocks until the host update of every unit is done; the copies to the device
+ * are enqueued and not waited for (compute_host must stay untouched until
+ * `stream` has passed them).  Every buffer of every unit is distinct
+ * (FSDP_E_ALIAS otherwise), so a unit appears at most once per call.  After a
+ * HIP error reported as FSDP_E_HIP, some units may have been stepped. */
+FSDP_API int fsdp_offload_step_units(const fsdp_offload_unit* units, int32_t n_units, int32_t world,
+                                     int32_t rank, fsdp_dtype grad_dt, int32_t fp32_reduce,
+                                     fsdp_dtype compute_dt, int64_t chunk_numel,
+                                     const fsdp_adamw_hp* hp, int32_t n_threads, void* stream,
+                                     void* copy_stream);
+
+/* fsdp_offload_step_units for one unit, its fields passed one by one. */
+FSDP_API int fsdp_offload_step(float* master, float* exp_avg, float* exp_avg_sq,
+                               const void* const* rank_grads, int32_t world, int32_t rank,
+                               fsdp_dtype grad_dt, int32_t fp32_reduce, void* grad_shard_dev,
+                               void* grad_shard_host, void* compute_host, void* compute_dev,
+                               fsdp_dtype compute_dt, int64_t shard_numel, int64_t chunk_numel,
+                               const fsdp_adamw_hp* hp, int32_t n_threads, void* stream,
+                               void* copy_stream);
 
 /* ------------------------------------------------------------------------
  * Sharded-state checkpoints.  [P4] "工作原理", checkpoint paragraph: with

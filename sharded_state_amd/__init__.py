@@ -23,11 +23,19 @@ from .api import (  # noqa: F401
     view_table,
 )
 from .state import RankState  # noqa: F401
+from .offload import (  # noqa: F401
+    OffloadState,
+    fsdp_host_adamw,
+    fsdp_offload_step,
+    fsdp_offload_step_units,
+    prepare_offload_step_units,
+)
 from .checkpoint import consolidate, load_shard, save_shard, shard_info, shard_path  # noqa: F401
 
 __all__ = [
     "AdamWHP", "FsdpError", "MAX_WORLD", "lib", "dtype_code", "fsdp_layout", "fsdp_flatten_pad",
     "fsdp_reduce_scatter_local", "fsdp_sharded_adamw", "fsdp_step_unit", "fsdp_step_units", "prepare_step_units", "fsdp_unshard_gather",
     "fsdp_unflatten_views", "view_table", "RankState", "save_shard", "load_shard", "shard_info",
-    "shard_path", "consolidate",
+    "shard_path", "consolidate", "fsdp_host_adamw", "fsdp_offload_step", "fsdp_offload_step_units",
+    "prepare_offload_step_units", "OffloadState",
 ]

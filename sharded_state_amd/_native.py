@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libfsdp_shard.so")
 F32, F16, BF16 = 0, 1, 2
 OK, E_INVAL, E_DTYPE, E_SIZE, E_ALIAS, E_HIP, E_IO, E_FORMAT = 0, -1, -2, -3, -4, -5, -6, -7
 MAX_WORLD = 128
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class AdamWHP(ctypes.Structure):
@@ -40,6 +40,14 @@ class Unit(ctypes.Structure):
                 ("rank_grads", ctypes.POINTER(ctypes.c_void_p)),
                 ("peer_shards", ctypes.POINTER(ctypes.c_void_p)), ("full_out", ctypes.c_void_p),
                 ("compute_shard", ctypes.c_void_p), ("shard_numel", ctypes.c_int64)]
+
+
+class OffloadUnit(ctypes.Structure):
+    """fsdp_offload_unit: one unit of an offloaded step."""
+    _fields_ = [("master", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("rank_grads", ctypes.POINTER(ctypes.c_void_p)), ("grad_shard_dev", ctypes.c_void_p),
+                ("grad_shard_host", ctypes.c_void_p), ("compute_host", ctypes.c_void_p),
+                ("compute_dev", ctypes.c_void_p), ("shard_numel", ctypes.c_int64)]
 
 
 class CkptInfo(ctypes.Structure):
@@ -105,6 +113,14 @@ def lib():
     L.fsdp_shard_info.argtypes = [ctypes.c_char_p, ctypes.POINTER(CkptInfo), i64p, i32]
     L.fsdp_load_shard.restype = ctypes.c_int
     L.fsdp_load_shard.argtypes = [ctypes.c_char_p, ctypes.POINTER(CkptInfo), vp, vp, vp, i64, i32, vp]
+    L.fsdp_host_adamw.restype = ctypes.c_int
+    L.fsdp_host_adamw.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, i64, ctypes.POINTER(AdamWHP), i32]
+    L.fsdp_offload_step.restype = ctypes.c_int
+    L.fsdp_offload_step.argtypes = [vp, vp, vp, vpp, i32, i32, ctypes.c_int, i32, vp, vp, vp, vp, ctypes.c_int,
+                                    i64, i64, ctypes.POINTER(AdamWHP), i32, vp, vp]
+    L.fsdp_offload_step_units.restype = ctypes.c_int
+    L.fsdp_offload_step_units.argtypes = [ctypes.POINTER(OffloadUnit), i32, i32, i32, ctypes.c_int, i32,
+                                          ctypes.c_int, i64, ctypes.POINTER(AdamWHP), i32, vp, vp]
     v = L.fsdp_abi_version()
     if v != ABI_VERSION:
         raise ImportError("libfsdp_shard.so ABI version %d, binding expects %d" % (v, ABI_VERSION))

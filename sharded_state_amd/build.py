@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfsdp_shard.so")
 SOURCES = [os.path.join(CSRC, "fsdp_kernels.hip"), os.path.join(CSRC, "fsdp_abi.cpp"),
-           os.path.join(CSRC, "fsdp_ckpt.cpp")]
+           os.path.join(CSRC, "fsdp_ckpt.cpp"), os.path.join(CSRC, "fsdp_offload.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

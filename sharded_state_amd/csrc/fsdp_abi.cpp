@@ -45,6 +45,31 @@ int64_t dt_size(int dt) { return dt == FSDP_F32 ? 4 : 2; }
 
 const char* last_error() { return g_err; }
 
+// AdamW constants: the per-element update uses these fp32 values.
+AdamScalars adam_scalars(const fsdp_adamw_hp& hp) {
+    const double b1 = hp.beta1, b2 = hp.beta2, lr = hp.lr, t = (double)hp.step;
+    const double bias1 = 1.0 - std::pow(b1, t);
+    const double bias2 = 1.0 - std::pow(b2, t);
+    AdamScalars s;
+    s.decay = (float)(1.0 - lr * (double)hp.weight_decay);
+    s.b1 = hp.beta1;
+    s.omb1 = 1.0f - hp.beta1;
+    s.b2 = hp.beta2;
+    s.omb2 = 1.0f - hp.beta2;
+    s.step_size = (float)(lr / bias1);
+    s.bc2_sqrt = (float)std::sqrt(bias2);
+    s.eps = hp.eps;
+    return s;
+}
+
+int check_hp(const char* fn, const fsdp_adamw_hp* hp) {
+    if (!hp) return fail(FSDP_E_INVAL, "%s: hp is NULL", fn);
+    if (hp->step < 1) return fail(FSDP_E_INVAL, "%s: hp->step = %lld < 1", fn, (long long)hp->step);
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+        return fail(FSDP_E_INVAL, "%s: betas must lie in [0, 1)", fn);
+    return FSDP_OK;
+}
+
 }  // namespace fsdp
 
 namespace {
@@ -54,6 +79,8 @@ using fsdp::fail;
 using fsdp::hip_fail;
 using fsdp::ok;
 using fsdp::valid_dtype;
+using fsdp::adam_scalars;
+using fsdp::check_hp;
 
 // Byte range [lo, lo + n) of device memory.
 struct Range {
@@ -91,23 +118,6 @@ fsdp::ReduceScalars reduce_scalars(int world) {
     r.n = (float)world;
     r.inv_n = (float)(1.0 / (double)world);
     return r;
-}
-
-// AdamW constants: the per-element update uses these fp32 values.
-fsdp::AdamScalars adam_scalars(const fsdp_adamw_hp& hp) {
-    const double b1 = hp.beta1, b2 = hp.beta2, lr = hp.lr, t = (double)hp.step;
-    const double bias1 = 1.0 - std::pow(b1, t);
-    const double bias2 = 1.0 - std::pow(b2, t);
-    fsdp::AdamScalars s;
-    s.decay = (float)(1.0 - lr * (double)hp.weight_decay);
-    s.b1 = hp.beta1;
-    s.omb1 = 1.0f - hp.beta1;
-    s.b2 = hp.beta2;
-    s.omb2 = 1.0f - hp.beta2;
-    s.step_size = (float)(lr / bias1);
-    s.bc2_sqrt = (float)std::sqrt(bias2);
-    s.eps = hp.eps;
-    return s;
 }
 
 // Shared validation of world / rank / shard size.
@@ -212,14 +222,6 @@ int build_unit(const char* fn, int idx, void* master, void* exp_avg, void* exp_a
     ub.a.out = own;
     ub.a.out2 = out2;
     ub.a.nvec = vec ? S / 8 : 0;
-    return FSDP_OK;
-}
-
-int check_hp(const char* fn, const fsdp_adamw_hp* hp) {
-    if (!hp) return fail(FSDP_E_INVAL, "%s: hp is NULL", fn);
-    if (hp->step < 1) return fail(FSDP_E_INVAL, "%s: hp->step = %lld < 1", fn, (long long)hp->step);
-    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
-        return fail(FSDP_E_INVAL, "%s: betas must lie in [0, 1)", fn);
     return FSDP_OK;
 }
 

@@ -1,9 +1,13 @@
-// fsdp_internal.h -- status and dtype helpers shared by the host-side sources
-// of libfsdp_shard.so (fsdp_abi.cpp, fsdp_ckpt.cpp).  Not installed.
+// fsdp_internal.h -- status, dtype and optimizer-scalar helpers shared by the
+// host-side sources of libfsdp_shard.so (fsdp_abi.cpp, fsdp_ckpt.cpp,
+// fsdp_offload.cpp).  Not installed.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "fsdp_kernels.h"
+#include "fsdp_shard.h"
 
 namespace fsdp {
 
@@ -16,5 +20,11 @@ int hip_fail(hipError_t e, const char* what);
 bool valid_dtype(int dt);
 int64_t dt_size(int dt);
 const char* last_error();
+// AdamW constants of step hp->step, computed in double and rounded once to fp32
+// (decay = 1 - lr*wd, step_size = lr / (1 - beta1^t), bc2_sqrt = sqrt(1 - beta2^t)).
+AdamScalars adam_scalars(const fsdp_adamw_hp& hp);
+// FSDP_E_INVAL (message prefixed with fn) unless hp is non-NULL, step >= 1 and
+// both betas lie in [0, 1).
+int check_hp(const char* fn, const fsdp_adamw_hp* hp);
 
 }  // namespace fsdp
