@@ -33,6 +33,13 @@ class _HP(ctypes.Structure):
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64)]
 
 
+class _OPT(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("weight_decay", ctypes.c_float), ("momentum", ctypes.c_float),
+                ("dampening", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("rho", ctypes.c_float), ("nesterov", ctypes.c_int32),
+                ("step", ctypes.c_int64)]
+
+
 def lib():
     """Load (building first if needed) the oracle shared library."""
     global _lib
@@ -63,6 +70,9 @@ def lib():
         L.orc_adamw.argtypes = [vp, vp, vp, vp, i64, ctypes.POINTER(_HP)]
         L.orc_adamw16.argtypes = [vp, vp, vp, ci, vp, i64, ctypes.POINTER(_HP)]
         L.orc_cast.argtypes = [vp, ci, vp, i64]
+        L.orc_sgd.argtypes = [vp, vp, vp, i64, ctypes.POINTER(_OPT)]
+        L.orc_adamax.argtypes = [vp, vp, vp, vp, i64, ctypes.POINTER(_OPT)]
+        L.orc_adadelta.argtypes = [vp, vp, vp, vp, i64, ctypes.POINTER(_OPT)]
         L.orc_gather.argtypes = [vpp, i32, i64, i64, vp]
         L.orc_memory_per_worker.argtypes = [i64, i32, ci, ci, ci, ctypes.c_double,
                                             ctypes.c_double, ctypes.c_double, vp]
@@ -212,6 +222,88 @@ def rank_step16(grads, rank, p_shard, m_shard, v_shard, h, grad_dt, fp32_reduce,
     g32 = gshard if gshard.dtype == np.float32 else to_f32(gshard, grad_dt)
     adamw16(p_shard, m_shard, v_shard, g32, h, state_dt)
     return gshard
+
+
+# ---------------------------------------------------------------- other pointwise optimizers
+# Defaults are torch.optim's: SGD lr 1e-3 here (torch has none), Adamax lr 2e-3,
+# betas (0.9, 0.999), eps 1e-8; Adadelta lr 1.0, rho 0.9, eps 1e-6.
+OPT_DEFAULTS = {
+    "sgd": dict(lr=1e-3, weight_decay=0.0, momentum=0.0, dampening=0.0, nesterov=False),
+    "adamax": dict(lr=2e-3, weight_decay=0.0, beta1=0.9, beta2=0.999, eps=1e-8),
+    "adadelta": dict(lr=1.0, weight_decay=0.0, rho=0.9, eps=1e-6),
+}
+
+
+def opt(kind, step=1, **kw):
+    """Hyper-parameters of a pointwise optimizer ("sgd", "adamax", "adadelta")."""
+    d = dict(OPT_DEFAULTS[kind])
+    unknown = set(kw) - set(d)
+    if unknown:
+        raise TypeError("%s takes no %s" % (kind, sorted(unknown)))
+    d.update(kw)
+    return _OPT(d.get("lr", 0.0), d.get("weight_decay", 0.0), d.get("momentum", 0.0), d.get("dampening", 0.0),
+                d.get("beta1", 0.0), d.get("beta2", 0.0), d.get("eps", 0.0), d.get("rho", 0.0),
+                int(bool(d.get("nesterov", False))), int(step))
+
+
+def _state(*arrs):
+    for a in arrs:
+        if not (a.dtype == np.float32 and a.flags.c_contiguous and a.flags.writeable):
+            raise TypeError("parameter and state must be writeable contiguous float32")
+
+
+def sgd(p, buf, g, o):
+    """In-place SGD on fp32 p (and the momentum buffer when o.momentum != 0)."""
+    _state(p)
+    g = _c(g, np.float32)
+    if g.size != p.size:
+        raise ValueError("size mismatch")
+    if o.momentum != 0.0:
+        _state(buf)
+        if buf.size != p.size:
+            raise ValueError("size mismatch")
+    lib().orc_sgd(_ptr(p), _ptr(buf) if o.momentum != 0.0 else None, _ptr(g), p.size, ctypes.byref(o))
+
+
+def adamax(p, m, u, g, o):
+    """In-place Adamax on fp32 p, m (first moment) and u (infinity norm)."""
+    _state(p, m, u)
+    g = _c(g, np.float32)
+    if not (m.size == u.size == g.size == p.size):
+        raise ValueError("size mismatch")
+    lib().orc_adamax(_ptr(p), _ptr(m), _ptr(u), _ptr(g), p.size, ctypes.byref(o))
+
+
+def adadelta(p, v, acc, g, o):
+    """In-place Adadelta on fp32 p, v (squared gradients) and acc (squared updates)."""
+    _state(p, v, acc)
+    g = _c(g, np.float32)
+    if not (v.size == acc.size == g.size == p.size):
+        raise ValueError("size mismatch")
+    lib().orc_adadelta(_ptr(p), _ptr(v), _ptr(acc), _ptr(g), p.size, ctypes.byref(o))
+
+
+def opt_step(kind, p, s1, s2, g, o):
+    """One step of optimizer `kind` ("adamw" takes an hp() as o) with state
+    buffers s1, s2 in the order the library's units hold them."""
+    if kind == "adamw":
+        adamw(p, s1, s2, g, o)
+    elif kind == "sgd":
+        sgd(p, s1, g, o)
+    elif kind == "adamax":
+        adamax(p, s1, s2, g, o)
+    elif kind == "adadelta":
+        adadelta(p, s1, s2, g, o)
+    else:
+        raise ValueError(kind)
+
+
+def rank_step_opt(kind, grads, rank, master_shard, s1, s2, o, grad_dt, fp32_reduce, compute_dt):
+    """rank_step with optimizer `kind`: reduce-scatter, update in place, cast."""
+    gshard = reduce_scatter(grads, rank, grad_dt, fp32_reduce)
+    g32 = gshard if gshard.dtype == np.float32 else to_f32(gshard, grad_dt)
+    opt_step(kind, master_shard, s1, s2, g32, o)
+    return gshard, cast(master_shard, compute_dt)
 
 
 def cast(master, dt):

@@ -328,6 +328,89 @@ void orc_adamw16(uint16_t* p, uint16_t* m, uint16_t* v, int state_dt, const floa
 }
 
 /* ------------------------------------------------------------------------ */
+/* Other pointwise optimizers.  [P4] "限制与兼容性说明": FSDP works with the  */
+/* pointwise optimizers (Adam, AdamW, Adadelta, Adamax, SGD and the like)    */
+/* and not with Adagrad, Adafactor or LAMB; the pages write none of their    */
+/* updates.  Reading: the published algorithms in the form torch.optim       */
+/* documents them (SGD with heavy-ball momentum, dampening and the Nesterov  */
+/* variant, the buffer starting as the first gradient; Adamax, the infinity- */
+/* norm Adam of Kingma & Ba 2015, section 7.1; Adadelta, Zeiler 2012,        */
+/* Algorithm 1, with a learning-rate factor), their weight decay added to    */
+/* the gradient (L2) and skipped when it is 0.  Scalars as for AdamW: fp32   */
+/* hyper-parameters, 1 - beta etc. one fp32 operation, bias terms in double  */
+/* rounded once.                                                             */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    float lr, weight_decay;
+    float momentum, dampening;   /* SGD */
+    float beta1, beta2;          /* Adamax */
+    float eps;                   /* Adamax, Adadelta */
+    float rho;                   /* Adadelta */
+    int32_t nesterov;            /* SGD */
+    int64_t step;                /* t >= 1 */
+} orc_opt;
+
+/* The gradient with L2 weight decay: d = g + wd*p (just g when wd == 0). */
+static float l2_grad(float g, float p, float wd)
+{
+    return wd != 0.0f ? g + (wd * p) : g;
+}
+
+/* SGD.  momentum == 0:  p <- p - lr*d.
+ * momentum mu > 0:  b <- d at t = 1, else b <- mu*b + (1 - dampening)*d;
+ *                   d <- d + mu*b (Nesterov) or d <- b;  p <- p - lr*d.
+ * buf (n elements) is read and written only when mu > 0 (may be NULL else). */
+void orc_sgd(float* p, float* buf, const float* g, int64_t n, const orc_opt* o)
+{
+    const float lr = o->lr, wd = o->weight_decay, mu = o->momentum;
+    const float omd = 1.0f - o->dampening;
+    for (int64_t i = 0; i < n; ++i) {
+        float d = l2_grad(g[i], p[i], wd);
+        if (mu != 0.0f) {
+            float b = o->step == 1 ? d : (mu * buf[i]) + (omd * d);
+            buf[i] = b;
+            d = o->nesterov ? d + (mu * b) : b;
+        }
+        p[i] = p[i] - (lr * d);
+    }
+}
+
+/* Adamax.  m <- beta1*m + (1-beta1)*d;  u <- max(beta2*u, |d| + eps) (NaN if
+ * either is NaN);  p <- p - (lr / (1 - beta1^t)) * (m / u). */
+void orc_adamax(float* p, float* m, float* u, const float* g, int64_t n, const orc_opt* o)
+{
+    const float b1 = o->beta1, omb1 = 1.0f - o->beta1, b2 = o->beta2, eps = o->eps, wd = o->weight_decay;
+    const float clr = (float)((double)o->lr / (1.0 - pow((double)o->beta1, (double)o->step)));
+    for (int64_t i = 0; i < n; ++i) {
+        float d = l2_grad(g[i], p[i], wd);
+        float m1 = (b1 * m[i]) + (omb1 * d);
+        float a = b2 * u[i], b = fabsf(d) + eps;
+        float u1 = (isnan(a) || isnan(b)) ? NAN : (b > a ? b : a);
+        m[i] = m1;
+        u[i] = u1;
+        p[i] = p[i] - (clr * (m1 / u1));
+    }
+}
+
+/* Adadelta.  v <- rho*v + (1-rho)*d*d;  delta = sqrt(acc + eps)/sqrt(v + eps) * d;
+ * acc <- rho*acc + (1-rho)*delta*delta;  p <- p - lr*delta.
+ * v is the running mean of squared gradients, acc that of squared updates. */
+void orc_adadelta(float* p, float* v, float* acc, const float* g, int64_t n, const orc_opt* o)
+{
+    const float rho = o->rho, omr = 1.0f - o->rho, eps = o->eps, lr = o->lr, wd = o->weight_decay;
+    for (int64_t i = 0; i < n; ++i) {
+        float d = l2_grad(g[i], p[i], wd);
+        float v1 = (rho * v[i]) + (omr * (d * d));
+        float delta = (sqrtf(acc[i] + eps) / sqrtf(v1 + eps)) * d;
+        float a1 = (rho * acc[i]) + (omr * (delta * delta));
+        v[i] = v1;
+        acc[i] = a1;
+        p[i] = p[i] - (lr * delta);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Cast to the compute dtype.  [P3] "Mixed Precision and FSDP": fp32 master  */
 /* weights with a 16-bit compute copy; [P4] fsdp_config mapping:             */
 /* compute_dtype is fp16 under --fp16 and fp32 otherwise.                    */
