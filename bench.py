@@ -66,6 +66,9 @@ def parse():
                     help="host threads of the offloaded AdamW (--pipeline offload)")
     ap.add_argument("--offload-chunk", type=int, default=0,
                     help="elements per copy/update chunk of the offloaded step (0: the library's 4 Mi)")
+    ap.add_argument("--optimizer", choices=["adamw", "sgd", "sgd-momentum", "adamax", "adadelta"], default="adamw",
+                    help="pointwise optimizer of the unit step (--pipeline units; others than AdamW keep fp32 "
+                         "state): SGD keeps no state, SGD with momentum one buffer, Adamax and Adadelta two")
     ap.add_argument("--state", choices=["f32", "bf16", "f16"], default="f32",
                     help="optimizer state: fp32 master/m/v (default) or 16-bit parameter/m/v with no fp32 "
                          "master (the parameter shard is the compute shard)")
@@ -87,19 +90,31 @@ def parse():
     return ap.parse_args()
 
 
-def sizes(cfg, pipeline, state="f32"):
-    """(fused kernel bytes, whole-step bytes) per shard element."""
+def sizes(cfg, pipeline, state="f32", n_states=2):
+    """(fused kernel bytes, whole-step bytes) per shard element; the parameter
+    and each of the optimizer's n_states state buffers are read and written."""
     g = 4 if cfg.grad_dt == "f32" else 2
     c = 4 if cfg.compute_dt == "f32" else 2
     N, G = cfg.world, cfg.gathers
     if state != "f32":               # 16-bit parameter, m, v; the parameter is the compute copy
         fused = N * g + 12 + c + 2 * (N - 1) * c
         return fused, fused + (G - 1) * 2 * N * c
+    st = 8 * (1 + n_states)
     if pipeline == "separate":
-        fused = N * g + 24 + c
+        fused = N * g + st + c
         return fused, fused + G * 2 * N * c
-    fused = N * g + 24 + c + 2 * (N - 1) * c + (c if G > 1 else 0)
+    fused = N * g + st + c + 2 * (N - 1) * c + (c if G > 1 else 0)
     return fused, fused + (G - 1) * 2 * N * c
+
+
+def optimizer_hp(name, cfg, N):
+    """Hyper-parameters of --optimizer (AdamW: the workload's)."""
+    if name == "adamw":
+        return None
+    return {"sgd": N.OptimHP.sgd(lr=1e-2, weight_decay=1e-4),
+            "sgd-momentum": N.OptimHP.sgd(lr=1e-2, momentum=0.9, weight_decay=1e-4),
+            "adamax": N.OptimHP.adamax(weight_decay=0.01),
+            "adadelta": N.OptimHP.adadelta(weight_decay=0.01)}[name].at_step(cfg.step)
 
 
 class Unit:
@@ -147,12 +162,12 @@ class Unit:
         torch.cuda.synchronize()
 
 
-def cpu_baseline(cfg, unit, budget_s, np_of_bytes, state="f32"):
+def cpu_baseline(cfg, unit, budget_s, np_of_bytes, state="f32", ohp=None):
     """The oracle, single-threaded on one host core, on rank 0's step of one
     resident block, repeated until the budget is spent."""
     import numpy as np
     import oracle
-    _, per_elt = sizes(cfg, "separate", state)
+    _, per_elt = sizes(cfg, "separate", state, ohp.n_states if ohp is not None else 2)
     S = unit.S
     cap = min(S, 4 * 1024 * 1024)          # bounded sample: first `cap` shard elements
     # rank 0's block of each rank's gradient is its first S elements
@@ -171,7 +186,11 @@ def cpu_baseline(cfg, unit, budget_s, np_of_bytes, state="f32"):
         p, m, v = p0.copy(), m0.copy(), v0.copy()
         avg = oracle.grad_average(grads, 0, cap, cfg.grad_dt, cfg.fp32_reduce)
         g32 = avg if avg.dtype == np.float32 else oracle.to_f32(avg, cfg.grad_dt)
-        if state == "f32":
+        if ohp is not None:
+            kind, o = oracle_opt(oracle, ohp)
+            oracle.opt_step(kind, p, m, v, g32, o)
+            comp = oracle.cast(p, cfg.compute_dt)
+        elif state == "f32":
             oracle.adamw(p, m, v, g32, h)
             comp = oracle.cast(p, cfg.compute_dt)
         else:
@@ -195,12 +214,25 @@ def cpu_baseline(cfg, unit, budget_s, np_of_bytes, state="f32"):
         pass
     return {
         "value": round(elems * per_elt / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": "rank 0's step (reduce-scatter, AdamW, cast, %d gather) on the first %d shard "
+        "sample": "rank 0's step (reduce-scatter, %s, cast, %d gather) on the first %d shard "
                   "elements of one %s block, repeated %d times in %.1f s; host %s (%s cpus)"
-                  % (cfg.gathers, cap, cfg.name, elems // cap, dt, model or platform.machine(),
-                     os.cpu_count()),
+                  % (ohp.name if ohp is not None else "AdamW", cfg.gathers, cap, cfg.name, elems // cap, dt,
+                     model or platform.machine(), os.cpu_count()),
         "elements_per_s": round(elems / dt, 1),
     }
+
+
+def oracle_opt(oracle, hp):
+    """(kind, oracle hyper-parameters) of an OptimHP, for opt_step(kind, p, s1, s2, g, o)."""
+    if hp.kind == 1:
+        o = oracle.opt("sgd", step=hp.step, lr=hp.lr, weight_decay=hp.weight_decay, momentum=hp.momentum,
+                       dampening=hp.dampening, nesterov=bool(hp.nesterov))
+        return "sgd", o
+    if hp.kind == 2:
+        return "adamax", oracle.opt("adamax", step=hp.step, lr=hp.lr, weight_decay=hp.weight_decay,
+                                    beta1=hp.beta1, beta2=hp.beta2, eps=hp.eps)
+    return "adadelta", oracle.opt("adadelta", step=hp.step, lr=hp.lr, weight_decay=hp.weight_decay, rho=hp.rho,
+                                  eps=hp.eps)
 
 
 class HipEvents:
@@ -253,10 +285,16 @@ def traffic_from_profiles(kernel_tag, src_hash):
         return None
 
 
+KERNEL_SOURCES = ("fsdp_kernels.hip", "fsdp_kernels.h", "fsdp_device.h", "fsdp_units.h", "fsdp_optim.h",
+                  "fsdp_units_adamw.hip", "fsdp_units_sgd.hip", "fsdp_units_adamax.hip", "fsdp_units_adadelta.hip")
+
+
 def kernel_source_hash():
+    """sha256 over the device sources, so counter figures taken on another
+    version of the kernels are not reported."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("fsdp_kernels.hip", "fsdp_kernels.h"):
+    for f in KERNEL_SOURCES:
         h.update(open(os.path.join(ROOT, "sharded_state_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
@@ -439,7 +477,12 @@ def main():
     if args.pipeline == "offload":
         bench_offload(args, cfg, torch, ss, N, workloads)
         return
-    fused_b, per_elt = sizes(cfg, "separate" if args.pipeline == "separate" else "unit", args.state)
+    ohp = optimizer_hp(args.optimizer, cfg, N)
+    if ohp is not None and (args.pipeline != "units" or args.state != "f32"):
+        print("--optimizer %s needs --pipeline units and fp32 state" % args.optimizer, file=sys.stderr)
+        sys.exit(2)
+    n_states = ohp.n_states if ohp is not None else 2
+    fused_b, per_elt = sizes(cfg, "separate" if args.pipeline == "separate" else "unit", args.state, n_states)
     pool = [Unit(cfg, b, ss, torch, workloads, args.state) for b in range(cfg.pool)]
     S = pool[0].S
     stream = torch.cuda.current_stream()
@@ -464,8 +507,8 @@ def main():
         peer_tab = N.ptr_array([0] + [q.data_ptr() for q in u.peers])
         full = ctypes.c_void_p(u.full.data_ptr())
         persistent = u.compute.data_ptr() if (G > 1 and not state16) else None
-        desc = N.Unit(u.master.data_ptr(), u.m.data_ptr(), u.v.data_ptr(), grads, peer_tab,
-                      u.full.data_ptr(), persistent, S)
+        desc = N.Unit(u.master.data_ptr(), u.m.data_ptr() if n_states >= 1 else None,
+                      u.v.data_ptr() if n_states >= 2 else None, grads, peer_tab, u.full.data_ptr(), persistent, S)
         unflat = (numels, len(cfg.numels), u.Pp, views, None, ccode, None, None)
         per_unit.append(dict(grads=grads, p=p, m=m, v=v, shards=shards, peer_tab=peer_tab, full=full,
                              persistent=ctypes.c_void_p(persistent), desc=desc, views=unflat))
@@ -482,8 +525,12 @@ def main():
             batch = slots[bounds[j]:bounds[j + 1]]
             st = st_handles[j % len(st_handles)]
             table = (N.Unit * len(batch))(*[per_unit[i]["desc"] for i in batch])
-            first = (lib.fsdp_step_units, (table, len(batch), cfg.world, 0, gcode, int(cfg.fp32_reduce), scode,
-                                           ccode, hp_ref, st))
+            if ohp is None:
+                first = (lib.fsdp_step_units, (table, len(batch), cfg.world, 0, gcode, int(cfg.fp32_reduce), scode,
+                                               ccode, hp_ref, st))
+            else:
+                first = (lib.fsdp_step_units_optim, (table, len(batch), cfg.world, 0, gcode, int(cfg.fp32_reduce),
+                                                     scode, ccode, ctypes.byref(ohp), st))
             trail = [(lib.fsdp_unshard_gather, (per_unit[i]["shards"], cfg.world, S, ccode, per_unit[i]["full"], st))
                      for i in batch for _ in range(G - 1)]
             trail += [(lib.fsdp_unflatten_views, per_unit[i]["views"]) for i in batch]
@@ -568,7 +615,8 @@ def main():
         units_per_launch = cfg.blocks / len(groups)
         bytes_per_launch = fused_b * S * units_per_launch
         achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
-        traffic = traffic_from_profiles("%s_%s" % (args.pipeline, cfg.name), kernel_source_hash())
+        tag = args.pipeline if args.optimizer == "adamw" else "%s-%s" % (args.pipeline, args.optimizer)
+        traffic = traffic_from_profiles("%s_%s" % (tag, cfg.name), kernel_source_hash())
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": ("k_units<GATHER> (fused reduce-scatter + AdamW + cast + all-gather, %g units per "
@@ -586,7 +634,7 @@ def main():
             if t.dtype in (torch.float16, torch.bfloat16):
                 return t.view(torch.int16).numpy().view(np.uint16)
             return t.numpy()
-        cpu = cpu_baseline(cfg, pool[0], args.cpu_seconds, np_of_bytes, args.state)
+        cpu = cpu_baseline(cfg, pool[0], args.cpu_seconds, np_of_bytes, args.state, ohp)
 
     ckpt = None
     if args.checkpoint:
@@ -619,7 +667,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "config": {"workload": "%s x%d" % (cfg.name, cfg.blocks), "pipeline": args.pipeline,
-                   "state_dtype": args.state,
+                   "optimizer": args.optimizer, "state_dtype": args.state,
                    "streams": len(streams),
                    "world": cfg.world, "rank": 0,
                    "shard_numel": S, "unit_numel": pool[0].P, "blocks_per_step": cfg.blocks,

@@ -51,7 +51,7 @@ extern "C" {
 
 #define FSDP_API __attribute__((visibility("default")))
 
-#define FSDP_ABI_VERSION 4
+#define FSDP_ABI_VERSION 5
 #define FSDP_MAX_WORLD 128
 
 typedef enum fsdp_dtype {
@@ -244,6 +244,60 @@ typedef struct fsdp_unit {
 FSDP_API int fsdp_step_units(const fsdp_unit* units, int32_t n_units, int32_t world, int32_t rank,
                              fsdp_dtype grad_dt, int32_t fp32_reduce, fsdp_dtype state_dt,
                              fsdp_dtype compute_dt, const fsdp_adamw_hp* hp, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Other pointwise optimizers.  [P4] "限制与兼容性说明": FSDP supports the
+ * pointwise optimizers (Adam, AdamW, Adadelta, Adamax, SGD, ...), whose update
+ * of an element needs only that element's gradient and state, and not
+ * Adagrad, Adafactor or LAMB.  The pages write none of the updates; these are
+ * the published algorithms in the form torch.optim documents them, weight
+ * decay added to the gradient (d = g + wd*p, skipped when wd == 0) except for
+ * AdamW's decoupled decay.  Host scalars: hyper-parameters as fp32, 1 - beta,
+ * 1 - dampening and 1 - rho one fp32 operation, lr / (1 - beta1^t) in double
+ * rounded once.  Per element, with t = step:
+ *   SGD, momentum == 0:  p <- p - lr*d                       (no state)
+ *   SGD, momentum mu:    b <- d if t == 1 else mu*b + (1 - dampening)*d;
+ *                        d <- d + mu*b (nesterov) or b;  p <- p - lr*d
+ *                        (state: exp_avg = momentum buffer)
+ *   Adamax:              m <- beta1*m + (1 - beta1)*d;
+ *                        u <- max(beta2*u, |d| + eps) (NaN if either is NaN);
+ *                        p <- p - (lr / (1 - beta1^t)) * (m / u)
+ *                        (state: exp_avg = m, exp_avg_sq = u)
+ *   Adadelta:            v <- rho*v + (1 - rho)*(d*d);
+ *                        delta = (sqrt(acc + eps) / sqrt(v + eps)) * d;
+ *                        acc <- rho*acc + (1 - rho)*(delta*delta); p <- p - lr*delta
+ *                        (state: exp_avg = v, exp_avg_sq = acc)
+ *   AdamW:               as fsdp_sharded_adamw (exp_avg = m, exp_avg_sq = v)
+ * ------------------------------------------------------------------------ */
+typedef enum fsdp_optimizer {
+    FSDP_OPT_ADAMW = 0,
+    FSDP_OPT_SGD = 1,
+    FSDP_OPT_ADAMAX = 2,
+    FSDP_OPT_ADADELTA = 3
+} fsdp_optimizer;
+
+typedef struct fsdp_optim_hp {
+    fsdp_optimizer kind;
+    float lr;             /* >= 0 */
+    float weight_decay;   /* >= 0 */
+    float beta1;          /* AdamW, Adamax: [0, 1) */
+    float beta2;          /* AdamW, Adamax: [0, 1) */
+    float eps;            /* AdamW, Adamax, Adadelta: >= 0 */
+    float momentum;       /* SGD: >= 0 */
+    float dampening;      /* SGD */
+    float rho;            /* Adadelta: [0, 1] */
+    int32_t nesterov;     /* SGD: needs momentum > 0 and dampening == 0 */
+    int64_t step;         /* t >= 1, the step being taken */
+} fsdp_optim_hp;
+
+/* fsdp_step_units with the optimizer named by hp->kind.  The state buffers the
+ * optimizer does not keep may be NULL (SGD without momentum: exp_avg and
+ * exp_avg_sq; SGD with momentum: exp_avg_sq) and are never touched.  16-bit
+ * state_dt only with FSDP_OPT_ADAMW (FSDP_E_DTYPE otherwise).  FSDP_E_INVAL for
+ * hyper-parameters outside the ranges above. */
+FSDP_API int fsdp_step_units_optim(const fsdp_unit* units, int32_t n_units, int32_t world, int32_t rank,
+                                   fsdp_dtype grad_dt, int32_t fp32_reduce, fsdp_dtype state_dt,
+                                   fsdp_dtype compute_dt, const fsdp_optim_hp* hp, void* stream);
 
 /* Per-tensor views of the full buffer.  [P3] "The FSDP Unit" (use_orig_params):
  * tensor k is full[off_k : off_k + numel_k]; the padding belongs to no view.

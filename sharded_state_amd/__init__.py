@@ -8,7 +8,7 @@ hand-written HIP kernels of ``libfsdp_shard.so`` behind the C ABI declared in
 ``include/fsdp_shard.h``.  This package is its Python binding: argument
 marshalling over ctypes, with PyTorch for device memory and streams.
 """
-from ._native import AdamWHP, FsdpError, MAX_WORLD, lib  # noqa: F401
+from ._native import AdamWHP, FsdpError, MAX_WORLD, OptimHP, lib  # noqa: F401
 from .api import (  # noqa: F401
     dtype_code,
     fsdp_flatten_pad,
@@ -33,7 +33,7 @@ from .offload import (  # noqa: F401
 from .checkpoint import consolidate, load_shard, save_shard, shard_info, shard_path  # noqa: F401
 
 __all__ = [
-    "AdamWHP", "FsdpError", "MAX_WORLD", "lib", "dtype_code", "fsdp_layout", "fsdp_flatten_pad",
+    "AdamWHP", "OptimHP", "FsdpError", "MAX_WORLD", "lib", "dtype_code", "fsdp_layout", "fsdp_flatten_pad",
     "fsdp_reduce_scatter_local", "fsdp_sharded_adamw", "fsdp_step_unit", "fsdp_step_units", "prepare_step_units", "fsdp_unshard_gather",
     "fsdp_unflatten_views", "view_table", "RankState", "save_shard", "load_shard", "shard_info",
     "shard_path", "consolidate", "fsdp_host_adamw", "fsdp_offload_step", "fsdp_offload_step_units",

@@ -13,7 +13,8 @@ LIB_PATH = os.path.join(_HERE, "libfsdp_shard.so")
 F32, F16, BF16 = 0, 1, 2
 OK, E_INVAL, E_DTYPE, E_SIZE, E_ALIAS, E_HIP, E_IO, E_FORMAT = 0, -1, -2, -3, -4, -5, -6, -7
 MAX_WORLD = 128
-ABI_VERSION = 4
+ABI_VERSION = 5
+OPT_ADAMW, OPT_SGD, OPT_ADAMAX, OPT_ADADELTA = 0, 1, 2, 3
 
 
 class AdamWHP(ctypes.Structure):
@@ -27,6 +28,52 @@ class AdamWHP(ctypes.Structure):
     def __repr__(self):
         return ("AdamWHP(lr=%g, beta1=%g, beta2=%g, eps=%g, weight_decay=%g, step=%d)"
                 % (self.lr, self.beta1, self.beta2, self.eps, self.weight_decay, self.step))
+
+
+class OptimHP(ctypes.Structure):
+    """fsdp_optim_hp: a pointwise optimizer and its hyper-parameters (use the
+    constructors sgd / adamax / adadelta / adamw; defaults are torch.optim's,
+    with lr 1e-3 for SGD)."""
+    _fields_ = [("kind", ctypes.c_int), ("lr", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+                ("momentum", ctypes.c_float), ("dampening", ctypes.c_float), ("rho", ctypes.c_float),
+                ("nesterov", ctypes.c_int32), ("step", ctypes.c_int64)]
+
+    @classmethod
+    def sgd(cls, lr=1e-3, momentum=0.0, dampening=0.0, weight_decay=0.0, nesterov=False, step=1):
+        return cls(OPT_SGD, lr, weight_decay, 0.0, 0.0, 0.0, momentum, dampening, 0.0, int(bool(nesterov)), step)
+
+    @classmethod
+    def adamax(cls, lr=2e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, step=1):
+        return cls(OPT_ADAMAX, lr, weight_decay, betas[0], betas[1], eps, 0.0, 0.0, 0.0, 0, step)
+
+    @classmethod
+    def adadelta(cls, lr=1.0, rho=0.9, eps=1e-6, weight_decay=0.0, step=1):
+        return cls(OPT_ADADELTA, lr, weight_decay, 0.0, 0.0, eps, 0.0, 0.0, rho, 0, step)
+
+    @classmethod
+    def adamw(cls, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, step=1):
+        return cls(OPT_ADAMW, lr, weight_decay, betas[0], betas[1], eps, 0.0, 0.0, 0.0, 0, step)
+
+    @property
+    def n_states(self):
+        """State buffers the optimizer keeps (exp_avg, then exp_avg_sq)."""
+        if self.kind == OPT_SGD:
+            return 1 if self.momentum != 0.0 else 0
+        return 2
+
+    @property
+    def name(self):
+        return {OPT_ADAMW: "adamw", OPT_SGD: "sgd", OPT_ADAMAX: "adamax", OPT_ADADELTA: "adadelta"}[self.kind]
+
+    def at_step(self, step):
+        c = OptimHP()
+        ctypes.pointer(c)[0] = self
+        c.step = step
+        return c
+
+    def __repr__(self):
+        return "OptimHP(%s, lr=%g, wd=%g, step=%d)" % (self.name, self.lr, self.weight_decay, self.step)
 
 
 class View(ctypes.Structure):
@@ -101,6 +148,9 @@ def lib():
     L.fsdp_step_units.restype = ctypes.c_int
     L.fsdp_step_units.argtypes = [ctypes.POINTER(Unit), i32, i32, i32, ctypes.c_int, i32, ctypes.c_int,
                                   ctypes.c_int, ctypes.POINTER(AdamWHP), vp]
+    L.fsdp_step_units_optim.restype = ctypes.c_int
+    L.fsdp_step_units_optim.argtypes = [ctypes.POINTER(Unit), i32, i32, i32, ctypes.c_int, i32, ctypes.c_int,
+                                        ctypes.c_int, ctypes.POINTER(OptimHP), vp]
     L.fsdp_unshard_gather.restype = ctypes.c_int
     L.fsdp_unshard_gather.argtypes = [vpp, i32, i64, ctypes.c_int, vp, vp]
     L.fsdp_unflatten_views.restype = ctypes.c_int

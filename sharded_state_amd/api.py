@@ -11,7 +11,7 @@ import ctypes
 import torch
 
 from . import _native as N
-from ._native import AdamWHP, Unit, View, check, i64_array, ptr_array
+from ._native import AdamWHP, OptimHP, Unit, View, check, i64_array, ptr_array
 
 _DT = {torch.float32: N.F32, torch.float16: N.F16, torch.bfloat16: N.BF16}
 _TORCH = {v: k for k, v in _DT.items()}
@@ -213,7 +213,10 @@ def fsdp_step_units(units, rank, fp32_reduce, hp, stream=None):
     dicts with keys master, exp_avg, exp_avg_sq, rank_grads, and either
     (peer_shards, full[, compute_shard]) for the fused step with all-gather or
     compute_shard alone for the step without it.  All units share world (the
-    length of rank_grads), rank, dtypes and hp.  Returns the prepared call
+    length of rank_grads), rank, dtypes and hp.  hp is an AdamWHP (AdamW,
+    fsdp_step_units) or an OptimHP (any pointwise optimizer,
+    fsdp_step_units_optim; state buffers it does not keep may be None).
+    Returns the prepared call
     (callable with no arguments) after running it once, so a training loop can
     re-issue it without marshalling again."""
     call = prepare_step_units(units, rank, fp32_reduce, hp, stream)
@@ -228,8 +231,10 @@ def prepare_step_units(units, rank, fp32_reduce, hp, stream=None):
     shard is the compute shard, so no compute_shard is given)."""
     if not units:
         raise ValueError("units is empty")
-    if not isinstance(hp, AdamWHP):
+    optim = isinstance(hp, OptimHP)
+    if not optim and not isinstance(hp, AdamWHP):
         hp = AdamWHP(**hp)
+    n_states = hp.n_states if optim else 2
     world = len(units[0]["rank_grads"])
     gather = units[0].get("full") is not None
     sdt = units[0]["master"].dtype
@@ -241,8 +246,16 @@ def prepare_step_units(units, rank, fp32_reduce, hp, stream=None):
     device = units[0]["master"].device
     tensors = []
     for k, u in enumerate(units):
-        master, m, v = u["master"], u["exp_avg"], u["exp_avg_sq"]
+        master, m, v = u["master"], u.get("exp_avg"), u.get("exp_avg_sq")
+        if n_states < 2:
+            v = None                              # not kept by the optimizer
+        if n_states < 1:
+            m = None
         for name, t in (("master", master), ("exp_avg", m), ("exp_avg_sq", v)):
+            if t is None and name != "master":
+                if n_states >= (1 if name == "exp_avg" else 2):
+                    raise ValueError("units[%d].%s is required by the optimizer" % (k, name))
+                continue
             _dev(t, "units[%d].%s" % (k, name))
             if t.dtype != sdt or t.numel() != master.numel():
                 raise ValueError("units[%d].%s must be %s with master's size" % (k, name, sdt))
@@ -266,7 +279,7 @@ def prepare_step_units(units, rank, fp32_reduce, hp, stream=None):
                 raise TypeError("every unit's compute dtype must be the same (and equal a 16-bit state dtype)")
         gptr = ptr_array([x.data_ptr() for x in grads])
         keep.append(gptr)
-        tensors += grads + [master, m, v]
+        tensors += grads + [t for t in (master, m, v) if t is not None]
         pptr = None
         if gather:
             _dev(full, "units[%d].full" % k)
@@ -293,17 +306,19 @@ def prepare_step_units(units, rank, fp32_reduce, hp, stream=None):
             if cs.numel() != S or (cdt is not None and cs.dtype != cdt):
                 raise ValueError("units[%d].compute_shard must hold %d elements of %s" % (k, S, cdt))
             tensors.append(cs)
-        table[k] = Unit(master.data_ptr(), m.data_ptr(), v.data_ptr(), gptr, pptr,
+        table[k] = Unit(master.data_ptr(), m.data_ptr() if m is not None else None,
+                        v.data_ptr() if v is not None else None, gptr, pptr,
                         full.data_ptr() if full is not None else None,
                         cs.data_ptr() if cs is not None else None, S)
     _same_device(tensors)
     args = (table, len(units), world, int(rank), dtype_code(gdt), int(bool(fp32_reduce)), dtype_code(sdt),
             dtype_code(cdt or torch.float32), ctypes.byref(hp), _stream(stream, device))
-    fn = N.lib().fsdp_step_units
+    name = "fsdp_step_units_optim" if optim else "fsdp_step_units"
+    fn = getattr(N.lib(), name)
 
     def call():
         with torch.cuda.device(device):
-            check("fsdp_step_units", fn(*args))
+            check(name, fn(*args))
 
     call.keep = (keep, table, hp, tensors)   # the C side reads these host arrays at every call
     return call

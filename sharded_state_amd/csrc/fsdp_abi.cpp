@@ -170,7 +170,7 @@ struct UnitBuild {
 };
 
 // Validate unit `idx` (fused step; with full_out the all-gather too) and fill ub.
-int build_unit(const char* fn, int idx, void* master, void* exp_avg, void* exp_avg_sq, int state_dt,
+int build_unit(const char* fn, int idx, void* master, void* exp_avg, void* exp_avg_sq, int n_states, int state_dt,
                const void* const* rank_grads, int32_t world, int32_t rank, int grad_dt, int compute_dt,
                int64_t S, void* compute_shard, const void* const* peer_shards, void* full_out, bool gather,
                UnitBuild& ub, std::vector<Range>& ins, std::vector<Range>& outs) {
@@ -181,8 +181,11 @@ int build_unit(const char* fn, int idx, void* master, void* exp_avg, void* exp_a
     ub.a.grads = ub.grads.data();
     ub.a.S = S;
     if (S == 0) return FSDP_OK;
-    if (!master || !exp_avg || !exp_avg_sq)
-        return fail(FSDP_E_INVAL, "%s: unit %d: master, exp_avg and exp_avg_sq must be non-NULL", fn, idx);
+    if (!master) return fail(FSDP_E_INVAL, "%s: unit %d: master is NULL", fn, idx);
+    if (n_states >= 1 && !exp_avg) return fail(FSDP_E_INVAL, "%s: unit %d: exp_avg is NULL", fn, idx);
+    if (n_states >= 2 && !exp_avg_sq) return fail(FSDP_E_INVAL, "%s: unit %d: exp_avg_sq is NULL", fn, idx);
+    if (n_states < 2) exp_avg_sq = nullptr;   // not kept by the optimizer: never touched
+    if (n_states < 1) exp_avg = nullptr;
     const int64_t cs = dt_size(compute_dt);
     void* own = compute_shard;
     void* out2 = nullptr;
@@ -207,11 +210,11 @@ int build_unit(const char* fn, int idx, void* master, void* exp_avg, void* exp_a
     }
     const int64_t ss = dt_size(state_dt);
     outs.push_back(range(master, S, ss));
-    outs.push_back(range(exp_avg, S, ss));
-    outs.push_back(range(exp_avg_sq, S, ss));
+    if (exp_avg) outs.push_back(range(exp_avg, S, ss));
+    if (exp_avg_sq) outs.push_back(range(exp_avg_sq, S, ss));
 
-    bool vec = aligned16(master) && aligned16(exp_avg) && aligned16(exp_avg_sq) && (!own || aligned16(own)) &&
-               (!out2 || aligned16(out2));
+    bool vec = aligned16(master) && (!exp_avg || aligned16(exp_avg)) && (!exp_avg_sq || aligned16(exp_avg_sq)) &&
+               (!own || aligned16(own)) && (!out2 || aligned16(out2));
     for (int q = 0; q < world; ++q) vec = vec && aligned16(ub.grads[q]);
     for (size_t j = 0; j < ub.psrc.size(); ++j) vec = vec && aligned16(ub.psrc[j]) && aligned16(ub.pdst[j]);
     ub.a.peer_src = ub.psrc.data();
@@ -225,9 +228,71 @@ int build_unit(const char* fn, int idx, void* master, void* exp_avg, void* exp_a
     return FSDP_OK;
 }
 
+// The AdamW policy's scalars (hp validated).
+fsdp::OptParams adamw_params(const fsdp_adamw_hp& hp) {
+    fsdp::OptParams op{};
+    op.kind = fsdp::kOptAdamW;
+    op.adam = adam_scalars(hp);
+    return op;
+}
+
+// Validate an optimizer's hyper-parameters; fill its policy scalars and the
+// number of state buffers it keeps.
+int optim_params(const char* fn, const fsdp_optim_hp* hp, fsdp::OptParams& op, int& n_states) {
+    if (!hp) return fail(FSDP_E_INVAL, "%s: hp is NULL", fn);
+    if (hp->step < 1) return fail(FSDP_E_INVAL, "%s: hp->step = %lld < 1", fn, (long long)hp->step);
+    if (!(hp->lr >= 0.0f) || !(hp->weight_decay >= 0.0f))
+        return fail(FSDP_E_INVAL, "%s: lr and weight_decay must be >= 0", fn);
+    const bool betas = hp->beta1 >= 0.0f && hp->beta1 < 1.0f && hp->beta2 >= 0.0f && hp->beta2 < 1.0f;
+    op = fsdp::OptParams{};
+    op.lr = hp->lr;
+    op.wd = hp->weight_decay;
+    op.eps = hp->eps;
+    switch (hp->kind) {
+    case FSDP_OPT_ADAMW: {
+        if (!betas || !(hp->eps >= 0.0f)) return fail(FSDP_E_INVAL, "%s: AdamW needs betas in [0, 1), eps >= 0", fn);
+        const fsdp_adamw_hp a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->step};
+        op = adamw_params(a);
+        n_states = 2;
+        return FSDP_OK;
+    }
+    case FSDP_OPT_SGD:
+        if (!(hp->momentum >= 0.0f) || !(hp->dampening == hp->dampening))
+            return fail(FSDP_E_INVAL, "%s: SGD needs momentum >= 0 and a finite dampening", fn);
+        if (hp->nesterov && (hp->momentum <= 0.0f || hp->dampening != 0.0f))
+            return fail(FSDP_E_INVAL, "%s: Nesterov momentum needs momentum > 0 and dampening == 0", fn);
+        op.kind = hp->momentum != 0.0f ? fsdp::kOptSgdMomentum : fsdp::kOptSgd;
+        op.mu = hp->momentum;
+        op.omd = 1.0f - hp->dampening;
+        op.first = hp->step == 1;
+        op.nesterov = hp->nesterov != 0;
+        n_states = hp->momentum != 0.0f ? 1 : 0;
+        return FSDP_OK;
+    case FSDP_OPT_ADAMAX:
+        if (!betas || !(hp->eps >= 0.0f)) return fail(FSDP_E_INVAL, "%s: Adamax needs betas in [0, 1), eps >= 0", fn);
+        op.kind = fsdp::kOptAdamax;
+        op.clr = (float)((double)hp->lr / (1.0 - std::pow((double)hp->beta1, (double)hp->step)));
+        op.b1 = hp->beta1;
+        op.omb1 = 1.0f - hp->beta1;
+        op.b2 = hp->beta2;
+        n_states = 2;
+        return FSDP_OK;
+    case FSDP_OPT_ADADELTA:
+        if (!(hp->rho >= 0.0f && hp->rho <= 1.0f) || !(hp->eps >= 0.0f))
+            return fail(FSDP_E_INVAL, "%s: Adadelta needs rho in [0, 1], eps >= 0", fn);
+        op.kind = fsdp::kOptAdadelta;
+        op.rho = hp->rho;
+        op.omr = 1.0f - hp->rho;
+        n_states = 2;
+        return FSDP_OK;
+    default:
+        return fail(FSDP_E_INVAL, "%s: unknown optimizer %d", fn, (int)hp->kind);
+    }
+}
+
 // Launch the validated units (one grid per table of units).
 int launch_built(const char* fn, std::vector<UnitBuild>& units, int32_t world, int grad_dt,
-                 int32_t fp32_reduce, int state_dt, int compute_dt, bool gather, const fsdp_adamw_hp* hp,
+                 int32_t fp32_reduce, int state_dt, int compute_dt, bool gather, const fsdp::OptParams& op,
                  const std::vector<Range>& ins, const std::vector<Range>& outs, void* stream) {
     if (!disjoint(outs, ins)) return fail(FSDP_E_ALIAS, "%s: an output overlaps an input or another output", fn);
     std::vector<fsdp::UnitArgs> args;
@@ -247,7 +312,7 @@ int launch_built(const char* fn, std::vector<UnitBuild>& units, int32_t world, i
     L.state_dt = state_dt;
     L.gather = gather;
     L.rs = reduce_scalars(world);
-    L.as = adam_scalars(*hp);
+    L.opt = op;
     L.stream = stream;
     (void)hipGetLastError();
     hipError_t e = fsdp::launch_units(args.data(), (int)args.size(), L);
@@ -402,10 +467,11 @@ int fsdp_sharded_adamw(float* master, float* exp_avg, float* exp_avg_sq, const v
     if (rc) return rc;
     std::vector<UnitBuild> units(1);
     std::vector<Range> ins, outs;
-    rc = build_unit(fn, 0, master, exp_avg, exp_avg_sq, FSDP_F32, rank_grads, world, rank, grad_dt, compute_dt,
+    rc = build_unit(fn, 0, master, exp_avg, exp_avg_sq, 2, FSDP_F32, rank_grads, world, rank, grad_dt, compute_dt,
                     shard_numel, compute_shard, nullptr, nullptr, false, units[0], ins, outs);
     if (rc) return rc;
-    return launch_built(fn, units, world, grad_dt, fp32_reduce, FSDP_F32, compute_dt, false, hp, ins, outs, stream);
+    return launch_built(fn, units, world, grad_dt, fp32_reduce, FSDP_F32, compute_dt, false, adamw_params(*hp), ins,
+                        outs, stream);
 }
 
 int fsdp_step_unit(float* master, float* exp_avg, float* exp_avg_sq, const void* const* rank_grads,
@@ -418,26 +484,31 @@ int fsdp_step_unit(float* master, float* exp_avg, float* exp_avg_sq, const void*
     if (rc) return rc;
     std::vector<UnitBuild> units(1);
     std::vector<Range> ins, outs;
-    rc = build_unit(fn, 0, master, exp_avg, exp_avg_sq, FSDP_F32, rank_grads, world, rank, grad_dt, compute_dt,
+    rc = build_unit(fn, 0, master, exp_avg, exp_avg_sq, 2, FSDP_F32, rank_grads, world, rank, grad_dt, compute_dt,
                     shard_numel, compute_shard, peer_shards, full_out, true, units[0], ins, outs);
     if (rc) return rc;
-    return launch_built(fn, units, world, grad_dt, fp32_reduce, FSDP_F32, compute_dt, true, hp, ins, outs, stream);
+    return launch_built(fn, units, world, grad_dt, fp32_reduce, FSDP_F32, compute_dt, true, adamw_params(*hp), ins,
+                        outs, stream);
 }
 
-int fsdp_step_units(const fsdp_unit* units, int32_t n_units, int32_t world, int32_t rank, fsdp_dtype grad_dt,
-                    int32_t fp32_reduce, fsdp_dtype state_dt, fsdp_dtype compute_dt, const fsdp_adamw_hp* hp,
-                    void* stream) {
-    const char* fn = "fsdp_step_units";
+}  // extern "C"
+
+namespace {
+
+// The batched unit step of fsdp_step_units / fsdp_step_units_optim (hp checked).
+int step_units_impl(const char* fn, const fsdp_unit* units, int32_t n_units, int32_t world, int32_t rank,
+                    int grad_dt, int32_t fp32_reduce, int state_dt, int compute_dt, const fsdp::OptParams& op,
+                    int n_states, bool state16_ok, void* stream) {
     if (n_units < 0) return fail(FSDP_E_INVAL, "%s: n_units = %d < 0", fn, n_units);
     if (n_units > 0 && !units) return fail(FSDP_E_INVAL, "%s: units is NULL", fn);
-    if (!valid_dtype(state_dt)) return fail(FSDP_E_DTYPE, "%s: state dtype %d unsupported", fn, (int)state_dt);
-    if (!valid_dtype(compute_dt)) return fail(FSDP_E_DTYPE, "%s: compute dtype %d unsupported", fn, (int)compute_dt);
+    if (!valid_dtype(state_dt)) return fail(FSDP_E_DTYPE, "%s: state dtype %d unsupported", fn, state_dt);
+    if (!valid_dtype(compute_dt)) return fail(FSDP_E_DTYPE, "%s: compute dtype %d unsupported", fn, compute_dt);
+    if (state_dt != FSDP_F32 && !state16_ok)
+        return fail(FSDP_E_DTYPE, "%s: 16-bit state is supported for AdamW only", fn);
     if (state_dt != FSDP_F32 && compute_dt != state_dt)
         return fail(FSDP_E_DTYPE, "%s: with 16-bit state the parameter is the compute copy: compute dtype "
                                   "must equal the state dtype", fn);
     int rc = check_world(world, rank, 0);
-    if (rc) return rc;
-    rc = check_hp(fn, hp);
     if (rc) return rc;
     if (n_units == 0) return ok();
     const bool gather = units[0].full_out != nullptr;
@@ -450,13 +521,39 @@ int fsdp_step_units(const fsdp_unit* units, int32_t n_units, int32_t world, int3
         if (state_dt != FSDP_F32 && u.compute_shard)
             return fail(FSDP_E_INVAL, "%s: unit %d: with 16-bit state the parameter shard is the compute shard; "
                                       "compute_shard must be NULL", fn, k);
-        rc = build_unit(fn, k, u.master, u.exp_avg, u.exp_avg_sq, state_dt, u.rank_grads, world, rank, grad_dt,
-                        compute_dt, u.shard_numel, u.compute_shard, u.peer_shards, u.full_out, gather, built[k],
-                        ins, outs);
+        rc = build_unit(fn, k, u.master, u.exp_avg, u.exp_avg_sq, n_states, state_dt, u.rank_grads, world, rank,
+                        grad_dt, compute_dt, u.shard_numel, u.compute_shard, u.peer_shards, u.full_out, gather,
+                        built[k], ins, outs);
         if (rc) return rc;
     }
-    return launch_built(fn, built, world, grad_dt, fp32_reduce, state_dt, compute_dt, gather, hp, ins, outs,
+    return launch_built(fn, built, world, grad_dt, fp32_reduce, state_dt, compute_dt, gather, op, ins, outs,
                         stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fsdp_step_units(const fsdp_unit* units, int32_t n_units, int32_t world, int32_t rank, fsdp_dtype grad_dt,
+                    int32_t fp32_reduce, fsdp_dtype state_dt, fsdp_dtype compute_dt, const fsdp_adamw_hp* hp,
+                    void* stream) {
+    const char* fn = "fsdp_step_units";
+    int rc = check_hp(fn, hp);
+    if (rc) return rc;
+    return step_units_impl(fn, units, n_units, world, rank, grad_dt, fp32_reduce, state_dt, compute_dt,
+                           adamw_params(*hp), 2, true, stream);
+}
+
+int fsdp_step_units_optim(const fsdp_unit* units, int32_t n_units, int32_t world, int32_t rank,
+                          fsdp_dtype grad_dt, int32_t fp32_reduce, fsdp_dtype state_dt, fsdp_dtype compute_dt,
+                          const fsdp_optim_hp* hp, void* stream) {
+    const char* fn = "fsdp_step_units_optim";
+    fsdp::OptParams op;
+    int n_states = 0;
+    int rc = optim_params(fn, hp, op, n_states);
+    if (rc) return rc;
+    return step_units_impl(fn, units, n_units, world, rank, grad_dt, fp32_reduce, state_dt, compute_dt, op,
+                           n_states, hp->kind == FSDP_OPT_ADAMW, stream);
 }
 
 int fsdp_unshard_gather(const void* const* shards, int32_t world, int64_t shard_numel, fsdp_dtype dt,

@@ -1,0 +1,219 @@
+// fsdp_device.h -- device primitives shared by the gfx950 kernels of
+// libfsdp_shard.so: 16-byte global accesses, number formats, the N-way
+// rank reduction, and the launch helper.  Not installed.
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include "fsdp_kernels.h"
+
+#pragma clang fp contract(off)
+
+namespace fsdp {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#ifndef FSDP_NT_LOAD
+#define FSDP_NT_LOAD 0
+#endif
+#ifndef FSDP_NT_STORE
+#define FSDP_NT_STORE 1   // streamed outputs: non-temporal (measured +1-9% on the unit step)
+#endif
+// 16-byte global accesses; the streamed buffers are touched once per launch,
+// so wide stores carry the non-temporal hint.
+__device__ __forceinline__ u32x4 ld16(const u32x4* p) {
+#if FSDP_NT_LOAD
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+__device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
+#if FSDP_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
+// ----------------------------------------------------------------- formats
+template <int F> __device__ __forceinline__ float to_f32(uint32_t bits);
+template <> __device__ __forceinline__ float to_f32<FSDP_F32>(uint32_t bits) { return __uint_as_float(bits); }
+template <> __device__ __forceinline__ float to_f32<FSDP_F16>(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);      // exact
+}
+template <> __device__ __forceinline__ float to_f32<FSDP_BF16>(uint32_t bits) {
+    return __uint_as_float(bits << 16);                                // exact
+}
+
+template <int F> __device__ __forceinline__ uint32_t from_f32(float x);
+template <> __device__ __forceinline__ uint32_t from_f32<FSDP_F32>(float x) { return __float_as_uint(x); }
+template <> __device__ __forceinline__ uint32_t from_f32<FSDP_F16>(float x) {
+    // v_cvt_f16_f32: round to nearest even, binary16 subnormals kept
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+template <> __device__ __forceinline__ uint32_t from_f32<FSDP_BF16>(float x) {
+    // Round the fp32 encoding at bit 16, ties to even; NaN stays a quiet NaN.
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int F> __device__ __forceinline__ float round_to(float x) { return to_f32<F>(from_f32<F>(x)); }
+
+// 8 consecutive elements of format F starting at element 8*vi (16-byte aligned).
+template <int F>
+__device__ __forceinline__ void load8(const void* __restrict__ base, int64_t vi, float (&x)[8]) {
+    if constexpr (F == FSDP_F32) {
+        const u32x4* q = reinterpret_cast<const u32x4*>(base) + 2 * vi;
+        u32x4 a = ld16(q), b = ld16(q + 1);
+        x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
+        x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+        x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
+        x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
+    } else {
+        u32x4 a = ld16(reinterpret_cast<const u32x4*>(base) + vi);
+        uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[2 * k] = to_f32<F>(w[k] & 0xffffu);
+            x[2 * k + 1] = to_f32<F>(w[k] >> 16);
+        }
+    }
+}
+
+template <int F>
+__device__ __forceinline__ void store8(void* __restrict__ base, int64_t vi, const float (&x)[8]) {
+    if constexpr (F == FSDP_F32) {
+        u32x4* q = reinterpret_cast<u32x4*>(base) + 2 * vi;
+        u32x4 a, b;
+        a.x = __float_as_uint(x[0]); a.y = __float_as_uint(x[1]);
+        a.z = __float_as_uint(x[2]); a.w = __float_as_uint(x[3]);
+        b.x = __float_as_uint(x[4]); b.y = __float_as_uint(x[5]);
+        b.z = __float_as_uint(x[6]); b.w = __float_as_uint(x[7]);
+        st16(q, a);
+        st16(q + 1, b);
+    } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = from_f32<F>(x[2 * k]) | (from_f32<F>(x[2 * k + 1]) << 16);
+        u32x4 a;
+        a.x = w[0]; a.y = w[1]; a.z = w[2]; a.w = w[3];
+        st16(reinterpret_cast<u32x4*>(base) + vi, a);
+    }
+}
+
+template <int F>
+__device__ __forceinline__ float load1(const void* __restrict__ base, int64_t i) {
+    if constexpr (F == FSDP_F32) return reinterpret_cast<const float*>(base)[i];
+    else return to_f32<F>(reinterpret_cast<const uint16_t*>(base)[i]);
+}
+
+template <int F>
+__device__ __forceinline__ void store1(void* __restrict__ base, int64_t i, float x) {
+    if constexpr (F == FSDP_F32) reinterpret_cast<float*>(base)[i] = x;
+    else reinterpret_cast<uint16_t*>(base)[i] = (uint16_t)from_f32<F>(x);
+}
+
+// ----------------------------------------------------------------- reduction
+// One step of the left fold over ranks.  fp32 mode: a single fp32 add.
+// 16-bit mode: the sum rounded back to the gradient format.
+template <int GF, bool FP32R>
+__device__ __forceinline__ float fold(float acc, float x) {
+    if constexpr (FP32R || GF == FSDP_F32) return acc + x;
+    else return round_to<GF>(acc + x);
+}
+
+// acc / N.  The specialised kernels (N in {1, 2, 4, 8}) multiply by 1/N: for a
+// power of two that product is the same correctly rounded value as the
+// quotient.  The generic kernel divides.  In 16-bit mode the quotient is then
+// rounded to the gradient format.
+template <int NW, int GF, bool FP32R>
+__device__ __forceinline__ float finish(float acc, const ReduceScalars& r) {
+    static_assert(NW == 0 || (NW & (NW - 1)) == 0, "specialised world sizes are powers of two");
+    float q = NW > 0 ? acc * r.inv_n : acc / r.n;
+    if constexpr (FP32R || GF == FSDP_F32) return q;
+    else return round_to<GF>(q);
+}
+
+
+// Gradient pointer accessors: gp(q) is rank q's block (shard-relative).
+template <int NW>
+struct GradsOf {                       // single-unit kernels: pointers by value
+    const GradPtrs<NW>& g;
+    __device__ __forceinline__ const void* operator()(int q) const { return g.p[q]; }
+};
+template <int NW>
+struct UnitGrads {                     // batched kernel: unit u of the launch's table
+    const UnitBatch<NW>& B;
+    int u;
+    __device__ __forceinline__ const void* operator()(int q) const { return B.g[u][q]; }
+};
+
+// Accumulate the N rank blocks of 8 elements into acc (all loads first).
+template <int NW, int GF, bool FP32R, typename GP>
+__device__ __forceinline__ void reduce8(const GP& gp, int world, int64_t vi, float (&acc)[8]) {
+    if constexpr (NW > 0) {
+        float x[NW][8];
+#pragma unroll
+        for (int q = 0; q < NW; ++q) load8<GF>(gp(q), vi, x[q]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = x[0][k];
+#pragma unroll
+        for (int q = 1; q < NW; ++q)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = fold<GF, FP32R>(acc[k], x[q][k]);
+    } else {
+        load8<GF>(gp(0), vi, acc);
+        int q = 1;
+        for (; q + 4 <= world; q += 4) {
+            float x[4][8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) load8<GF>(gp(q + j), vi, x[j]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[k] = fold<GF, FP32R>(acc[k], x[j][k]);
+        }
+        for (; q < world; ++q) {
+            float x[8];
+            load8<GF>(gp(q), vi, x);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = fold<GF, FP32R>(acc[k], x[k]);
+        }
+    }
+}
+
+template <int NW, int GF, bool FP32R, typename GP>
+__device__ __forceinline__ float reduce1(const GP& gp, int world, int64_t i) {
+    const int n = NW > 0 ? NW : world;
+    float acc = load1<GF>(gp(0), i);
+    for (int q = 1; q < n; ++q) acc = fold<GF, FP32R>(acc, load1<GF>(gp(q), i));
+    return acc;
+}
+
+
+// ----------------------------------------------------------------- launch
+// Launch with the events armed by set_launch_events(), if any, attached to the
+// kernel's own dispatch packet (hipExtLaunchKernel); the pair is consumed.
+void take_launch_events(hipEvent_t* start, hipEvent_t* stop);
+
+template <typename K, typename... Args>
+static void launch(K kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+    hipEvent_t a, b;
+    take_launch_events(&a, &b);
+    if (a || b)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, a, b, 0, args...);
+    else
+        kernel<<<grid, block, 0, st>>>(args...);
+}
+
+static inline int64_t grid_for(int64_t work, int cus) {
+    int64_t want = (work + kThreads - 1) / kThreads;
+    int64_t cap = (int64_t)cus * kBlocksPerCU;
+    if (want > cap) want = cap;
+    return want < 1 ? 1 : want;
+}
+
+}  // namespace fsdp

@@ -1,5 +1,5 @@
 // fsdp_kernels.h -- internal interface between the C ABI host layer
-// (fsdp_abi.cpp part of fsdp_shard.hip) and the gfx950 kernels.  Not installed.
+// (fsdp_abi.cpp, fsdp_offload.cpp) and the gfx950 kernels.  Not installed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,6 +20,21 @@ constexpr int64_t kSegChunkBytes = 32768;
 // Per-element AdamW constants, computed on the host (double, rounded once).
 struct AdamScalars {
     float decay, b1, omb1, b2, omb2, step_size, bc2_sqrt, eps;
+};
+
+// The pointwise optimizer of a unit launch and its per-launch scalars
+// (host-computed; each policy in fsdp_optim.h reads its own fields).
+enum OptKind { kOptAdamW = 0, kOptSgd = 1, kOptSgdMomentum = 2, kOptAdamax = 3, kOptAdadelta = 4 };
+
+struct OptParams {
+    int kind;
+    AdamScalars adam;                  // AdamW
+    float lr, wd;                      // SGD, SGD with momentum, Adadelta (lr); all but AdamW (wd)
+    float mu, omd;                     // SGD with momentum: momentum, 1 - dampening
+    int first, nesterov;               // SGD with momentum: step == 1, Nesterov
+    float clr, b1, omb1, b2;           // Adamax: lr / (1 - beta1^t), betas
+    float eps;                         // Adamax, Adadelta
+    float rho, omr;                    // Adadelta
 };
 
 // Division by N (n) or, for specialised power-of-two N, product with 1/N.
@@ -97,7 +112,7 @@ struct UnitLaunch {
     int state_dt;                  // FSDP_F32, or the 16-bit format shared with compute_dt
     bool gather;
     ReduceScalars rs;
-    AdamScalars as;
+    OptParams opt;
     void* stream;
 };
 
@@ -115,6 +130,11 @@ struct ReduceArgs {
 };
 
 hipError_t launch_units(const UnitArgs* units, int n, const UnitLaunch& L);
+// per optimizer family (fsdp_units_*.hip)
+hipError_t launch_units_adamw(const UnitArgs* units, int n, const UnitLaunch& L);
+hipError_t launch_units_sgd(const UnitArgs* units, int n, const UnitLaunch& L);
+hipError_t launch_units_adamax(const UnitArgs* units, int n, const UnitLaunch& L);
+hipError_t launch_units_adadelta(const UnitArgs* units, int n, const UnitLaunch& L);
 hipError_t launch_reduce_scatter(const ReduceArgs& a);
 void set_launch_events(void* start, void* stop);
 hipError_t launch_gather(const void* const* srcs, void* const* dsts, int n, int64_t bytes, int cus,

@@ -157,3 +157,48 @@ def test_step_units_validation():
     with_cs = (N.Unit * 1)(N.Unit(FAKE, FAKE + (1 << 28), FAKE + (2 << 28), g, peers, FAKE + (40 << 30),
                                   FAKE + (50 << 30), 1000))
     assert L.fsdp_step_units(with_cs, 1, 2, 0, N.BF16, 0, N.BF16, N.BF16, ctypes.byref(hp), None) == N.E_INVAL
+
+
+def test_step_units_optim_validation():
+    """The optimizer entry point checks hyper-parameters and the state buffers
+    its optimizer keeps before anything is launched."""
+    L = N.lib()
+    g = N.ptr_array([FAKE + (30 << 30), FAKE + (31 << 30)])
+    peers = N.ptr_array([0, FAKE + (32 << 30)])
+    full = FAKE + (40 << 30)
+
+    def call(hp, m=FAKE + (1 << 28), v=FAKE + (2 << 28), state=N.F32, compute=N.BF16, master=FAKE):
+        t = (N.Unit * 1)(N.Unit(master, m, v, g, peers, full, None, 1000))
+        return L.fsdp_step_units_optim(t, 1, 2, 0, N.BF16, 0, state, compute, ctypes.byref(hp), None)
+
+    H = N.OptimHP
+    assert L.fsdp_step_units_optim(None, 0, 2, 0, N.BF16, 0, N.F32, N.BF16, None, None) == N.E_INVAL
+    bad = H.sgd()
+    bad.kind = 9
+    assert call(bad) == N.E_INVAL                                       # unknown optimizer
+    assert call(H.sgd(lr=-1.0)) == N.E_INVAL
+    assert call(H.sgd(weight_decay=-0.1)) == N.E_INVAL
+    assert call(H.sgd(step=0)) == N.E_INVAL
+    assert call(H.sgd(momentum=-0.5)) == N.E_INVAL
+    assert call(H.sgd(nesterov=True)) == N.E_INVAL                      # Nesterov needs momentum
+    assert call(H.sgd(momentum=0.9, dampening=0.1, nesterov=True)) == N.E_INVAL   # ... and no dampening
+    assert call(H.adamax(betas=(1.0, 0.999))) == N.E_INVAL
+    assert call(H.adamax(eps=-1e-8)) == N.E_INVAL
+    assert call(H.adadelta(rho=1.5)) == N.E_INVAL
+    assert call(H.adamw(betas=(0.9, 1.0))) == N.E_INVAL
+    # 16-bit state is AdamW's only
+    for hp in (H.sgd(momentum=0.9), H.adamax(), H.adadelta()):
+        assert call(hp, state=N.BF16, compute=N.BF16) == N.E_DTYPE
+        assert "AdamW only" in L.fsdp_last_error().decode()
+    # the state buffers the optimizer keeps must be given
+    assert call(H.sgd(momentum=0.9), m=0) == N.E_INVAL
+    assert call(H.adamax(), v=0) == N.E_INVAL
+    assert call(H.adadelta(), m=0) == N.E_INVAL
+    assert call(H.adamw(), v=0) == N.E_INVAL
+    # ... and overlaps are checked among those only: an unused exp_avg_sq may
+    # point anywhere (here: into the full buffer) and is never touched, while a
+    # used one may not
+    assert call(H.adamax(), v=full + 8) == N.E_ALIAS
+    assert call(H.sgd(momentum=0.9), m=full + 8) == N.E_ALIAS
+    assert call(H.sgd(momentum=0.9), v=full + 8, master=0) == N.E_INVAL   # (stops at master, no launch)
+    assert H.sgd().n_states == 0 and H.sgd(momentum=0.9).n_states == 1 and H.adadelta().n_states == 2
