@@ -195,18 +195,24 @@ __device__ __forceinline__ float reduce1(const GP& gp, int world, int64_t i) {
 
 
 // ----------------------------------------------------------------- launch
-// Launch with the events armed by set_launch_events(), if any, attached to the
-// kernel's own dispatch packet (hipExtLaunchKernel); the pair is consumed.
+// Launch (with `lds` bytes of dynamic LDS per workgroup) with the events armed
+// by set_launch_events(), if any, attached to the kernel's own dispatch packet
+// (hipExtLaunchKernel); the pair is consumed.
 void take_launch_events(hipEvent_t* start, hipEvent_t* stop);
 
 template <typename K, typename... Args>
-static void launch(K kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+static void launch_lds(K kernel, dim3 grid, dim3 block, unsigned lds, hipStream_t st, Args... args) {
     hipEvent_t a, b;
     take_launch_events(&a, &b);
     if (a || b)
-        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, a, b, 0, args...);
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, st, a, b, 0, args...);
     else
-        kernel<<<grid, block, 0, st>>>(args...);
+        kernel<<<grid, block, lds, st>>>(args...);
+}
+
+template <typename K, typename... Args>
+static void launch(K kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+    launch_lds(kernel, grid, block, 0u, st, args...);
 }
 
 static inline int64_t grid_for(int64_t work, int cus) {

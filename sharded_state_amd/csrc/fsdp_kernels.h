@@ -14,6 +14,13 @@ namespace fsdp {
 #endif
 constexpr int kThreads = 256;                          // 4 wave64 per workgroup
 constexpr int kBlocksPerCU = FSDP_BLOCKS_PER_CU;       // grid cap = CUs * kBlocksPerCU (one trip per lane up to ~1e9 elements)
+// Dynamic LDS reserved by every unit-kernel workgroup (the kernel uses none):
+// with 160 KB of LDS per CU it holds residency at 2 workgroups (8 waves) per
+// CU.  Fewer tiles in flight at once streams the unit step's 8-11 address
+// streams through HBM measurably faster (+1.5 to +3 points of peak on every
+// workload, same-process A/B); the copy and reduce kernels, with one or two
+// loads per lane, need full occupancy instead and reserve none.
+constexpr unsigned kUnitLdsBytes = 81920;
 constexpr int kSegMax = 64;             // segments per flatten/unflatten launch
 constexpr int64_t kSegChunkBytes = 32768;
 

@@ -141,9 +141,11 @@ template <class OPT, int NW, int GF, bool FP32R, int CF, int SF>
 static hipError_t units_go(const UnitBatch<NW>& B, int64_t tiles, bool gather, const ReduceScalars& rs,
                            const OPT& op, hipStream_t st) {
     if (gather)
-        launch(k_units<OPT, NW, GF, FP32R, CF, true, SF>, dim3((unsigned)tiles), dim3(kThreads), st, B, rs, op);
+        launch_lds(k_units<OPT, NW, GF, FP32R, CF, true, SF>, dim3((unsigned)tiles), dim3(kThreads), kUnitLdsBytes,
+                   st, B, rs, op);
     else
-        launch(k_units<OPT, NW, GF, FP32R, CF, false, SF>, dim3((unsigned)tiles), dim3(kThreads), st, B, rs, op);
+        launch_lds(k_units<OPT, NW, GF, FP32R, CF, false, SF>, dim3((unsigned)tiles), dim3(kThreads), kUnitLdsBytes,
+                   st, B, rs, op);
     return hipGetLastError();
 }
 
