@@ -14,20 +14,18 @@ namespace fsdp {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef FSDP_NT_LOAD
-#define FSDP_NT_LOAD 0
-#endif
 #ifndef FSDP_NT_STORE
 #define FSDP_NT_STORE 1   // streamed outputs: non-temporal (measured +1-9% on the unit step)
 #endif
 // 16-byte global accesses; the streamed buffers are touched once per launch,
-// so wide stores carry the non-temporal hint.
+// so wide stores carry the non-temporal hint.  Loads carry it where it was
+// measured to pay (NT = true): in the unit step at its residency cap (+1 to +3
+// points of HBM peak on most workloads) and in the copies (+2%); the
+// read-mostly reduce-scatter alone is faster with plain loads (-6% with the hint).
+template <bool NT = false>
 __device__ __forceinline__ u32x4 ld16(const u32x4* p) {
-#if FSDP_NT_LOAD
-    return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
 }
 __device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
 #if FSDP_NT_STORE
@@ -63,17 +61,17 @@ template <> __device__ __forceinline__ uint32_t from_f32<FSDP_BF16>(float x) {
 template <int F> __device__ __forceinline__ float round_to(float x) { return to_f32<F>(from_f32<F>(x)); }
 
 // 8 consecutive elements of format F starting at element 8*vi (16-byte aligned).
-template <int F>
+template <int F, bool NT = false>
 __device__ __forceinline__ void load8(const void* __restrict__ base, int64_t vi, float (&x)[8]) {
     if constexpr (F == FSDP_F32) {
         const u32x4* q = reinterpret_cast<const u32x4*>(base) + 2 * vi;
-        u32x4 a = ld16(q), b = ld16(q + 1);
+        u32x4 a = ld16<NT>(q), b = ld16<NT>(q + 1);
         x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
         x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
         x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
         x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
     } else {
-        u32x4 a = ld16(reinterpret_cast<const u32x4*>(base) + vi);
+        u32x4 a = ld16<NT>(reinterpret_cast<const u32x4*>(base) + vi);
         uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -152,12 +150,12 @@ struct UnitGrads {                     // batched kernel: unit u of the launch's
 };
 
 // Accumulate the N rank blocks of 8 elements into acc (all loads first).
-template <int NW, int GF, bool FP32R, typename GP>
+template <int NW, int GF, bool FP32R, bool NT = false, typename GP>
 __device__ __forceinline__ void reduce8(const GP& gp, int world, int64_t vi, float (&acc)[8]) {
     if constexpr (NW > 0) {
         float x[NW][8];
 #pragma unroll
-        for (int q = 0; q < NW; ++q) load8<GF>(gp(q), vi, x[q]);
+        for (int q = 0; q < NW; ++q) load8<GF, NT>(gp(q), vi, x[q]);
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[k] = x[0][k];
 #pragma unroll
@@ -165,12 +163,12 @@ __device__ __forceinline__ void reduce8(const GP& gp, int world, int64_t vi, flo
 #pragma unroll
             for (int k = 0; k < 8; ++k) acc[k] = fold<GF, FP32R>(acc[k], x[q][k]);
     } else {
-        load8<GF>(gp(0), vi, acc);
+        load8<GF, NT>(gp(0), vi, acc);
         int q = 1;
         for (; q + 4 <= world; q += 4) {
             float x[4][8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) load8<GF>(gp(q + j), vi, x[j]);
+            for (int j = 0; j < 4; ++j) load8<GF, NT>(gp(q + j), vi, x[j]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -178,7 +176,7 @@ __device__ __forceinline__ void reduce8(const GP& gp, int world, int64_t vi, flo
         }
         for (; q < world; ++q) {
             float x[8];
-            load8<GF>(gp(q), vi, x);
+            load8<GF, NT>(gp(q), vi, x);
 #pragma unroll
             for (int k = 0; k < 8; ++k) acc[k] = fold<GF, FP32R>(acc[k], x[k]);
         }

@@ -61,7 +61,7 @@ __device__ __forceinline__ void copy_range(char* __restrict__ dst, const char* _
         u32x4* d = reinterpret_cast<u32x4*>(dst);
         const u32x4* s = reinterpret_cast<const u32x4*>(src);
         if (src) {
-            for (int64_t i = lane; i < nv; i += nthreads) st16(d + i, ld16(s + i));
+            for (int64_t i = lane; i < nv; i += nthreads) st16(d + i, ld16<true>(s + i));
         } else {
             const u32x4 z = {0u, 0u, 0u, 0u};
             for (int64_t i = lane; i < nv; i += nthreads) st16(d + i, z);

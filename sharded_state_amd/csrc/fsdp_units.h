@@ -39,12 +39,12 @@ __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t 
 #pragma unroll
         for (int j = 0; j < NW - 1; ++j)
 #pragma unroll
-            for (int w = 0; w < kW; ++w) peer[j][w] = ld16(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + kW * vi + w);
+            for (int w = 0; w < kW; ++w) peer[j][w] = ld16<true>(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + kW * vi + w);
     }
-    load8<SF>(p, vi, pp);
-    if constexpr (OPT::kStates >= 1) load8<SF>(m, vi, mm);
-    if constexpr (OPT::kStates >= 2) load8<SF>(v, vi, vv);
-    reduce8<NW, GF, FP32R>(UnitGrads<NW>{B, u}, B.world, vi, acc);
+    load8<SF, true>(p, vi, pp);
+    if constexpr (OPT::kStates >= 1) load8<SF, true>(m, vi, mm);
+    if constexpr (OPT::kStates >= 2) load8<SF, true>(v, vi, vv);
+    reduce8<NW, GF, FP32R, true>(UnitGrads<NW>{B, u}, B.world, vi, acc);
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the math
 #pragma unroll
     for (int k = 0; k < 8; ++k) op(finish<NW, GF, FP32R>(acc[k], rs), pp[k], mm[k], vv[k]);
@@ -67,7 +67,7 @@ __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t 
 #pragma unroll
                 for (int w = 0; w < kW; ++w)
                     st16(reinterpret_cast<u32x4*>(B.pdst[u][j]) + kW * vi + w,
-                         ld16(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + kW * vi + w));
+                         ld16<true>(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + kW * vi + w));
         }
     } else {
         if (out) store8<CF>(out, vi, pp);
