@@ -299,6 +299,29 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+def copy_ceiling(torch, N, lib, reps=20):
+    """Achievable HBM rate of a plain copy: 1 GiB through the library's gather
+    kernel (one shard), the ceiling a read+write stream reaches on this machine."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    copy = (N.ptr_array([a.data_ptr()]), 1, n // 4, N.F32, ctypes.c_void_p(b.data_ptr()), st)
+    for _ in range(3):
+        N.check("fsdp_unshard_gather", lib.fsdp_unshard_gather(*copy))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        lib.fsdp_unshard_gather(*copy)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_read": n, "bytes_written": n, "ms": round(ms, 5), "gbps": round(2 * n / ms / 1e6, 1)}
+
+
 def bench_offload(args, cfg, torch, ss, N, workloads):
     """--pipeline offload: the step of every unit slot with its optimizer state
     in pinned host memory (fsdp_offload_step_units over batches of distinct
@@ -450,24 +473,7 @@ def main():
     torch.cuda.set_device(0)
 
     if args.probe == "copy":
-        n = 1 << 30
-        a = torch.empty(n, dtype=torch.uint8, device="cuda")
-        b = torch.empty(n, dtype=torch.uint8, device="cuda")
-        a.fill_(1)
-        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        copy = (N.ptr_array([a.data_ptr()]), 1, n // 4, N.F32, ctypes.c_void_p(b.data_ptr()), st)
-        for _ in range(3):
-            N.check("fsdp_unshard_gather", lib.fsdp_unshard_gather(*copy))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        reps = 20
-        for _ in range(reps):
-            lib.fsdp_unshard_gather(*copy)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        print(json.dumps({"probe": "copy", "bytes_read": n, "bytes_written": n, "ms": ms,
-                          "gbps": 2 * n / ms / 1e6}))
+        print(json.dumps(dict(probe="copy", **copy_ceiling(torch, N, lib))))
         return
 
     cfg = workloads.CONFIGS[args.workload]
@@ -661,6 +667,9 @@ def main():
                         "(load: read, CRC32C, host-to-device)"}
 
     flat_ms = statistics.fmean(u.flatten_ms for u in pool)
+    ceil = copy_ceiling(torch, N, lib)
+    ceil["frac_of_peak"] = round(ceil["gbps"] / HBM_PEAK_GBPS, 4)
+    ceil["step_frac_of_copy"] = round(gbps / ceil["gbps"], 4)
     out = {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
@@ -680,6 +689,7 @@ def main():
         "flatten": {"avg_ms": round(flat_ms, 4),
                     "gbps": round(pool[0].flatten_bytes / (flat_ms * 1e-3) / 1e9, 1)},
         "roofline": roof,
+        "copy_ceiling": ceil,
         "cpu_baseline": cpu,
         "checkpoint": ckpt,
     }
