@@ -1,0 +1,95 @@
+"""GPU parity at the limits of the interface.
+
+* world = FSDP_MAX_WORLD (128) simulated ranks through the generic kernel, with
+  the fused all-gather (127 peer copies) and through the separate reduce-scatter;
+* a shard of more than 2**31 elements (64-bit element indexing end to end:
+  tile numbers, vector and byte offsets), sampled against the oracle, with the
+  last elements and the elements around 2**31 always in the sample.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sharded_state_amd as ss
+from parity import assert_bitexact, np_of
+from sharded_state_amd import _native as N
+
+pytestmark = pytest.mark.gpu
+
+
+def test_max_world_fused_step_and_gather():
+    world = N.MAX_WORLD
+    S = 263                                        # ragged: not a multiple of 8
+    g = torch.Generator(device="cpu").manual_seed(3)
+    grads = [(torch.randn(world * S, generator=g) * 1e-3).to(torch.float16).cuda() for _ in range(world)]
+    master0 = (torch.randn(world * S, generator=g) * 0.02)
+    peers = [(torch.randn(S, generator=g) * 0.02).to(torch.float16).cuda() for _ in range(world)]
+    hp = ss.AdamWHP(step=3)
+    gs = [np_of(x) for x in grads]
+    h = oracle.hp(step=3)
+    for rank in (0, 77, world - 1):
+        sl = slice(rank * S, (rank + 1) * S)
+        p = master0[sl].clone().cuda()
+        m = torch.zeros(S, device="cuda")
+        v = torch.zeros(S, device="cuda")
+        full = torch.empty(world * S, dtype=torch.float16, device="cuda")
+        ss.fsdp_step_unit(p, m, v, grads, rank, True, hp, [None if q == rank else peers[q] for q in range(world)],
+                          full)
+        rs = ss.fsdp_reduce_scatter_local(grads, rank, True, shard_numel=S)
+        torch.cuda.synchronize()
+        op, om, ov = np_of(master0[sl]), np.zeros(S, np.float32), np.zeros(S, np.float32)
+        gshard, comp = oracle.rank_step(gs, rank, op, om, ov, h, "f16", True, "f16")
+        assert_bitexact(np_of(rs), gshard, "reduce-scatter, rank %d of 128" % rank)
+        assert_bitexact(np_of(p), op, "master, rank %d of 128" % rank)
+        assert_bitexact(np_of(v), ov, "exp_avg_sq, rank %d of 128" % rank)
+        f = np_of(full)
+        assert_bitexact(f[sl], comp, "own slot, rank %d" % rank)
+        want = np.concatenate([comp if q == rank else np_of(peers[q]) for q in range(world)])
+        assert_bitexact(f, want, "gathered full buffer, rank %d" % rank)
+
+
+def test_world_above_max_is_rejected():
+    g = [torch.zeros(16, device="cuda") for _ in range(N.MAX_WORLD + 1)]
+    with pytest.raises(ss.FsdpError):
+        ss.fsdp_reduce_scatter_local(g, 0, True, shard_numel=0)
+
+
+def test_shard_of_more_than_2_31_elements():
+    """One rank (N = 1) with a shard of 2**31 + 4099 elements: fp16 gradient,
+    fp32 master / m / v (8.6 GB each), bf16 compute copy written into the
+    (single-slot) full buffer."""
+    S = (1 << 31) + 4099                            # ragged tail past 2**31
+    free, total = torch.cuda.mem_get_info()
+    need = S * (2 + 12 + 2) + (1 << 30)
+    if free < need:
+        pytest.skip("needs %.1f GB of free device memory, %.1f GB free" % (need / 1e9, free / 1e9))
+    print("S =", S, flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    grad = torch.empty(S, dtype=torch.float16, device="cuda")
+    master = torch.empty(S, device="cuda")
+    chunk = 1 << 28
+    for lo in range(0, S, chunk):                   # fill in chunks (no fp32 temporary of 8.6 GB)
+        hi = min(S, lo + chunk)
+        grad[lo:hi] = (torch.randn(hi - lo, device="cuda", generator=g) * 1e-3).to(torch.float16)
+        master[lo:hi] = torch.randn(hi - lo, device="cuda", generator=g) * 0.02
+    m = torch.zeros(S, device="cuda")
+    v = torch.zeros(S, device="cuda")
+    rng = np.random.default_rng(0)
+    two31 = 1 << 31
+    idx = np.unique(np.concatenate([np.arange(2048), np.arange(two31 - 2048, two31 + 2048),
+                                    np.arange(S - 4096, S), rng.integers(0, S, 200_000)]))
+    sel = torch.from_numpy(idx).cuda()
+    g0, p0 = np_of(grad[sel]), np_of(master[sel])
+    full = torch.empty(S, dtype=torch.bfloat16, device="cuda")
+    ss.fsdp_step_units([dict(master=master, exp_avg=m, exp_avg_sq=v, rank_grads=[grad], full=full,
+                             peer_shards=[None])], 0, True, ss.AdamWHP(step=1))
+    torch.cuda.synchronize()
+    h = oracle.hp(step=1)
+    pm, mm, vm = p0.copy(), np.zeros(idx.size, np.float32), np.zeros(idx.size, np.float32)
+    oracle.adamw(pm, mm, vm, oracle.to_f32(g0, "f16"), h)
+    assert_bitexact(np_of(master[sel]), pm, "master")
+    assert_bitexact(np_of(m[sel]), mm, "exp_avg")
+    assert_bitexact(np_of(v[sel]), vm, "exp_avg_sq")
+    assert_bitexact(np_of(full[sel]), oracle.cast(pm, "bf16"), "compute copy in the full buffer")
