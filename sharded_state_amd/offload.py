@@ -136,7 +136,7 @@ def prepare_offload_step_units(units, rank, fp32_reduce, hp, chunk_numel=0, n_th
         elif meta != (world, gdt, cdt, st.fp32_reduce, cdev.device):
             raise ValueError("unit %d: world, dtypes, fp32_reduce and device must match unit 0" % k)
         table[k] = u
-        keep.append(gptr)
+        keep.append((gptr, st, list(grads), cdev))    # the C side reads these at every call
     world, gdt, cdt, fp32, device = meta
     hp = _hp(hp)
     L = N.lib()
