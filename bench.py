@@ -630,7 +630,8 @@ def main():
                            "k_units (fused reduce-scatter + AdamW + cast)"),
                 "bytes_per_launch": int(bytes_per_launch), "avg_launch_ms": round(avg_ms, 5),
                 "timed_launches": len(durs),
-                "median_launch_ms": round(statistics.median(durs), 5)}
+                "median_launch_ms": round(statistics.median(durs), 5),
+                "min_launch_ms": round(min(durs), 5), "max_launch_ms": round(max(durs), 5)}
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -685,6 +686,7 @@ def main():
                    "gathers_per_step": G, "bytes_per_shard_element": per_elt,
                    "bytes_per_step": bytes_step},
         "shard_elements_per_s": round(S * cfg.blocks / (ms_step * 1e-3), 1),
+        "unit_elements_per_s": round(cfg.world * S * cfg.blocks / (ms_step * 1e-3), 1),
         "wall_s_timed": round(wall, 3),
         "flatten": {"avg_ms": round(flat_ms, 4),
                     "gbps": round(pool[0].flatten_bytes / (flat_ms * 1e-3) / 1e9, 1)},
