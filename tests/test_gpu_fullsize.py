@@ -150,3 +150,54 @@ def test_sharded_state_is_one_nth_of_unsharded_state():
         assert 0 <= sharded - exact <= slack
         assert abs(world * sharded - unsharded) <= world * slack + pad * per_elt
         del st
+
+
+@pytest.mark.parametrize("name,per_launch", [("gpt2-large-block", 36), ("gpt3-13b-block", 4),
+                                             ("llama70b-block", 2)])
+def test_full_size_batched_launch(name, per_launch):
+    """The benchmark's launch configuration: `per_launch` distinct full-size
+    units of rank 0 in one fsdp_step_units launch with the fused gather (and,
+    with two gathers per step, the persistent own shard).  Per unit: sampled
+    master, m, v and own-slot values against the oracle; the peer slots equal
+    the peer shards bit for bit."""
+    cfg = CONFIGS[name]
+    print("case", name, per_launch, "units per launch", flush=True)
+    dev = "cuda"
+    world = cfg.world
+    P, Pp, S = ss.fsdp_layout(cfg.numels, world)
+    cdt = TORCH_DTYPE[cfg.compute_dt]
+    hp = ss.AdamWHP(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.step)
+    h = oracle.hp(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.step)
+    gd = cfg.grad_dt
+    units, refs = [], []
+    for b in range(per_launch):
+        flat = ss.fsdp_flatten_pad(param_tensors(cfg, b, dev), world)
+        master = flat[:S].clone()
+        del flat
+        grads = [rank_grad(cfg, b, q, Pp, dev) for q in range(world)]
+        m, v = moments(cfg, b, 0, S, P, dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(100 + b)
+        peers = [None] + [(torch.randn(S, device=dev, generator=g) * 0.02).to(cdt) for _ in range(world - 1)]
+        full = torch.empty(world * S, dtype=cdt, device=dev)
+        persistent = torch.empty(S, dtype=cdt, device=dev) if cfg.gathers > 1 else None
+        rng = np.random.default_rng(b)
+        idx = np.unique(np.concatenate([np.arange(1024), np.arange(S - 1024, S), rng.integers(0, S, 20_000)]))
+        sel = torch.from_numpy(idx).to(dev)
+        refs.append((idx, sel, [np_of(x[sel]) for x in grads], np_of(master[sel]), np_of(m[sel]), np_of(v[sel])))
+        units.append(dict(master=master, exp_avg=m, exp_avg_sq=v, rank_grads=grads, peer_shards=peers, full=full,
+                          compute_shard=persistent))
+    ss.fsdp_step_units(units, 0, cfg.fp32_reduce, hp)
+    torch.cuda.synchronize()
+    for b, (u, (idx, sel, gs, p0, m0, v0)) in enumerate(zip(units, refs)):
+        p, mm, vv = p0.copy(), m0.copy(), v0.copy()
+        _, comp = oracle.elementwise_step(gs, p, mm, vv, h, gd, cfg.fp32_reduce, cfg.compute_dt)
+        assert_bitexact(np_of(u["master"][sel]), p, "master, unit %d" % b)
+        assert_bitexact(np_of(u["exp_avg"][sel]), mm, "exp_avg, unit %d" % b)
+        assert_bitexact(np_of(u["exp_avg_sq"][sel]), vv, "exp_avg_sq, unit %d" % b)
+        own = u["full"][:S]
+        assert_bitexact(np_of(own[sel]), comp, "own slot, unit %d" % b)
+        if u["compute_shard"] is not None:
+            assert _bits_equal(u["compute_shard"], own)
+        for q in range(1, world):
+            assert _bits_equal(u["full"][q * S:(q + 1) * S], u["peer_shards"][q]), (b, q)
