@@ -16,11 +16,13 @@
 // payload.  A file is written to "<path>.tmp", flushed, synced and renamed, so a
 // reader never sees a partial file under the final name.  Device buffers move
 // through two pinned host staging buffers: the copy of chunk k+1 overlaps the
-// file write of chunk k.
+// file write of chunk k, and each chunk's checksum runs on a helper thread
+// beside its write (save) or beside the read of the next chunk (load).
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <future>
 #include <cerrno>
 #include <cstdio>
 #include <cstring>
@@ -110,11 +112,80 @@ __attribute__((target("sse4.2"))) uint32_t crc_hw(uint32_t crc, const unsigned c
     return c32;
 }
 
+// The CRC register update is linear over GF(2): running it over `n` zero bytes
+// maps a register value x to Z_n(x) for a fixed 32x32 bit matrix Z_n.  So for
+// two consecutive blocks A, B:  reg(s, A || B) = Z_|B|(reg(s, A)) ^ reg(0, B),
+// which lets independent chains over parts of a buffer be combined.
+struct Gf2Matrix {
+    uint32_t col[32];   // col[i] = image of the register value with only bit i set
+};
+
+uint32_t gf2_apply(const Gf2Matrix& m, uint32_t v) {
+    uint32_t r = 0;
+    for (int i = 0; v; ++i, v >>= 1)
+        if (v & 1) r ^= m.col[i];
+    return r;
+}
+
+Gf2Matrix gf2_mul(const Gf2Matrix& a, const Gf2Matrix& b) {   // a after b
+    Gf2Matrix r;
+    for (int i = 0; i < 32; ++i) r.col[i] = gf2_apply(a, b.col[i]);
+    return r;
+}
+
+// Z_n: the register map of n zero bytes (reflected polynomial 0x82F63B78).
+Gf2Matrix zero_bytes_map(uint64_t n) {
+    Gf2Matrix bit;   // one zero bit: x -> (x >> 1) ^ (x & 1 ? poly : 0)
+    bit.col[0] = 0x82F63B78u;
+    for (int i = 1; i < 32; ++i) bit.col[i] = 1u << (i - 1);
+    Gf2Matrix byte = bit;
+    for (int k = 0; k < 3; ++k) byte = gf2_mul(byte, byte);   // 8 zero bits
+    Gf2Matrix r;
+    for (int i = 0; i < 32; ++i) r.col[i] = 1u << i;          // identity
+    while (n) {
+        if (n & 1) r = gf2_mul(byte, r);
+        byte = gf2_mul(byte, byte);
+        n >>= 1;
+    }
+    return r;
+}
+
+// Three independent hardware chains over thirds of the buffer (the crc32
+// instruction's latency is three times its issue interval), combined with Z.
+__attribute__((target("sse4.2"))) uint32_t crc_hw3(uint32_t crc, const unsigned char* p, size_t n) {
+    const size_t lane = (n / 3) & ~(size_t)7;
+    const unsigned char* pb = p + lane;
+    const unsigned char* pc = p + 2 * lane;
+    uint64_t a = crc, b = 0, c = 0;
+    for (size_t off = 0; off < lane; off += 8) {
+        uint64_t wa, wb, wc;
+        memcpy(&wa, p + off, 8);
+        memcpy(&wb, pb + off, 8);
+        memcpy(&wc, pc + off, 8);
+        a = __builtin_ia32_crc32di(a, wa);
+        b = __builtin_ia32_crc32di(b, wb);
+        c = __builtin_ia32_crc32di(c, wc);
+    }
+    const uint32_t c_rest = crc_hw((uint32_t)c, pc + lane, n - 3 * lane);   // lane C's tail
+    const size_t len_c = n - 2 * lane;
+    thread_local uint64_t z_len[2] = {~0ull, ~0ull};
+    thread_local Gf2Matrix z[2];
+    const uint64_t want[2] = {lane, len_c};
+    for (int k = 0; k < 2; ++k)
+        if (z_len[k] != want[k]) {
+            z[k] = zero_bytes_map(want[k]);
+            z_len[k] = want[k];
+        }
+    const uint32_t ab = gf2_apply(z[0], (uint32_t)a) ^ (uint32_t)b;
+    return gf2_apply(z[1], ab) ^ c_rest;
+}
+
 // Continue a CRC32C over n more bytes (state: the running value before the final xor).
 uint32_t crc_update(uint32_t state, const void* data, size_t n) {
     static const bool hw = __builtin_cpu_supports("sse4.2");
     const unsigned char* p = (const unsigned char*)data;
-    return hw ? crc_hw(state, p, n) : crc_soft(state, p, n);
+    if (!hw) return crc_soft(state, p, n);
+    return n >= (64u << 10) ? crc_hw3(state, p, n) : crc_hw(state, p, n);
 }
 
 // ------------------------------------------------------------------ staging
@@ -258,9 +329,13 @@ int fsdp_save_shard(const char* path, const fsdp_ckpt_info* info, const int64_t*
             if ((e = hipEventSynchronize(st.ev[k % 2])) != hipSuccess) return fsdp::hip_fail(e, "device-to-host copy");
             if (k + 1 < chunks.size() && (e = issue(k + 1)) != hipSuccess)
                 return fsdp::hip_fail(e, "device-to-host copy");
-            crc = crc_update(crc, st.buf[k % 2], chunks[k].n);
-            if (!write_all(out.f, st.buf[k % 2], chunks[k].n))
-                return fsdp::fail(FSDP_E_IO, "write to %s failed: %s", tmp.c_str(), strerror(errno));
+            // checksum on a helper thread while this thread writes the same bytes
+            const void* b = st.buf[k % 2];
+            const size_t n = chunks[k].n;
+            std::future<uint32_t> sum = std::async(std::launch::async, [crc, b, n] { return crc_update(crc, b, n); });
+            const bool wrote = write_all(out.f, b, n);
+            crc = sum.get();
+            if (!wrote) return fsdp::fail(FSDP_E_IO, "write to %s failed: %s", tmp.c_str(), strerror(errno));
         }
     } else {
         for (const Piece& p : pieces) {
@@ -356,19 +431,29 @@ int fsdp_load_shard(const char* path, fsdp_ckpt_info* info_out, void* master, vo
         if (e != hipSuccess) return fsdp::hip_fail(e, "pinned staging allocation");
         hipStream_t s = (hipStream_t)stream;
         size_t k = 0;
+        std::future<uint32_t> sum;   // checksum of the previous chunk, running on a helper thread
         for (const Piece& p : pieces) {
             for (uint64_t off = 0; off < p.bytes; off += kChunk, ++k) {
                 const size_t n = (size_t)std::min<uint64_t>(kChunk, p.bytes - off);
                 // the staging buffer of chunk k was last used by chunk k-2's copy
-                if (k >= 2 && (e = hipEventSynchronize(st.ev[k % 2])) != hipSuccess)
+                if (k >= 2 && (e = hipEventSynchronize(st.ev[k % 2])) != hipSuccess) {
+                    if (sum.valid()) sum.wait();
                     return fsdp::hip_fail(e, "host-to-device copy");
-                if (!read_all(in.f, st.buf[k % 2], n)) return fsdp::fail(FSDP_E_FORMAT, "%s: truncated payload", path);
-                crc = crc_update(crc, st.buf[k % 2], n);
+                }
+                const bool got = read_all(in.f, st.buf[k % 2], n);   // overlaps chunk k-1's checksum
+                if (sum.valid()) crc = sum.get();
+                if (!got) return fsdp::fail(FSDP_E_FORMAT, "%s: truncated payload", path);
+                const void* b = st.buf[k % 2];
+                sum = std::async(std::launch::async, [crc, b, n] { return crc_update(crc, b, n); });
                 e = hipMemcpyAsync(p.dst + off, st.buf[k % 2], n, hipMemcpyHostToDevice, s);
                 if (e == hipSuccess) e = hipEventRecord(st.ev[k % 2], s);
-                if (e != hipSuccess) return fsdp::hip_fail(e, "host-to-device copy");
+                if (e != hipSuccess) {
+                    sum.wait();
+                    return fsdp::hip_fail(e, "host-to-device copy");
+                }
             }
         }
+        if (sum.valid()) crc = sum.get();
         for (int i = 0; i < 2; ++i)
             if ((e = hipEventSynchronize(st.ev[i])) != hipSuccess) return fsdp::hip_fail(e, "host-to-device copy");
     } else {

@@ -47,6 +47,32 @@ def _state(S, seed):
     return [(rng.standard_normal(S) * s).astype(np.float32) for s in (0.02, 1e-3, 1e-6)]
 
 
+def _crc_table_ref(data):
+    """CRC32C with a byte table derived from the bitwise definition (fast
+    enough in Python for a few MB)."""
+    table = []
+    for i in range(256):
+        c = i
+        for _ in range(8):
+            c = (c >> 1) ^ (0x82F63B78 if c & 1 else 0)
+        table.append(c)
+    crc = 0xFFFFFFFF
+    for byte in data:
+        crc = (crc >> 8) ^ table[(crc ^ byte) & 0xFF]
+    return crc ^ 0xFFFFFFFF
+
+
+def test_crc32c_multi_lane_path_on_large_buffers():
+    """Buffers of 64 KiB and more take three interleaved hardware chains whose
+    registers are combined with the zero-bytes map; lengths on both sides of
+    the switch, with lane tails of every residue, must give the plain CRC."""
+    rng = np.random.default_rng(5)
+    assert _crc_table_ref(b"123456789") == 0xE3069283
+    for n in (65535, 65536, 65537, 65536 + 23, 3 * 65536 + 7, 200003, (1 << 20) + 5):
+        data = rng.integers(0, 256, size=n, dtype=np.uint8).tobytes()
+        assert _crc(data) == _crc_table_ref(data), n
+
+
 def test_host_round_trip(tmp_path):
     numels = [1000 * 999, 999, 1]
     P, Pp, S = ss.fsdp_layout(numels, 2)
