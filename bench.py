@@ -399,20 +399,20 @@ def bench_offload(args, cfg, torch, ss, N, workloads):
         torch.cuda.synchronize()
         return src.numel() * src.element_size() * reps / (time.perf_counter() - t) / 1e9
 
-    # host memory rates on the same cores: a threaded read-only pass (sum) and
-    # a threaded copy of 1 GiB
-    a = torch.ones(1 << 28, dtype=torch.float32)
+    # host memory rates on the same cores: a threaded copy and a threaded
+    # read-only pass (sum) of 2 GiB, the best of 7 passes each
+    a = torch.ones(1 << 29, dtype=torch.float32)
     b = torch.empty_like(a)
     b.copy_(a)
-    t = time.perf_counter()
-    for _ in range(reps):
-        b.copy_(a)
-    host_copy = 2 * a.numel() * 4 * reps / (time.perf_counter() - t) / 1e9
     a.sum()
-    t = time.perf_counter()
-    for _ in range(reps):
+    host_copy = host_read = 0.0
+    for _ in range(7):
+        t = time.perf_counter()
+        b.copy_(a)
+        host_copy = max(host_copy, 2 * a.numel() * 4 / (time.perf_counter() - t) / 1e9)
+        t = time.perf_counter()
         a.sum()
-    host_read = a.numel() * 4 * reps / (time.perf_counter() - t) / 1e9
+        host_read = max(host_read, a.numel() * 4 / (time.perf_counter() - t) / 1e9)
     del a, b
     d2h = copy_rate(st.grad_host, st.grad_dev)
     h2d = copy_rate(u.compute, st.compute_host)
@@ -433,13 +433,14 @@ def bench_offload(args, cfg, torch, ss, N, workloads):
         "step_pcie_gbps": round(pcie_b * cfg.blocks / (ms_step * 1e-3) / 1e9, 2),
     }
     # the bound of the offloaded step is host DRAM: the host AdamW's own bytes
-    # plus the copies' DMA into and out of host memory, against the measured
-    # read-only rate of the same cores (no published figure for this host)
-    ach = off["step_host_gbps_with_dma"]
+    # per step time, against the best threaded read-only rate of the same cores
+    # measured in this run (no published figure for this host); the copies'
+    # DMA through host memory is reported beside it (step_host_gbps_with_dma)
+    ach = off["step_host_gbps"]
     roof = {"bound": "host", "achieved": ach, "peak": off["host_read_gbps"], "unit": "GB/s",
             "frac": round(ach / off["host_read_gbps"], 4), "traffic": None,
-            "kernel": "fsdp_host_adamw (%d threads) + PCIe DMA; peak = threaded host read rate measured in "
-                      "this run" % threads}
+            "kernel": "fsdp_host_adamw (%d threads) inside the offloaded step; peak = best threaded host read "
+                      "rate measured in this run" % threads}
     out = {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,

@@ -122,11 +122,22 @@ __attribute__((target("avx2,f16c"))) inline __m256 load8_g(const void* g, int dt
     return _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(h), 16));
 }
 
+// The compute copy is written once and read next by the device's copy engine,
+// so with STREAM (8 elements aligned to their own size) it is written with
+// non-temporal stores: no read-for-ownership of the destination lines.
+template <bool STREAM>
+__attribute__((target("avx2,f16c"))) inline void put16(void* dst, __m128i x) {
+    if constexpr (STREAM) _mm_stream_si128((__m128i*)dst, x);
+    else _mm_storeu_si128((__m128i*)dst, x);
+}
+
+template <bool STREAM>
 __attribute__((target("avx2,f16c"))) inline void store8_c(void* c, int dt, int64_t i, __m256 x) {
     if (dt == FSDP_F32) {
-        _mm256_storeu_ps((float*)c + i, x);
+        if constexpr (STREAM) _mm256_stream_ps((float*)c + i, x);
+        else _mm256_storeu_ps((float*)c + i, x);
     } else if (dt == FSDP_F16) {
-        _mm_storeu_si128((__m128i*)((uint16_t*)c + i), _mm256_cvtps_ph(x, _MM_FROUND_TO_NEAREST_INT));
+        put16<STREAM>((uint16_t*)c + i, _mm256_cvtps_ph(x, _MM_FROUND_TO_NEAREST_INT));
     } else {
         // bfloat16: round the encoding at bit 16 to nearest even; NaN -> quiet NaN
         const __m256i u = _mm256_castps_si256(x);
@@ -140,10 +151,11 @@ __attribute__((target("avx2,f16c"))) inline void store8_c(void* c, int dt, int64
         const __m128i lo = _mm256_castsi256_si128(r), hi = _mm256_extracti128_si256(r, 1);
         const __m128i shuf = _mm_setr_epi8(0, 1, 4, 5, 8, 9, 12, 13, -1, -1, -1, -1, -1, -1, -1, -1);
         const __m128i pl = _mm_shuffle_epi8(lo, shuf), ph = _mm_shuffle_epi8(hi, shuf);
-        _mm_storeu_si128((__m128i*)((uint16_t*)c + i), _mm_unpacklo_epi64(pl, ph));
+        put16<STREAM>((uint16_t*)c + i, _mm_unpacklo_epi64(pl, ph));
     }
 }
 
+template <bool STREAM>
 __attribute__((target("avx2,f16c"))) void adamw_avx2(float* p, float* m, float* v, const void* g, int gdt, void* c,
                                                       int cdt, int64_t lo, int64_t hi, const Scalars& s) {
     const __m256 decay = _mm256_set1_ps(s.decay), b1 = _mm256_set1_ps(s.b1), omb1 = _mm256_set1_ps(s.omb1);
@@ -161,8 +173,9 @@ __attribute__((target("avx2,f16c"))) void adamw_avx2(float* p, float* m, float* 
         _mm256_storeu_ps(p + i, p2);
         _mm256_storeu_ps(m + i, m1);
         _mm256_storeu_ps(v + i, v1);
-        if (c) store8_c(c, cdt, i, p2);
+        if (c) store8_c<STREAM>(c, cdt, i, p2);
     }
+    if constexpr (STREAM) _mm_sfence();   // the streamed lines are visible before anyone reads them
     adamw_scalar(p, m, v, g, gdt, c, cdt, i, hi, s);
 }
 
@@ -172,7 +185,10 @@ void adamw_range(float* p, float* m, float* v, const void* g, int gdt, void* c, 
     const unsigned int csr = _mm_getcsr();
     _mm_setcsr(csr & ~0x8040u);
     static const bool avx2 = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("f16c");
-    if (avx2) adamw_avx2(p, m, v, g, gdt, c, cdt, lo, hi, s);
+    const uintptr_t c_lo = (uintptr_t)c + (uintptr_t)lo * (uintptr_t)fsdp::dt_size(cdt);
+    const bool stream = c && c_lo % (8 * (uintptr_t)fsdp::dt_size(cdt)) == 0;
+    if (avx2 && stream) adamw_avx2<true>(p, m, v, g, gdt, c, cdt, lo, hi, s);
+    else if (avx2) adamw_avx2<false>(p, m, v, g, gdt, c, cdt, lo, hi, s);
     else adamw_scalar(p, m, v, g, gdt, c, cdt, lo, hi, s);
     _mm_setcsr(csr);
 }
