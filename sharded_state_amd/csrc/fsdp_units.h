@@ -41,11 +41,11 @@ __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t 
 #pragma unroll
             for (int w = 0; w < kW; ++w) peer[j][w] = ld16<true>(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + kW * vi + w);
     }
-    // master/m/v loads: non-temporal except with gradients reduced in bf16,
-    // where plain loads measured faster (same process: +1.2 to +3.3 points
-    // with N = 2, a tie with N = 8; the fp16 / fp32-reduce shapes are faster
-    // with the hint)
-    constexpr bool kNtState = !(GF == FSDP_BF16 && !FP32R);
+    // master/m/v loads: non-temporal only with at most two ranks and gradients
+    // not reduced in bf16 (GPT-2 Large shape: +0.3 to +0.6 points in the bench);
+    // plain otherwise (bf16-reduced N = 2: +2.5; fp16 N = 8: +1.5; bf16 N = 8:
+    // a tie), measured same box, same bench
+    constexpr bool kNtState = NW >= 1 && NW <= 2 && !(GF == FSDP_BF16 && !FP32R);
     load8<SF, kNtState>(p, vi, pp);
     if constexpr (OPT::kStates >= 1) load8<SF, kNtState>(m, vi, mm);
     if constexpr (OPT::kStates >= 2) load8<SF, kNtState>(v, vi, vv);
