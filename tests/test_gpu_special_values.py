@@ -1,0 +1,115 @@
+"""Special values through the fused unit step for every optimizer, on the GPU
+against the oracle: NaN, +-Inf, subnormals, signed zeros and values that
+overflow binary16 in the parameter, the gradients and the optimizer state;
+fp16 and bf16 compute copies.  fp32 outputs must match bit for bit (NaN by
+NaN-ness), 16-bit outputs bit for bit away from NaN and NaN-ness at NaN."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sharded_state_amd as ss
+from parity import assert_bitexact, assert_ulp16, np_of
+
+pytestmark = pytest.mark.gpu
+
+H = ss.OptimHP
+OPTS = {
+    "adamw": None,
+    "sgd": H.sgd(lr=1e-2, weight_decay=1e-4),
+    "sgd-wd0": H.sgd(lr=1e-2),
+    "sgd-momentum": H.sgd(lr=1e-2, momentum=0.9, dampening=0.1, weight_decay=1e-4),
+    "sgd-nesterov": H.sgd(lr=1e-2, momentum=0.9, nesterov=True),
+    "adamax": H.adamax(weight_decay=0.01),
+    "adadelta": H.adadelta(weight_decay=0.01),
+}
+SPECIAL = np.array([np.nan, np.inf, -np.inf, 1e-40, -1e-40, 0.0, -0.0, 65504.0, 65520.0, 70000.0, -70000.0,
+                    3e38, -3e38, 5.9e-8, 3e-8, 1e-45, 1.0, -1.0], dtype=np.float32)
+
+
+def _orc(name, hp, step):
+    if name == "adamw":
+        return "adamw", oracle.hp(step=step)
+    if hp.kind == 1:
+        return "sgd", oracle.opt("sgd", step=step, lr=hp.lr, weight_decay=hp.weight_decay, momentum=hp.momentum,
+                                 dampening=hp.dampening, nesterov=bool(hp.nesterov))
+    if hp.kind == 2:
+        return "adamax", oracle.opt("adamax", step=step, lr=hp.lr, weight_decay=hp.weight_decay, beta1=hp.beta1,
+                                    beta2=hp.beta2, eps=hp.eps)
+    return "adadelta", oracle.opt("adadelta", step=step, lr=hp.lr, weight_decay=hp.weight_decay, rho=hp.rho,
+                                  eps=hp.eps)
+
+
+@pytest.mark.parametrize("cdt", ["f16", "bf16"])
+@pytest.mark.parametrize("name", list(OPTS))
+def test_special_values_every_optimizer(name, cdt):
+    world, S = 2, 1003                                 # ragged: the vector body and the scalar tail
+    rng = np.random.default_rng(len(name))
+    n = world * S
+
+    def with_specials(x, shift):
+        x = x.copy()
+        for k, val in enumerate(SPECIAL):
+            x[(k * 37 + shift) % n] = val
+            x[(k * 53 + shift + 900) % n] = val       # also in the other rank's block and the tail
+        return x
+
+    p = with_specials((rng.standard_normal(n) * 0.02).astype(np.float32), 0)
+    grads = [with_specials((rng.standard_normal(n) * 1e-3).astype(np.float32), 11 + q) for q in range(world)]
+    m = with_specials(np.abs(rng.standard_normal(n) * 1e-4).astype(np.float32), 5)
+    v = with_specials(np.abs(rng.standard_normal(n) * 1e-6).astype(np.float32), 7)
+    ctd = {"f16": torch.float16, "bf16": torch.bfloat16}[cdt]
+    hp = OPTS[name]
+    gd = [torch.from_numpy(g).cuda() for g in grads]
+    for step in (1, 2):
+        for r in range(world):
+            sl = slice(r * S, (r + 1) * S)
+            tp, tm, tv = (torch.from_numpy(x[sl].copy()).cuda() for x in (p, m, v))
+            cs = torch.empty(S, dtype=ctd, device="cuda")
+            unit = dict(master=tp, exp_avg=tm, exp_avg_sq=tv, rank_grads=gd, compute_shard=cs)
+            ss.fsdp_step_units([unit], r, True, ss.AdamWHP(step=step) if hp is None else hp.at_step(step))
+            torch.cuda.synchronize()
+            kind, o = _orc(name, hp, step)
+            op, om, ov = p[sl].copy(), m[sl].copy(), v[sl].copy()
+            _, oc = oracle.rank_step_opt(kind, grads, r, op, om, ov, o, "f32", True, cdt)
+            what = "%s %s step %d rank %d" % (name, cdt, step, r)
+            assert_bitexact(np_of(tp), op, "param, " + what)
+            n_states = 2 if hp is None else hp.n_states
+            if n_states >= 1:
+                assert_bitexact(np_of(tm), om, "state 1, " + what)
+            if n_states >= 2:
+                assert_bitexact(np_of(tv), ov, "state 2, " + what)
+            got = np_of(cs)
+            assert_ulp16(got, oc, cdt, "compute, " + what, tol=0)
+
+
+@pytest.mark.parametrize("sdt", ["bf16", "f16"])
+def test_special_values_16bit_state(sdt):
+    """The pure 16-bit state step (parameter, m, v stored in bf16 / fp16) with
+    special values in every input."""
+    world, S = 2, 1003
+    rng = np.random.default_rng(3)
+    n = world * S
+    torch_dt = {"f16": torch.float16, "bf16": torch.bfloat16}[sdt]
+
+    def with_specials(x, shift):
+        x = x.copy()
+        for k, val in enumerate(SPECIAL):
+            x[(k * 41 + shift) % n] = val
+        return x
+
+    p = oracle.f32_to(with_specials((rng.standard_normal(n) * 0.02).astype(np.float32), 0), sdt)
+    m = oracle.f32_to(with_specials(np.abs(rng.standard_normal(n) * 1e-4).astype(np.float32), 5), sdt)
+    v = oracle.f32_to(with_specials(np.abs(rng.standard_normal(n) * 1e-6).astype(np.float32), 9), sdt)
+    grads = [with_specials((rng.standard_normal(n) * 1e-3).astype(np.float32), 13 + q) for q in range(world)]
+    gd = [torch.from_numpy(g).cuda() for g in grads]
+    h = oracle.hp(step=2)
+    for r in range(world):
+        sl = slice(r * S, (r + 1) * S)
+        tp, tm, tv = (torch.from_numpy(x[sl].copy().view(np.int16)).view(torch_dt).cuda() for x in (p, m, v))
+        ss.fsdp_step_units([dict(master=tp, exp_avg=tm, exp_avg_sq=tv, rank_grads=gd)], r, True, ss.AdamWHP(step=2))
+        torch.cuda.synchronize()
+        op, om, ov = p[sl].copy(), m[sl].copy(), v[sl].copy()
+        oracle.rank_step16(grads, r, op, om, ov, h, "f32", True, sdt)
+        for nm, got, ref in (("param", tp, op), ("exp_avg", tm, om), ("exp_avg_sq", tv, ov)):
+            assert_ulp16(np_of(got), ref, sdt, "%s %s rank %d" % (nm, sdt, r), tol=0)
