@@ -65,9 +65,9 @@ def fsdp_flatten_pad(tensors, world, flat=None, stream=None):
     if any(t.dtype != dt for t in tensors):
         raise TypeError("all tensors of a unit must share one dtype")
     numels = [t.numel() for t in tensors]
-    _, padded, _ = fsdp_layout(numels, world)
     device = tensors[0].device
-    if flat is None:
+    if flat is None:   # (with `flat` given, the library call below is the only one)
+        _, padded, _ = fsdp_layout(numels, world)
         flat = torch.empty(padded, dtype=dt, device=device)
     _dev(flat, "flat")
     if flat.dtype != dt:
