@@ -35,6 +35,20 @@ __device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
 #endif
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <bool NT = false>
+__device__ __forceinline__ u32x2 ld8(const u32x2* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+__device__ __forceinline__ void st8(u32x2* p, u32x2 v) {
+#if FSDP_NT_STORE
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
 // ----------------------------------------------------------------- formats
 template <int F> __device__ __forceinline__ float to_f32(uint32_t bits);
 template <> __device__ __forceinline__ float to_f32<FSDP_F32>(uint32_t bits) { return __uint_as_float(bits); }
@@ -102,6 +116,68 @@ __device__ __forceinline__ void store8(void* __restrict__ base, int64_t vi, cons
     }
 }
 
+// Group layout of the unit kernel.  A group is 64 vectors, one per lane of a
+// wave: group g = vi / 64 holds elements [512 g, 512 g + 512), and lane
+// l = vi % 64 owns elements 512 g + 4 l + k and 512 g + 256 + 4 l + k (k < 4).
+// Each access instruction of the wave then covers one contiguous span (1 KB
+// of fp32, 512 B of a 16-bit format), so no cache line is half-written by one
+// instruction and completed by the next; with load8/store8 (8 consecutive
+// elements per lane) an fp32 access is two instructions of 32-byte-strided
+// halves.  Only for groups wholly inside the buffer.
+template <int F, bool NT = false>
+__device__ __forceinline__ void load8g(const void* __restrict__ base, int64_t vi, float (&x)[8]) {
+    const int64_t g = vi >> 6, l = vi & 63;
+    if constexpr (F == FSDP_F32) {
+        const u32x4* q = reinterpret_cast<const u32x4*>(base) + g * 128 + l;
+        u32x4 a = ld16<NT>(q), b = ld16<NT>(q + 64);
+        x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
+        x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+        x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
+        x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
+    } else {
+        const u32x2* q = reinterpret_cast<const u32x2*>(base) + g * 128 + l;
+        u32x2 a = ld8<NT>(q), b = ld8<NT>(q + 64);
+        uint32_t w[4] = {a.x, a.y, b.x, b.y};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[2 * k] = to_f32<F>(w[k] & 0xffffu);
+            x[2 * k + 1] = to_f32<F>(w[k] >> 16);
+        }
+    }
+}
+
+template <int F>
+__device__ __forceinline__ void store8g(void* __restrict__ base, int64_t vi, const float (&x)[8]) {
+    const int64_t g = vi >> 6, l = vi & 63;
+    if constexpr (F == FSDP_F32) {
+        u32x4* q = reinterpret_cast<u32x4*>(base) + g * 128 + l;
+        u32x4 a, b;
+        a.x = __float_as_uint(x[0]); a.y = __float_as_uint(x[1]);
+        a.z = __float_as_uint(x[2]); a.w = __float_as_uint(x[3]);
+        b.x = __float_as_uint(x[4]); b.y = __float_as_uint(x[5]);
+        b.z = __float_as_uint(x[6]); b.w = __float_as_uint(x[7]);
+        st16(q, a);
+        st16(q + 64, b);
+    } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = from_f32<F>(x[2 * k]) | (from_f32<F>(x[2 * k + 1]) << 16);
+        u32x2* q = reinterpret_cast<u32x2*>(base) + g * 128 + l;
+        u32x2 a, b;
+        a.x = w[0]; a.y = w[1];
+        b.x = w[2]; b.y = w[3];
+        st8(q, a);
+        st8(q + 64, b);
+    }
+}
+
+// The 8 elements of vector vi: consecutive (GROUP = false) or in the group layout.
+template <int F, bool NT, bool GROUP>
+__device__ __forceinline__ void load8x(const void* __restrict__ base, int64_t vi, float (&x)[8]) {
+    if constexpr (GROUP) load8g<F, NT>(base, vi, x);
+    else load8<F, NT>(base, vi, x);
+}
+
 template <int F>
 __device__ __forceinline__ float load1(const void* __restrict__ base, int64_t i) {
     if constexpr (F == FSDP_F32) return reinterpret_cast<const float*>(base)[i];
@@ -150,12 +226,12 @@ struct UnitGrads {                     // batched kernel: unit u of the launch's
 };
 
 // Accumulate the N rank blocks of 8 elements into acc (all loads first).
-template <int NW, int GF, bool FP32R, bool NT = false, typename GP>
+template <int NW, int GF, bool FP32R, bool NT = false, bool GROUP = false, typename GP>
 __device__ __forceinline__ void reduce8(const GP& gp, int world, int64_t vi, float (&acc)[8]) {
     if constexpr (NW > 0) {
         float x[NW][8];
 #pragma unroll
-        for (int q = 0; q < NW; ++q) load8<GF, NT>(gp(q), vi, x[q]);
+        for (int q = 0; q < NW; ++q) load8x<GF, NT, GROUP>(gp(q), vi, x[q]);
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[k] = x[0][k];
 #pragma unroll
@@ -163,12 +239,12 @@ __device__ __forceinline__ void reduce8(const GP& gp, int world, int64_t vi, flo
 #pragma unroll
             for (int k = 0; k < 8; ++k) acc[k] = fold<GF, FP32R>(acc[k], x[q][k]);
     } else {
-        load8<GF, NT>(gp(0), vi, acc);
+        load8x<GF, NT, GROUP>(gp(0), vi, acc);
         int q = 1;
         for (; q + 4 <= world; q += 4) {
             float x[4][8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) load8<GF, NT>(gp(q + j), vi, x[j]);
+            for (int j = 0; j < 4; ++j) load8x<GF, NT, GROUP>(gp(q + j), vi, x[j]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -176,7 +252,7 @@ __device__ __forceinline__ void reduce8(const GP& gp, int world, int64_t vi, flo
         }
         for (; q < world; ++q) {
             float x[8];
-            load8<GF, NT>(gp(q), vi, x);
+            load8x<GF, NT, GROUP>(gp(q), vi, x);
 #pragma unroll
             for (int k = 0; k < 8; ++k) acc[k] = fold<GF, FP32R>(acc[k], x[k]);
         }

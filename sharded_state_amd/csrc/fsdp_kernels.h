@@ -67,7 +67,7 @@ struct UnitBatch {
     int32_t world;
     int32_t npeers;
     int64_t tile_begin[kMax + 1];
-    int64_t nvec[kMax];
+    int64_t nvec[kMax];            // vectors, whole 64-vector groups (the rest: single elements)
     int64_t S[kMax];
     void* p[kMax];                 // state: fp32 master/m/v, or 16-bit parameter/m/v
     void* m[kMax];

@@ -21,10 +21,12 @@
 namespace fsdp {
 
 // ----------------------------------------------------------------- kernels
-// One unit's step on vector vi (8 elements): every load first (the N gradient
-// blocks, the parameter and the optimizer's state, the peers' compute vectors),
-// then the math, then every store.  With GATHER, `out` is this rank's slot of the full buffer and the
-// peers' vectors are copied into their slots.
+// One unit's step on vector vi (8 elements of a whole group in the group
+// layout, load8g): every load first (the N gradient blocks, the parameter and
+// the optimizer's state, the peers' compute vectors), then the math, then every
+// store.  With GATHER, `out` is this rank's slot of the full buffer and the
+// peers' vectors are copied into their slots (the copy moves the group's bytes
+// in contiguous 1 KB spans per instruction whatever the format).
 template <class OPT, int NW, int GF, bool FP32R, int CF, bool GATHER, int SF>
 __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t vi, const ReduceScalars& rs,
                                          const OPT& op) {
@@ -34,50 +36,52 @@ __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t 
     void* __restrict__ m = B.m[u];
     void* __restrict__ v = B.v[u];
     float acc[8], pp[8], mm[8] = {}, vv[8] = {};
+    const int64_t g = vi >> 6, l = vi & 63;
+    auto pv = [&](int w) -> int64_t { return g * (64 * kW) + w * 64 + l; };   // 16-byte index in the group
     u32x4 peer[kP][kW];
     if constexpr (GATHER && NW > 1) {
 #pragma unroll
         for (int j = 0; j < NW - 1; ++j)
 #pragma unroll
-            for (int w = 0; w < kW; ++w) peer[j][w] = ld16<true>(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + kW * vi + w);
+            for (int w = 0; w < kW; ++w) peer[j][w] = ld16<true>(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + pv(w));
     }
-    // master/m/v loads: non-temporal only with at most two ranks and gradients
-    // not reduced in bf16 (GPT-2 Large shape: +0.3 to +0.6 points in the bench);
-    // plain otherwise (bf16-reduced N = 2: +2.5; fp16 N = 8: +1.5; bf16 N = 8:
-    // a tie), measured same box, same bench
-    constexpr bool kNtState = NW >= 1 && NW <= 2 && !(GF == FSDP_BF16 && !FP32R);
-    load8<SF, kNtState>(p, vi, pp);
-    if constexpr (OPT::kStates >= 1) load8<SF, kNtState>(m, vi, mm);
-    if constexpr (OPT::kStates >= 2) load8<SF, kNtState>(v, vi, vv);
-    reduce8<NW, GF, FP32R, true>(UnitGrads<NW>{B, u}, B.world, vi, acc);
+    // parameter/state loads: non-temporal for fp32 state, and for 16-bit state
+    // with more than two ranks; plain for 16-bit state with N <= 2 (+0.8 points
+    // there; the hint gains 0.5 to 3 points on the fp32-state shapes and 0.7 on
+    // the N = 8 bf16-state shape; same box, same bench)
+    constexpr bool kNtState = SF == FSDP_F32 || NW == 0 || NW > 2;
+    load8g<SF, kNtState>(p, vi, pp);
+    if constexpr (OPT::kStates >= 1) load8g<SF, kNtState>(m, vi, mm);
+    if constexpr (OPT::kStates >= 2) load8g<SF, kNtState>(v, vi, vv);
+    reduce8<NW, GF, FP32R, true, true>(UnitGrads<NW>{B, u}, B.world, vi, acc);
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the math
 #pragma unroll
     for (int k = 0; k < 8; ++k) op(finish<NW, GF, FP32R>(acc[k], rs), pp[k], mm[k], vv[k]);
-    store8<SF>(p, vi, pp);
-    if constexpr (OPT::kStates >= 1) store8<SF>(m, vi, mm);
-    if constexpr (OPT::kStates >= 2) store8<SF>(v, vi, vv);
+    store8g<SF>(p, vi, pp);
+    if constexpr (OPT::kStates >= 1) store8g<SF>(m, vi, mm);
+    if constexpr (OPT::kStates >= 2) store8g<SF>(v, vi, vv);
     void* out = B.out[u];
     void* out2 = B.out2[u];
     if constexpr (GATHER) {
         // the unit step always has its own slot; keep the peer stores in the
         // same basic block as their loads so they are not sunk past the math
-        store8<CF>(out, vi, pp);
+        store8g<CF>(out, vi, pp);
         if constexpr (NW > 1) {
 #pragma unroll
             for (int j = 0; j < NW - 1; ++j)
 #pragma unroll
-                for (int w = 0; w < kW; ++w) st16(reinterpret_cast<u32x4*>(B.pdst[u][j]) + kW * vi + w, peer[j][w]);
+                for (int w = 0; w < kW; ++w) st16(reinterpret_cast<u32x4*>(B.pdst[u][j]) + pv(w), peer[j][w]);
         } else if constexpr (NW == 0) {
             for (int j = 0; j < B.npeers; ++j)
 #pragma unroll
                 for (int w = 0; w < kW; ++w)
-                    st16(reinterpret_cast<u32x4*>(B.pdst[u][j]) + kW * vi + w,
-                         ld16<true>(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + kW * vi + w));
+                    st16(reinterpret_cast<u32x4*>(B.pdst[u][j]) + pv(w),
+                         ld16<true>(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + pv(w)));
         }
     } else {
-        if (out) store8<CF>(out, vi, pp);
+        if (out) store8g<CF>(out, vi, pp);
     }
-    if (out2) store8<CF>(out2, vi, pp);
+    if (out2) store8g<CF>(out2, vi, pp);
 }
 
 // Element i of unit u, one lane (the tail past the last full vector, or every
@@ -111,9 +115,11 @@ __device__ __forceinline__ void unit_elem(const UnitBatch<NW>& B, int u, int64_t
 // Fused reduce-scatter + optimizer step + cast (+ all-gather with GATHER) over the
 // shards of up to UnitBatch<NW>::kMax units in one launch.  Workgroup b owns
 // tile b: unit u holds tiles [tile_begin[u], tile_begin[u+1]); its first
-// ceil(nvec/256) tiles are 256 vectors of 8 elements each, the rest 256
-// single elements (the tail, or the whole unit when unaligned).  One launch
-// pays the ramp-up and drain of the grid once for all its units.
+// ceil(nvec/256) tiles are 256 vectors of 8 elements each (nvec a multiple of
+// 64: whole groups, so each wave is either wholly in range or wholly out), the
+// rest 256 single elements (the tail of fewer than 520 elements, or the whole
+// unit when unaligned).  One launch pays the ramp-up and drain of the grid once
+// for all its units.
 // SF is the state format: FSDP_F32 for fp32 master/m/v with a separate compute
 // copy of format CF, or a 16-bit format (CF == SF) where the parameter shard is
 // itself the compute copy.
@@ -199,7 +205,8 @@ static hipError_t units_all(const UnitArgs* units, int n, const UnitLaunch& L, c
         for (; c < kMax && done + c < n; ++c) {
             const UnitArgs& a = units[done + c];
             B.tile_begin[c] = tiles;
-            B.nvec[c] = a.nvec;
+            const int64_t nvec = a.nvec & ~int64_t(63);   // whole groups; the rest joins the tail
+            B.nvec[c] = nvec;
             B.S[c] = a.S;
             B.p[c] = a.p;
             B.m[c] = a.m;
@@ -211,7 +218,7 @@ static hipError_t units_all(const UnitArgs* units, int n, const UnitLaunch& L, c
                 B.psrc[c][q] = (const char*)a.peer_src[q];
                 B.pdst[c][q] = (char*)a.peer_dst[q];
             }
-            tiles += (a.nvec + kThreads - 1) / kThreads + (a.S - 8 * a.nvec + kThreads - 1) / kThreads;
+            tiles += (nvec + kThreads - 1) / kThreads + (a.S - 8 * nvec + kThreads - 1) / kThreads;
         }
         B.count = c;
         B.tile_begin[c] = tiles;

@@ -72,6 +72,25 @@ def test_padding_and_odd_world_sizes(P, world, base):
     assert pad == oracle.padded_numel(P, world) - P
 
 
+@pytest.mark.parametrize("S", [8, 504, 512, 520, 1024, 1032, 2552, 6664])
+@pytest.mark.parametrize("base,world", [("gpt2-large-block", 2), ("llama70b-block", 8)])
+def test_shards_around_whole_groups(S, base, world):
+    """The unit kernel takes whole groups of 512 elements on the vector path and
+    the rest (up to 519 elements) one element per lane: shards just under, at
+    and just over multiples of 512 give the oracle's results."""
+    print("case", base, S, world, flush=True)
+    P = S * world
+    tensors = [("t0", (P // 2,)), ("t1", (P - P // 2,))]
+    cfg = scaled(CONFIGS[base], tensors, world=world)
+    run = UnitRun(cfg)
+    assert run.S == S
+    run.run_gpu()
+    run.run_oracle()
+    run.compare()
+    run.run_gpu_step_unit(persistent=True)
+    run.compare_step_unit()
+
+
 @pytest.mark.parametrize("step", [1, 10, 1000])
 def test_later_steps(step):
     run = UnitRun(scaled(CONFIGS["gpt2-xl-model"], gpt_block(64)))
