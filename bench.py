@@ -90,9 +90,12 @@ def parse():
     return ap.parse_args()
 
 
-def sizes(cfg, pipeline, state="f32", n_states=2):
-    """(fused kernel bytes, whole-step bytes) per shard element; the parameter
-    and each of the optimizer's n_states state buffers are read and written."""
+def sizes(cfg, pipeline, state="f32", n_states=2, split=False):
+    """(dominant kernel bytes, whole-step bytes) per shard element; the
+    parameter and each of the optimizer's n_states state buffers are read and
+    written.  Unit step: the kernel writes the own slot, and copies the N-1
+    peers' shards in its trip unless `split` (the library's launch plan,
+    unit_gather_split) leaves them to a launch of their own."""
     g = 4 if cfg.grad_dt == "f32" else 2
     c = 4 if cfg.compute_dt == "f32" else 2
     N, G = cfg.world, cfg.gathers
@@ -103,8 +106,9 @@ def sizes(cfg, pipeline, state="f32", n_states=2):
     if pipeline == "separate":
         fused = N * g + st + c
         return fused, fused + G * 2 * N * c
-    fused = N * g + st + c + 2 * (N - 1) * c + (c if G > 1 else 0)
-    return fused, fused + (G - 1) * 2 * N * c
+    kernel = N * g + st + c + (c if G > 1 else 0)
+    step = kernel + 2 * (N - 1) * c + (G - 1) * 2 * N * c
+    return (kernel if split else kernel + 2 * (N - 1) * c), step
 
 
 def optimizer_hp(name, cfg, N):
@@ -139,8 +143,13 @@ class Unit:
             mq, vq = (x.to(sd) for x in workloads.moments(cfg, block, q * S, S, P, dev))
             pq = flat[q * S:(q + 1) * S].clone()
             if state == "f32":
+                # reduce-scatter, then the step on the reduced shard (same bytes as the fused
+                # form; its one-rank kernel keeps set-up launches apart from the timed ones
+                # in profiles)
                 cq = torch.empty(S, dtype=cdt, device=dev)
-                ss.fsdp_sharded_adamw(pq, mq, vq, self.grads, q, cfg.fp32_reduce, hp, compute_shard=cq)
+                gq = ss.fsdp_reduce_scatter_local(self.grads, q, cfg.fp32_reduce)
+                ss.fsdp_sharded_adamw(pq, mq, vq, [gq], 0, cfg.fp32_reduce, hp, compute_shard=cq)
+                del gq
             else:
                 ss.fsdp_step_units([dict(master=pq, exp_avg=mq, exp_avg_sq=vq, rank_grads=self.grads)], q,
                                    cfg.fp32_reduce, hp)
@@ -659,15 +668,22 @@ def main():
         evs.close()
         avg_ms = statistics.fmean(durs)
         units_per_launch = cfg.blocks / len(groups)
+        split = unit_pipe and ss.unit_gather_split(pool[0].master.dtype, n_states,
+                                                   S * max(n for _, n, _, _ in groups))
+        fused_b, _ = sizes(cfg, "separate" if args.pipeline == "separate" else "unit", args.state, n_states,
+                           split)
         bytes_per_launch = fused_b * S * units_per_launch
         achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
         tag = args.pipeline if args.optimizer == "adamw" else "%s-%s" % (args.pipeline, args.optimizer)
         traffic = traffic_from_profiles("%s_%s" % (tag, cfg.name), kernel_source_hash())
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": ("k_units<GATHER> (fused reduce-scatter + AdamW + cast + all-gather, %g units per "
-                           "launch)" % units_per_launch if unit_pipe else
-                           "k_units (fused reduce-scatter + AdamW + cast)"),
+                "kernel": (("k_units<GATHER> (fused reduce-scatter + optimizer + cast + all-gather, %g units "
+                            "per launch)" if not split else
+                            "k_units (fused reduce-scatter + optimizer + cast + own-slot write, %g units per "
+                            "launch; the peers' slots follow in one batched copy launch)") % units_per_launch
+                           if unit_pipe else "k_units (fused reduce-scatter + optimizer + cast)"),
+                "peer_copies_in_own_launch": bool(split),
                 "bytes_per_launch": int(bytes_per_launch), "avg_launch_ms": round(avg_ms, 5),
                 "timed_launches": len(durs),
                 "median_launch_ms": round(statistics.median(durs), 5),

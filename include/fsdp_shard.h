@@ -51,7 +51,7 @@ extern "C" {
 
 #define FSDP_API __attribute__((visibility("default")))
 
-#define FSDP_ABI_VERSION 5
+#define FSDP_ABI_VERSION 6
 #define FSDP_MAX_WORLD 128
 
 typedef enum fsdp_dtype {
@@ -179,10 +179,13 @@ FSDP_API int fsdp_sharded_adamw(float* master, float* exp_avg, float* exp_avg_sq
 FSDP_API int fsdp_unshard_gather(const void* const* shards, int32_t world, int64_t shard_numel,
                                  fsdp_dtype dt, void* full_out, void* stream);
 
-/* One FSDP unit's step in one launch: the fused reduce-scatter + AdamW + cast
- * of fsdp_sharded_adamw followed by the all-gather of fsdp_unshard_gather,
- * with this rank's compute shard written straight into its slot of the full
- * buffer (the all-gather then moves only the peers' shards).  Sources as for
+/* One FSDP unit's step: the fused reduce-scatter + AdamW + cast of
+ * fsdp_sharded_adamw followed by the all-gather of fsdp_unshard_gather, with
+ * this rank's compute shard written straight into its slot of the full buffer
+ * (the all-gather then moves only the peers' shards).  The peers' shards are
+ * copied in the step's own trip (one launch), or, where fsdp_unit_gather_split
+ * says so, by a second launch after the step (fsdp_time_next_launch times the
+ * step).  Sources as for
  * those two calls; [TR] "From all-reduce to sharded parameters": after the
  * reduce-scatter each rank updates its own shard, and the full weights are
  * gathered from every rank's shard before the next compute.
@@ -238,7 +241,10 @@ typedef struct fsdp_unit {
  * compute_dt must equal state_dt, the parameter shard is the compute shard
  * (compute_shard NULL), and with full_out the gather copies it.
  * Units are packed into launches of up to 40 (world <= 2), 24 (world 4) or
- * 16 (world 8) units; other world sizes take one launch per unit.  No output
+ * 16 (world 8) units; other world sizes take one launch per unit.  With
+ * full_out, a launch copies the peers' shards of its units in its own trip, or,
+ * where fsdp_unit_gather_split says so for its units' shard elements, is
+ * followed by one launch that copies them (up to 128 copies).  No output
  * of any unit may overlap an input or an output of any unit (FSDP_E_ALIAS): a
  * unit may appear only once per call. */
 FSDP_API int fsdp_step_units(const fsdp_unit* units, int32_t n_units, int32_t world, int32_t rank,
@@ -298,6 +304,17 @@ typedef struct fsdp_optim_hp {
 FSDP_API int fsdp_step_units_optim(const fsdp_unit* units, int32_t n_units, int32_t world, int32_t rank,
                                    fsdp_dtype grad_dt, int32_t fp32_reduce, fsdp_dtype state_dt,
                                    fsdp_dtype compute_dt, const fsdp_optim_hp* hp, void* stream);
+
+/* Launch plan of the unit step, for tools that time or count its kernels
+ * (host only).  1 when a step launch of fsdp_step_units / fsdp_step_units_optim
+ * / fsdp_step_unit with full_out, whose units hold `shard_elements` shard
+ * elements together, writes only the own slots and a second launch copies the
+ * peers' shards; 0 when the step launch copies them in its own trip.  Measured
+ * rule: 1 for fp32 state (state_dt FSDP_F32) with an optimizer that keeps
+ * n_states >= 1 state buffers (AdamW, Adamax, Adadelta: 2; SGD with momentum: 1;
+ * SGD without momentum: 0) and shard_elements >= 2^24.  FSDP_E_INVAL for
+ * n_states outside [0, 2] or shard_elements < 0, FSDP_E_DTYPE for state_dt. */
+FSDP_API int fsdp_unit_gather_split(fsdp_dtype state_dt, int32_t n_states, int64_t shard_elements);
 
 /* Per-tensor views of the full buffer.  [P3] "The FSDP Unit" (use_orig_params):
  * tensor k is full[off_k : off_k + numel_k]; the padding belongs to no view.

@@ -20,6 +20,7 @@ from .api import (  # noqa: F401
     prepare_step_units,
     fsdp_unflatten_views,
     fsdp_unshard_gather,
+    unit_gather_split,
     view_table,
 )
 from .state import RankState  # noqa: F401
@@ -37,5 +38,5 @@ __all__ = [
     "fsdp_reduce_scatter_local", "fsdp_sharded_adamw", "fsdp_step_unit", "fsdp_step_units", "prepare_step_units", "fsdp_unshard_gather",
     "fsdp_unflatten_views", "view_table", "RankState", "save_shard", "load_shard", "shard_info",
     "shard_path", "consolidate", "fsdp_host_adamw", "fsdp_offload_step", "fsdp_offload_step_units",
-    "prepare_offload_step_units", "OffloadState",
+    "prepare_offload_step_units", "OffloadState", "unit_gather_split",
 ]

@@ -55,6 +55,16 @@ def fsdp_layout(numels, world):
     return total.value, padded.value, shard.value
 
 
+def unit_gather_split(state_dtype, n_states, shard_elements):
+    """True when a unit-step launch with a gather over `shard_elements` shard
+    elements (all its units together) writes only the own slots and a second
+    launch copies the peers' shards; False when the step copies them itself."""
+    rc = N.lib().fsdp_unit_gather_split(dtype_code(state_dtype), int(n_states), int(shard_elements))
+    if rc < 0:
+        check("fsdp_unit_gather_split", rc)
+    return rc == 1
+
+
 def fsdp_flatten_pad(tensors, world, flat=None, stream=None):
     """Flatten the unit's tensors into one buffer padded with +0 to a multiple of
     `world`.  Returns the flat buffer (allocated if `flat` is None)."""

@@ -313,6 +313,7 @@ int launch_built(const char* fn, std::vector<UnitBuild>& units, int32_t world, i
     L.gather = gather;
     L.rs = reduce_scalars(world);
     L.opt = op;
+    L.cus = cu_count();
     L.stream = stream;
     (void)hipGetLastError();
     hipError_t e = fsdp::launch_units(args.data(), (int)args.size(), L);
@@ -327,6 +328,15 @@ extern "C" {
 int fsdp_abi_version(void) { return FSDP_ABI_VERSION; }
 
 const char* fsdp_last_error(void) { return fsdp::last_error(); }
+
+int fsdp_unit_gather_split(fsdp_dtype state_dt, int32_t n_states, int64_t shard_elements) {
+    if (!valid_dtype(state_dt)) return fail(FSDP_E_DTYPE, "fsdp_unit_gather_split: dtype %d unsupported", (int)state_dt);
+    if (n_states < 0 || n_states > 2 || shard_elements < 0)
+        return fail(FSDP_E_INVAL, "fsdp_unit_gather_split: n_states %d / shard_elements %lld out of range", n_states,
+                    (long long)shard_elements);
+    ok();
+    return fsdp::split_gather(state_dt, n_states, shard_elements) ? 1 : 0;
+}
 
 int fsdp_time_next_launch(void* start_event, void* stop_event) {
     fsdp::set_launch_events(start_event, stop_event);

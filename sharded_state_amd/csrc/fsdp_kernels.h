@@ -88,6 +88,17 @@ struct CopyList {
     char* dst[MAXN];
 };
 
+// Batched copies (the peers' slots of the full buffers of a table of units):
+// copy j moves bytes[j] bytes src[j] -> dst[j].
+struct CopyBatch {
+    static constexpr int kMax = 128;
+    int32_t count;
+    const char* src[kMax];
+    char* dst[kMax];
+    int64_t bytes[kMax];
+};
+static_assert(sizeof(CopyBatch) <= 4000, "copy tables travel in kernel arguments");
+
 struct SegBatch {
     int32_t count;
     int64_t chunk_begin[kSegMax + 1];
@@ -120,6 +131,7 @@ struct UnitLaunch {
     bool gather;
     ReduceScalars rs;
     OptParams opt;
+    int cus;                       // compute units of the device (grid caps)
     void* stream;
 };
 
@@ -144,6 +156,16 @@ hipError_t launch_units_adamax(const UnitArgs* units, int n, const UnitLaunch& L
 hipError_t launch_units_adadelta(const UnitArgs* units, int n, const UnitLaunch& L);
 hipError_t launch_reduce_scatter(const ReduceArgs& a);
 void set_launch_events(void* start, void* stop);
+hipError_t launch_copies(const CopyBatch& b, int cus, void* stream);
+
+// Whether a unit-step launch with a gather, over `elems` shard elements in
+// all, leaves the peers' copies to a launch of their own (peer_copies in
+// fsdp_units.h): fp32 state, an optimizer that keeps state, and at least 2^24
+// shard elements; otherwise the step's own trip copies them.
+constexpr int64_t kSplitGatherElems = int64_t(1) << 24;
+inline bool split_gather(int state_dt, int n_states, int64_t elems) {
+    return state_dt == FSDP_F32 && n_states >= 1 && elems >= kSplitGatherElems;
+}
 hipError_t launch_gather(const void* const* srcs, void* const* dsts, int n, int64_t bytes, int cus,
                          void* stream);
 hipError_t launch_segments(const SegBatch& b, int64_t chunks, void* stream);

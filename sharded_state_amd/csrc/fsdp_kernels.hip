@@ -93,6 +93,14 @@ __global__ __launch_bounds__(kThreads) void k_gather(CopyList<MAXN> L, int64_t b
                (int64_t)gridDim.x * kThreads);
 }
 
+// Batched copies: blockIdx.y selects copy j; blocks along x stride over its bytes
+// (copies shorter than the longest leave their surplus blocks idle).
+__global__ __launch_bounds__(kThreads) void k_copies(CopyBatch L) {
+    const int j = blockIdx.y;
+    copy_range(L.dst[j], L.src[j], L.bytes[j], (int64_t)blockIdx.x * kThreads + threadIdx.x,
+               (int64_t)gridDim.x * kThreads);
+}
+
 // Segmented copy for flatten/unflatten: workgroup b handles chunk b of the
 // batch; segment k owns chunks [chunk_begin[k], chunk_begin[k+1]).
 __global__ __launch_bounds__(kThreads) void k_segments(SegBatch B) {
@@ -186,6 +194,18 @@ hipError_t launch_gather(const void* const* srcs, void* const* dsts, int n, int6
         for (int j = 0; j < n; ++j) { L.src[j] = (const char*)srcs[j]; L.dst[j] = (char*)dsts[j]; }
         launch(k_gather<FSDP_MAX_WORLD>, grid, dim3(kThreads), (hipStream_t)stream, L, bytes);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_copies(const CopyBatch& b, int cus, void* stream) {
+    int64_t most = 0;
+    for (int j = 0; j < b.count; ++j) most = b.bytes[j] > most ? b.bytes[j] : most;
+    if (b.count <= 0 || most <= 0) return hipSuccess;
+    int64_t per = (most / 16 + kThreads - 1) / kThreads;
+    const int64_t cap = ((int64_t)cus * kBlocksPerCU + b.count - 1) / b.count;
+    if (per > cap) per = cap;
+    if (per < 1) per = 1;
+    launch(k_copies, dim3((unsigned)per, (unsigned)b.count), dim3(kThreads), (hipStream_t)stream, b);
     return hipGetLastError();
 }
 

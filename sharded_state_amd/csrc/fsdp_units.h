@@ -1,7 +1,9 @@
 // fsdp_units.h -- the fused unit kernel of libfsdp_shard.so: reduce-scatter
 // of the N ranks' gradient blocks, a pointwise optimizer step on the rank's
-// shard, the cast to the compute format and, optionally, the all-gather of the
-// full buffer, for a table of units per launch.  Templated on the optimizer
+// shard, the cast to the compute format and the write of the own slot of the
+// full buffer, for a table of units per launch; then the rest of the
+// all-gather (the peers' slots): in the step's own trip, or as a batched copy
+// launch of its own where that was measured faster (peer_copies).  Templated on the optimizer
 // policy (fsdp_optim.h); each optimizer family is instantiated in a
 // translation unit of its own (fsdp_units_*.hip).  Not installed.
 //
@@ -191,6 +193,41 @@ static hipError_t units_batch(const UnitBatch<NW>& B, int64_t tiles, const UnitL
     return units_cf<OPT, NW, FSDP_BF16, false>(B, tiles, L, op, st);
 }
 
+// The all-gather of a table of units after their step: every unit's N-1 peer
+// shards copied into their slots of its full buffer, batched into launches of
+// up to CopyBatch::kMax copies.
+//
+// When split_gather() holds, the step and the copies run as two launches: the
+// fused form (the peer copies in the step's own trip, GATHER = true) keeps 8 to
+// 26 address streams in flight at once, and draining the step before the copies
+// start was measured faster for fp32 state with an optimizer that keeps state
+// (same box, two repetitions, % of 8 TB/s for the whole step: GPT-2 Large x36
+// 73.1 -> 75.5, GPT-2 XL 74.7 -> 76.0, 13B x40 72.0 -> 78.7, 70B x96 69.9 ->
+// 77.2; Adamax and SGD with momentum +1.7 and +2.2 points).  The fused form
+// stays where the second launch lost: 16-bit state (1 to 11%), SGD without
+// momentum (1.9 points) and launches of fewer than 2^24 shard elements (GPT-2
+// Large, one 9.8M-element unit per launch: 2.1 points).  The copies as
+// workgroups of the same launch, after the step's tiles, lost to both forms.
+template <int NW>
+static hipError_t peer_copies(const UnitBatch<NW>& B, int c, const UnitLaunch& L) {
+    const int64_t cs = L.compute_dt == FSDP_F32 ? 4 : 2;
+    CopyBatch cb;
+    cb.count = 0;
+    for (int k = 0; k < c; ++k)
+        for (int q = 0; q < B.npeers; ++q) {
+            if (cb.count == CopyBatch::kMax) {
+                hipError_t e = launch_copies(cb, L.cus, L.stream);
+                if (e != hipSuccess) return e;
+                cb.count = 0;
+            }
+            cb.src[cb.count] = B.psrc[k][q];
+            cb.dst[cb.count] = B.pdst[k][q];
+            cb.bytes[cb.count] = B.S[k] * cs;
+            ++cb.count;
+        }
+    return launch_copies(cb, L.cus, L.stream);
+}
+
 // Pack the units into tables of at most kMax and launch one grid per table.
 template <class OPT, int NW>
 static hipError_t units_all(const UnitArgs* units, int n, const UnitLaunch& L, const OPT& op) {
@@ -224,6 +261,18 @@ static hipError_t units_all(const UnitArgs* units, int n, const UnitLaunch& L, c
         B.tile_begin[c] = tiles;
         done += c;
         if (tiles == 0) continue;
+        int64_t elems = 0;
+        for (int k = 0; k < c; ++k) elems += B.S[k];
+        if (L.gather && split_gather(L.state_dt, OPT::kStates, elems)) {
+            // the step writes the own slot, then one launch copies every
+            // unit's peer shards into their slots (peer_copies)
+            UnitLaunch L1 = L;
+            L1.gather = false;
+            hipError_t e = units_batch<OPT, NW>(B, tiles, L1, op);
+            if (e == hipSuccess) e = peer_copies(B, c, L);
+            if (e != hipSuccess) return e;
+            continue;
+        }
         hipError_t e = units_batch<OPT, NW>(B, tiles, L, op);
         if (e != hipSuccess) return e;
     }

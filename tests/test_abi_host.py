@@ -202,3 +202,21 @@ def test_step_units_optim_validation():
     assert call(H.sgd(momentum=0.9), m=full + 8) == N.E_ALIAS
     assert call(H.sgd(momentum=0.9), v=full + 8, master=0) == N.E_INVAL   # (stops at master, no launch)
     assert H.sgd().n_states == 0 and H.sgd(momentum=0.9).n_states == 1 and H.adadelta().n_states == 2
+
+
+def test_unit_gather_split_launch_plan():
+    """The launch-plan query: the peers' copies get a launch of their own only
+    for fp32 state, an optimizer that keeps state, and >= 2^24 shard elements."""
+    import torch
+    f32, bf16 = torch.float32, torch.bfloat16
+    assert ss.unit_gather_split(f32, 2, 1 << 24)
+    assert ss.unit_gather_split(f32, 1, 1 << 30)
+    assert not ss.unit_gather_split(f32, 2, (1 << 24) - 1)
+    assert not ss.unit_gather_split(f32, 0, 1 << 30)
+    assert not ss.unit_gather_split(bf16, 2, 1 << 30)
+    assert not ss.unit_gather_split(torch.float16, 2, 1 << 30)
+    for bad in ((f32, 3, 10), (f32, -1, 10), (f32, 2, -1)):
+        with pytest.raises(ss.FsdpError):
+            ss.unit_gather_split(*bad)
+    lib = ss.lib()
+    assert lib.fsdp_unit_gather_split(9, 2, 10) == -2          # FSDP_E_DTYPE

@@ -1,0 +1,116 @@
+"""GPU: the two forms of the unit step's all-gather give the same bytes.
+
+A step launch with a gather copies the peers' shards in its own trip, or -- for
+fp32 state, an optimizer that keeps state, and at least 2^24 shard elements in
+the launch (unit_gather_split) -- writes only the own slots and leaves the
+copies to a batched copy launch.  Here the same units are stepped once as one
+batch (past the threshold: two launches) and once one unit per call (under it:
+the fused form), from identical inputs, and every output is compared bit for
+bit; the full buffers are also checked against the concatenation of the own
+compute shard and the peers' shards.
+"""
+import pytest
+import torch
+
+import sharded_state_amd as ss
+from parity import np_of
+
+pytestmark = pytest.mark.gpu
+
+SPLIT_ELEMS = 1 << 24
+
+
+def _bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+
+
+def _units(world, rank, sizes, gdt, cdt, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    out = []
+    for S in sizes:
+        grads = [(torch.randn(world * S, device="cuda", generator=g) * 1e-3).to(gdt) for _ in range(world)]
+        master = torch.randn(S, device="cuda", generator=g) * 0.02
+        m = torch.randn(S, device="cuda", generator=g) * 1e-3
+        v = torch.rand(S, device="cuda", generator=g) * 1e-6
+        peers = [None if q == rank else (torch.randn(S, device="cuda", generator=g) * 0.02).to(cdt)
+                 for q in range(world)]
+        out.append(dict(master=master, exp_avg=m, exp_avg_sq=v, rank_grads=grads, peer_shards=peers,
+                        full=torch.full((world * S,), float("nan"), dtype=cdt, device="cuda")))
+    return out
+
+
+def _clone(units):
+    return [dict(master=u["master"].clone(), exp_avg=u["exp_avg"].clone(), exp_avg_sq=u["exp_avg_sq"].clone(),
+                 rank_grads=u["rank_grads"], peer_shards=u["peer_shards"],
+                 full=torch.full_like(u["full"], float("nan"))) for u in units]
+
+
+HPS = {
+    "adamw": lambda: ss.AdamWHP(1e-3, 0.9, 0.999, 1e-8, 0.01, 3),
+    "adamax": lambda: ss.OptimHP.adamax(weight_decay=0.01, step=3),
+    "adadelta": lambda: ss.OptimHP.adadelta(weight_decay=0.01, step=3),
+    "sgd-momentum": lambda: ss.OptimHP.sgd(lr=1e-2, momentum=0.9, weight_decay=1e-4, step=3),
+    "sgd": lambda: ss.OptimHP.sgd(lr=1e-2, weight_decay=1e-4, step=3),
+}
+
+
+@pytest.mark.parametrize("world,gdt,fp32_reduce,cdt,opt", [
+    (2, torch.float16, True, torch.float16, "adamw"),
+    (2, torch.bfloat16, False, torch.bfloat16, "adamax"),
+    (2, torch.float16, True, torch.float32, "adadelta"),
+    (2, torch.float16, True, torch.float16, "sgd-momentum"),
+    (2, torch.float16, True, torch.float16, "sgd"),
+    (8, torch.bfloat16, False, torch.bfloat16, "adamw"),
+    (4, torch.float32, True, torch.float16, "adamw"),
+])
+def test_batched_split_gather_equals_fused(world, gdt, fp32_reduce, cdt, opt):
+    hp = HPS[opt]()
+    n_states = hp.n_states if isinstance(hp, ss.OptimHP) else 2
+    # three units, each under the threshold, together over it; ragged sizes
+    sizes = [(SPLIT_ELEMS // 2) + 8 * 37 + 5, (SPLIT_ELEMS // 3) + 1, (SPLIT_ELEMS // 4) + 512]
+    print("case", world, gdt, fp32_reduce, cdt, opt, sizes, flush=True)
+    assert all(not ss.unit_gather_split(torch.float32, n_states, S) for S in sizes)
+    split = ss.unit_gather_split(torch.float32, n_states, sum(sizes))
+    assert split == (n_states >= 1)
+    rank = world - 1
+    a = _units(world, rank, sizes, gdt, cdt, 7)
+    b = _clone(a)
+    ss.fsdp_step_units(a, rank, fp32_reduce, hp)                 # one launch table: split when n_states >= 1
+    for u in b:
+        ss.fsdp_step_units([u], rank, fp32_reduce, hp)           # one unit per call: the fused form
+    torch.cuda.synchronize()
+    for k, (ua, ub, S) in enumerate(zip(a, b, sizes)):
+        for key in ("master", "exp_avg", "exp_avg_sq", "full"):
+            if key == "exp_avg" and n_states < 1 or key == "exp_avg_sq" and n_states < 2:
+                continue
+            assert torch.equal(_bits(ua[key]), _bits(ub[key])), (k, key)
+        full = ua["full"]
+        own = ua["master"].to(cdt) if cdt != torch.float32 else ua["master"]
+        assert torch.equal(_bits(full[rank * S:(rank + 1) * S]), _bits(own)), k
+        for q in range(world):
+            if q != rank:
+                assert torch.equal(_bits(full[q * S:(q + 1) * S]), _bits(ua["peer_shards"][q])), (k, q)
+
+
+def test_split_gather_generic_world_one_unit_per_launch():
+    """World 3 takes the generic kernel, one unit per launch: a unit of 2^24
+    shard elements takes the split form and matches the two-call pipeline
+    (reduce-scatter + step without gather, then the all-gather)."""
+    world, S, rank = 3, SPLIT_ELEMS, 1
+    assert ss.unit_gather_split(torch.float32, 2, S)
+    hp = ss.AdamWHP(1e-3, 0.9, 0.999, 1e-8, 0.01, 2)
+    a = _units(world, rank, [S], torch.float16, torch.bfloat16, 11)
+    b = _clone(a)
+    ss.fsdp_step_units(a, rank, True, hp)
+    u = b[0]
+    comp = torch.empty(S, dtype=torch.bfloat16, device="cuda")
+    ss.fsdp_step_units([dict(master=u["master"], exp_avg=u["exp_avg"], exp_avg_sq=u["exp_avg_sq"],
+                             rank_grads=u["rank_grads"], compute_shard=comp)], rank, True, hp)
+    shards = [comp if q == rank else u["peer_shards"][q] for q in range(world)]
+    full = ss.fsdp_unshard_gather(shards)
+    torch.cuda.synchronize()
+    for key in ("master", "exp_avg", "exp_avg_sq"):
+        assert torch.equal(_bits(a[0][key]), _bits(u[key])), key
+    assert torch.equal(_bits(a[0]["full"]), _bits(full))
+    assert np_of(comp).size == S
