@@ -337,13 +337,23 @@ KERNEL_SOURCES = ("fsdp_kernels.hip", "fsdp_kernels.h", "fsdp_device.h", "fsdp_u
                   "fsdp_units_adamw.hip", "fsdp_units_sgd.hip", "fsdp_units_adamax.hip", "fsdp_units_adadelta.hip")
 
 
+def kernel_code(text):
+    """A device source with its comments and blank lines removed (the sources
+    hold no comment markers inside string literals)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash():
-    """sha256 over the device sources, so counter figures taken on another
-    version of the kernels are not reported."""
+    """sha256 over the device sources' code (comments excluded), so counter
+    figures taken on another version of the kernels are not reported."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, "sharded_state_amd", "csrc", f), "rb").read())
+        src = open(os.path.join(ROOT, "sharded_state_amd", "csrc", f), encoding="utf-8").read()
+        h.update(kernel_code(src).encode())
     return h.hexdigest()
 
 

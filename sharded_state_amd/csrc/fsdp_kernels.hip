@@ -3,7 +3,9 @@
 //
 // Design (MI355X, 256 CUs in 8 XCDs, 64-wide waves, HBM3E ~8 TB/s):
 //  * 16-byte (dwordx4) global loads/stores per lane; a lane owns 8 consecutive
-//    elements of the shard per step (one dwordx4 of 16-bit data, two of fp32);
+//    elements of the shard per step (one dwordx4 of 16-bit data, two of fp32),
+//    except in the unit kernel, whose group layout (load8g in fsdp_device.h)
+//    gives each wave access instruction one contiguous span;
 //  * grid-stride loops over a grid sized to a multiple of the CU count, so a
 //    launch is a few thousand workgroups regardless of the unit size;
 //  * the N simulated ranks' gradient blocks are accumulated in registers, all N
