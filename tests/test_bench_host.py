@@ -1,0 +1,83 @@
+"""bench.py's host logic (no GPU): the byte accounting against the closed forms
+of the algorithmic bytes per shard element, the counter-summary key, and the
+refusal of more than one GPU."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from workloads import CONFIGS  # noqa: E402
+
+
+def _canonical(cfg):
+    """Bytes per shard element when every buffer is touched once and each gather
+    reads and writes all N shards: N*g + 12 (read master, m, v) + 12 (write) +
+    c (own compute shard) + G * 2N*c."""
+    g = 4 if cfg.grad_dt == "f32" else 2
+    c = 4 if cfg.compute_dt == "f32" else 2
+    return cfg.world * g + 24 + c + cfg.gathers * 2 * cfg.world * c
+
+
+@pytest.mark.parametrize("name,expected", [("tiny", 52), ("gpt2-large-block", 38), ("gpt2-xl-model", 38),
+                                           ("gpt3-13b-block", 106), ("llama70b-block", 74)])
+def test_canonical_bytes_per_element(name, expected):
+    cfg = CONFIGS[name]
+    assert _canonical(cfg) == expected
+    # the three-launch pipeline moves exactly the canonical bytes
+    assert bench.sizes(cfg, "separate")[1] == expected
+
+
+@pytest.mark.parametrize("name", ["tiny", "gpt2-large-block", "gpt2-xl-model", "gpt3-13b-block", "llama70b-block"])
+@pytest.mark.parametrize("split", [False, True])
+def test_unit_step_bytes_skip_only_the_own_shard_copy(name, split):
+    """The unit step writes its own compute shard once, straight into its slot
+    of the full buffer, and the first gather never reads it back: with one
+    gather that is 2c bytes fewer than the canonical count (the reduced count
+    N*g + 24 + (2N-1)*c); with two gathers the step also writes the persistent
+    own copy the second gather reads, c fewer.  Nothing else differs, and the
+    timed kernel carries the peers' copies unless they run in their own launch."""
+    cfg = CONFIGS[name]
+    c = 4 if cfg.compute_dt == "f32" else 2
+    kernel, step = bench.sizes(cfg, "unit", "f32", 2, split)
+    assert step == _canonical(cfg) - (2 * c if cfg.gathers == 1 else c)
+    if cfg.gathers == 1:
+        assert step == cfg.world * (4 if cfg.grad_dt == "f32" else 2) + 24 + (2 * cfg.world - 1) * c
+    peers = 2 * (cfg.world - 1) * c
+    others = (cfg.gathers - 1) * 2 * cfg.world * c
+    assert kernel == step - others - (peers if split else 0)
+
+
+def test_state_buffers_change_only_the_state_bytes():
+    cfg = CONFIGS["gpt2-large-block"]
+    k2, s2 = bench.sizes(cfg, "unit", "f32", 2, True)
+    k1, s1 = bench.sizes(cfg, "unit", "f32", 1, True)
+    k0, s0 = bench.sizes(cfg, "unit", "f32", 0, False)
+    assert (k2 - k1, s2 - s1) == (8, 8)
+    assert s1 - s0 == 8
+    assert k0 == s0                      # SGD keeps the copies in its trip: the kernel is the whole step
+
+
+def test_sixteen_bit_state_bytes():
+    cfg = CONFIGS["llama70b-block"]      # N = 8, bf16 grads and compute
+    kernel, step = bench.sizes(cfg, "unit", "bf16")
+    assert kernel == step == 8 * 2 + 12 + 2 + 2 * 7 * 2
+
+
+def test_kernel_code_ignores_comments_only():
+    a = "int x; // one\n/* two\n three */ int y;\n\n"
+    b = "int x;\n int y; // other words\n"
+    assert bench.kernel_code(a) == "int x;\n int y;"
+    assert bench.kernel_code(a) == bench.kernel_code(b)
+    assert bench.kernel_code("int x;") != bench.kernel_code("int z;")
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one-GPU" in r.stderr and not r.stdout
