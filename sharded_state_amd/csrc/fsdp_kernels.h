@@ -21,6 +21,9 @@ constexpr int kBlocksPerCU = FSDP_BLOCKS_PER_CU;       // grid cap = CUs * kBloc
 // workload, same-process A/B); the copy and reduce kernels, with one or two
 // loads per lane, need full occupancy instead and reserve none.
 constexpr unsigned kUnitLdsBytes = 81920;
+// 3 per CU instead: measured faster for 16-bit state with N <= 2 (+1.5 to +3.7
+// points; with N = 8 it loses 3.7), so those instantiations reserve this.
+constexpr unsigned kUnitLdsBytes3 = 53248;
 constexpr int kSegMax = 64;             // segments per flatten/unflatten launch
 constexpr int64_t kSegChunkBytes = 32768;
 

@@ -153,12 +153,13 @@ __global__ __launch_bounds__(kThreads) void k_units(UnitBatch<NW> B, ReduceScala
 template <class OPT, int NW, int GF, bool FP32R, int CF, int SF>
 static hipError_t units_go(const UnitBatch<NW>& B, int64_t tiles, bool gather, const ReduceScalars& rs,
                            const OPT& op, hipStream_t st) {
+    constexpr unsigned lds = (SF != FSDP_F32 && NW >= 1 && NW <= 2) ? kUnitLdsBytes3 : kUnitLdsBytes;
     if (gather)
-        launch_lds(k_units<OPT, NW, GF, FP32R, CF, true, SF>, dim3((unsigned)tiles), dim3(kThreads), kUnitLdsBytes,
-                   st, B, rs, op);
+        launch_lds(k_units<OPT, NW, GF, FP32R, CF, true, SF>, dim3((unsigned)tiles), dim3(kThreads), lds, st, B, rs,
+                   op);
     else
-        launch_lds(k_units<OPT, NW, GF, FP32R, CF, false, SF>, dim3((unsigned)tiles), dim3(kThreads), kUnitLdsBytes,
-                   st, B, rs, op);
+        launch_lds(k_units<OPT, NW, GF, FP32R, CF, false, SF>, dim3((unsigned)tiles), dim3(kThreads), lds, st, B, rs,
+                   op);
     return hipGetLastError();
 }
 
