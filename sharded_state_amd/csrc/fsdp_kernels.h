@@ -25,7 +25,7 @@ constexpr unsigned kUnitLdsBytes = 81920;
 // points; with N = 8 it loses 3.7), so those instantiations reserve this.
 constexpr unsigned kUnitLdsBytes3 = 53248;
 constexpr int kSegMax = 64;             // segments per flatten/unflatten launch
-constexpr int64_t kSegChunkBytes = 32768;
+constexpr int64_t kSegChunkBytes = 8192;    // bytes per flatten/unflatten workgroup (8 KB: 6.0-6.5 TB/s; 32 KB 5.5-5.9, 4 KB 5.7-6.2)
 
 // Per-element AdamW constants, computed on the host (double, rounded once).
 struct AdamScalars {
