@@ -114,3 +114,21 @@ def test_split_gather_generic_world_one_unit_per_launch():
         assert torch.equal(_bits(a[0][key]), _bits(u[key])), key
     assert torch.equal(_bits(a[0]["full"]), _bits(full))
     assert np_of(comp).size == S
+
+
+def test_one_call_with_a_split_launch_and_a_fused_launch():
+    """45 units at N = 2 take two launches (40 + 5): the first holds 2^24+ shard
+    elements and splits, the second does not; every unit still matches its
+    one-unit (fused) step bit for bit."""
+    world, rank, S, n = 2, 0, 420_000, 45
+    assert ss.unit_gather_split(torch.float32, 2, 40 * S) and not ss.unit_gather_split(torch.float32, 2, 5 * S)
+    hp = ss.AdamWHP(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    a = _units(world, rank, [S + 8 * (k % 3) for k in range(n)], torch.float16, torch.float16, 21)
+    b = _clone(a)
+    ss.fsdp_step_units(a, rank, True, hp)
+    for u in b:
+        ss.fsdp_step_units([u], rank, True, hp)
+    torch.cuda.synchronize()
+    for k, (ua, ub) in enumerate(zip(a, b)):
+        for key in ("master", "exp_avg", "exp_avg_sq", "full"):
+            assert torch.equal(_bits(ua[key]), _bits(ub[key])), (k, key)
