@@ -147,8 +147,6 @@ __global__ __launch_bounds__(kThreads) void k_units(UnitBatch<NW> B, ReduceScala
     }
 }
 
-// Reduce-scatter alone: averaged gradient shard in fp32 (fp32 mode) or in the
-
 // ----------------------------------------------------------------- launchers
 template <class OPT, int NW, int GF, bool FP32R, int CF, int SF>
 static hipError_t units_go(const UnitBatch<NW>& B, int64_t tiles, bool gather, const ReduceScalars& rs,
