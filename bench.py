@@ -80,6 +80,9 @@ def parse():
                          "shard files in DIR (sharded-state checkpoint), reported beside the line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--cpu-all-cores-seconds", type=float, default=4.0,
+                    help="time budget of the oracle on every host core over disjoint chunks of the shard, "
+                         "reported beside the baseline (0 disables it)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="skip the per-launch HIP events (the roofline figure needs them)")
     ap.add_argument("--event-every", type=int, default=10,
@@ -209,33 +212,31 @@ def flatten_rate(cfg, ss, torch, N, lib, workloads, state="f32", reps=5):
             "tensors": len(cfg.numels), "launches": launches}
 
 
-def cpu_baseline(cfg, unit, budget_s, np_of_bytes, state="f32", ohp=None):
-    """The oracle, single-threaded on one host core, on rank 0's step of one
-    resident block, repeated until the budget is spent."""
+def cpu_baseline(cfg, unit, budget_s, np_of_bytes, state="f32", ohp=None, threads=1):
+    """The oracle on rank 0's step of one resident block, repeated until the
+    budget is spent: single-threaded on one host core over the block's first
+    4 Mi shard elements (threads == 1), or on `threads` Python threads over
+    disjoint chunks of the whole shard (the oracle's C calls run outside the
+    GIL)."""
     import numpy as np
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
     _, per_elt = sizes(cfg, "separate", state, ohp.n_states if ohp is not None else 2)
     S = unit.S
-    cap = min(S, 4 * 1024 * 1024)          # bounded sample: first `cap` shard elements
+    cap = min(S, 4 * 1024 * 1024) if threads == 1 else S    # bounded sample: the first `cap` shard elements
     # rank 0's block of each rank's gradient is its first S elements
     grads = [np_of_bytes(x[:cap]) for x in unit.grads]
     peers = [np_of_bytes(p[:cap]) for p in unit.peers]
     p0, m0, v0 = (np_of_bytes(t[:cap]) for t in (unit.master, unit.m, unit.v))
     h = oracle.hp(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.step)
-    try:
-        cores_before = os.sched_getaffinity(0)
-        os.sched_setaffinity(0, {sorted(cores_before)[0]})
-    except (AttributeError, OSError):
-        cores_before = None
-    elems = 0
-    t0 = time.perf_counter()
-    while True:
-        p, m, v = p0.copy(), m0.copy(), v0.copy()
-        avg = oracle.grad_average(grads, 0, cap, cfg.grad_dt, cfg.fp32_reduce)
+    opt = oracle_opt(oracle, ohp) if ohp is not None else None
+
+    def step(lo, n):
+        p, m, v = p0[lo:lo + n].copy(), m0[lo:lo + n].copy(), v0[lo:lo + n].copy()
+        avg = oracle.grad_average(grads, lo, n, cfg.grad_dt, cfg.fp32_reduce)
         g32 = avg if avg.dtype == np.float32 else oracle.to_f32(avg, cfg.grad_dt)
-        if ohp is not None:
-            kind, o = oracle_opt(oracle, ohp)
-            oracle.opt_step(kind, p, m, v, g32, o)
+        if opt is not None:
+            oracle.opt_step(opt[0], p, m, v, g32, opt[1])
             comp = oracle.cast(p, cfg.compute_dt)
         elif state == "f32":
             oracle.adamw(p, m, v, g32, h)
@@ -244,10 +245,31 @@ def cpu_baseline(cfg, unit, budget_s, np_of_bytes, state="f32", ohp=None):
             oracle.adamw16(p, m, v, g32, h, state)
             comp = p
         for _ in range(cfg.gathers):
-            oracle.gather([comp] + peers, cfg.compute_dt if state == "f32" else state)
-        elems += cap
-        if time.perf_counter() - t0 >= budget_s:
-            break
+            oracle.gather([comp] + [q[lo:lo + n] for q in peers], cfg.compute_dt if state == "f32" else state)
+
+    cores_before = None
+    if threads == 1:
+        try:
+            cores_before = os.sched_getaffinity(0)
+            os.sched_setaffinity(0, {sorted(cores_before)[0]})
+        except (AttributeError, OSError):
+            cores_before = None
+    t0 = time.perf_counter()
+
+    def worker(lo, n):
+        done = 0
+        while True:
+            step(lo, n)
+            done += n
+            if time.perf_counter() - t0 >= budget_s:
+                return done
+
+    if threads == 1:
+        elems = worker(0, cap)
+    else:
+        bounds = [cap * k // threads for k in range(threads + 1)]
+        with ThreadPoolExecutor(threads) as ex:
+            elems = sum(ex.map(worker, bounds[:-1], [b - a for a, b in zip(bounds[:-1], bounds[1:])]))
     dt = time.perf_counter() - t0
     if cores_before is not None:
         os.sched_setaffinity(0, cores_before)
@@ -259,11 +281,13 @@ def cpu_baseline(cfg, unit, budget_s, np_of_bytes, state="f32", ohp=None):
                 break
     except OSError:
         pass
+    what = ("the first %d shard elements" % cap) if threads == 1 else (
+        "all %d shard elements in %d disjoint chunks on %d threads" % (cap, threads, threads))
     return {
-        "value": round(elems * per_elt / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": "rank 0's step (reduce-scatter, %s, cast, %d gather) on the first %d shard "
-                  "elements of one %s block, repeated %d times in %.1f s; host %s (%s cpus)"
-                  % (ohp.name if ohp is not None else "AdamW", cfg.gathers, cap, cfg.name, elems // cap, dt,
+        "value": round(elems * per_elt / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": "rank 0's step (reduce-scatter, %s, cast, %d gather) on %s of one %s block, %.1f passes "
+                  "in %.1f s; host %s (%s cpus)"
+                  % (ohp.name if ohp is not None else "AdamW", cfg.gathers, what, cfg.name, elems / cap, dt,
                      model or platform.machine(), os.cpu_count()),
         "elements_per_s": round(elems / dt, 1),
     }
@@ -716,7 +740,7 @@ def main():
                 "median_launch_ms": round(statistics.median(durs), 5),
                 "min_launch_ms": round(min(durs), 5), "max_launch_ms": round(max(durs), 5)}
 
-    cpu = None
+    cpu = cpu_all = None
     if args.cpu_seconds > 0:
         def np_of_bytes(t):
             import numpy as np
@@ -725,6 +749,14 @@ def main():
                 return t.view(torch.int16).numpy().view(np.uint16)
             return t.numpy()
         cpu = cpu_baseline(cfg, pool[0], args.cpu_seconds, np_of_bytes, args.state, ohp)
+        if args.cpu_all_cores_seconds > 0:
+            try:
+                host_threads = len(os.sched_getaffinity(0))
+            except (AttributeError, OSError):
+                host_threads = os.cpu_count() or 1
+            if host_threads > 1:
+                cpu_all = cpu_baseline(cfg, pool[0], args.cpu_all_cores_seconds, np_of_bytes, args.state, ohp,
+                                       threads=host_threads)
 
     ckpt = None
     if args.checkpoint:
@@ -775,6 +807,7 @@ def main():
         "roofline": roof,
         "copy_ceiling": ceil,
         "cpu_baseline": cpu,
+        "cpu_all_cores": cpu_all,
         "checkpoint": ckpt,
     }
     print(json.dumps(out))

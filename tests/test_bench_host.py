@@ -81,3 +81,30 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one-GPU" in r.stderr and not r.stdout
+
+
+def test_cpu_baseline_single_core_and_all_cores():
+    """The oracle baseline runs on the host alone: one pinned core over the
+    first elements, or several threads over disjoint chunks of the shard."""
+    import types
+    import torch
+    cfg = CONFIGS["gpt2-large-block"]           # N = 2, fp16 grads reduced in fp32, fp16 compute
+    S = 8192
+    g = torch.Generator().manual_seed(0)
+    unit = types.SimpleNamespace(
+        S=S, grads=[(torch.randn(2 * S, generator=g) * 1e-3).half() for _ in range(2)],
+        peers=[torch.randn(S, generator=g).half()], master=torch.randn(S, generator=g) * 0.02,
+        m=torch.zeros(S), v=torch.zeros(S))
+
+    def np_of_bytes(t):
+        import numpy as np
+        if t.dtype == torch.float16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    one = bench.cpu_baseline(cfg, unit, 0.2, np_of_bytes)
+    many = bench.cpu_baseline(cfg, unit, 0.2, np_of_bytes, threads=4)
+    assert one["cores"] == 1 and many["cores"] == 4
+    for r in (one, many):
+        assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0 and r["elements_per_s"] > 0
+    assert "disjoint chunks on 4 threads" in many["sample"]
