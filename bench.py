@@ -623,8 +623,9 @@ def main():
     slots = [k % len(pool) for k in range(cfg.blocks)]
     groups = []
     if args.pipeline == "units":
-        kmax = {1: 40, 2: 40, 4: 24, 8: 16}.get(cfg.world, 1)
-        lim = min(kmax, len(pool))           # a unit appears at most once per launch
+        # one call per step launch, packed as the library packs (units_in_launch);
+        # a unit appears at most once per launch
+        lim = min(ss.units_in_launch(cfg.world, [S] * len(pool)), len(pool))
         nb = -(-len(slots) // lim)
         bounds = [round(j * len(slots) / nb) for j in range(nb + 1)]
         for j in range(nb):

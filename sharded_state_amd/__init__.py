@@ -21,6 +21,7 @@ from .api import (  # noqa: F401
     fsdp_unflatten_views,
     fsdp_unshard_gather,
     unit_gather_split,
+    units_in_launch,
     view_table,
 )
 from .state import RankState  # noqa: F401
@@ -38,5 +39,5 @@ __all__ = [
     "fsdp_reduce_scatter_local", "fsdp_sharded_adamw", "fsdp_step_unit", "fsdp_step_units", "prepare_step_units", "fsdp_unshard_gather",
     "fsdp_unflatten_views", "view_table", "RankState", "save_shard", "load_shard", "shard_info",
     "shard_path", "consolidate", "fsdp_host_adamw", "fsdp_offload_step", "fsdp_offload_step_units",
-    "prepare_offload_step_units", "OffloadState", "unit_gather_split",
+    "prepare_offload_step_units", "OffloadState", "unit_gather_split", "units_in_launch",
 ]

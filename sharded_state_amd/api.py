@@ -65,6 +65,15 @@ def unit_gather_split(state_dtype, n_states, shard_elements):
     return rc == 1
 
 
+def units_in_launch(world, shard_numels):
+    """How many of the units with these shard sizes, in order, the next step
+    launch of fsdp_step_units takes (0 for none)."""
+    rc = N.lib().fsdp_units_in_launch(int(world), i64_array(shard_numels), len(shard_numels))
+    if rc < 0:
+        check("fsdp_units_in_launch", rc)
+    return rc
+
+
 def fsdp_flatten_pad(tensors, world, flat=None, stream=None):
     """Flatten the unit's tensors into one buffer padded with +0 to a multiple of
     `world`.  Returns the flat buffer (allocated if `flat` is None)."""

@@ -227,7 +227,8 @@ static hipError_t peer_copies(const UnitBatch<NW>& B, int c, const UnitLaunch& L
     return launch_copies(cb, L.cus, L.stream);
 }
 
-// Pack the units into tables of at most kMax and launch one grid per table.
+// Pack the units into tables (units_in_launch: at most kMax units and
+// kLaunchShardElems shard elements) and launch one grid per table.
 template <class OPT, int NW>
 static hipError_t units_all(const UnitArgs* units, int n, const UnitLaunch& L, const OPT& op) {
     constexpr int kMax = UnitBatch<NW>::kMax;
@@ -238,8 +239,11 @@ static hipError_t units_all(const UnitArgs* units, int n, const UnitLaunch& L, c
         B.npeers = L.gather ? L.world - 1 : 0;
         int64_t tiles = 0;
         int c = 0;
+        int64_t packed = 0;
         for (; c < kMax && done + c < n; ++c) {
             const UnitArgs& a = units[done + c];
+            if (c > 0 && packed + a.S > kLaunchShardElems) break;   // as units_in_launch
+            packed += a.S;
             B.tile_begin[c] = tiles;
             const int64_t nvec = a.nvec & ~int64_t(63);   // whole groups; the rest joins the tail
             B.nvec[c] = nvec;

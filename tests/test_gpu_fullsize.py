@@ -155,8 +155,9 @@ def test_sharded_state_is_one_nth_of_unsharded_state():
 @pytest.mark.parametrize("name,per_launch", [("gpt2-large-block", 36), ("gpt3-13b-block", 4),
                                              ("llama70b-block", 2)])
 def test_full_size_batched_launch(name, per_launch):
-    """The benchmark's launch configuration: `per_launch` distinct full-size
-    units of rank 0 in one fsdp_step_units launch with the fused gather (and,
+    """The benchmark's call: `per_launch` distinct full-size units of rank 0 in
+    one fsdp_step_units call with the gather (packed into launches as the
+    library packs them; and,
     with two gathers per step, the persistent own shard).  Per unit: sampled
     master, m, v and own-slot values against the oracle; the peer slots equal
     the peer shards bit for bit."""
