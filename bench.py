@@ -625,7 +625,7 @@ def main():
     if args.pipeline == "units":
         # one call per step launch, packed as the library packs (units_in_launch);
         # a unit appears at most once per launch
-        lim = min(ss.units_in_launch(cfg.world, [S] * len(pool)), len(pool))
+        lim = min(ss.units_in_launch(cfg.world, [S] * len(pool))[0], len(pool))
         nb = -(-len(slots) // lim)
         bounds = [round(j * len(slots) / nb) for j in range(nb + 1)]
         for j in range(nb):
@@ -719,22 +719,27 @@ def main():
         durs = [evs.elapsed_ms(2 * k, 2 * k + 1) for k in range(nslot * len(ev_steps))]
         evs.close()
         avg_ms = statistics.fmean(durs)
-        units_per_launch = cfg.blocks / len(groups)
-        split = unit_pipe and ss.unit_gather_split(pool[0].master.dtype, n_states,
-                                                   S * max(n for _, n, _, _ in groups))
+        # the timed launch is the first of each call: the library's plan says how
+        # many units it takes and how many shard elements it covers (a unit above
+        # 2^26 elements is stepped in 2^26-element slices, a launch each)
+        plan_units, launch_elems = ss.units_in_launch(cfg.world, [S] * groups[0][1])
+        split = unit_pipe and ss.unit_gather_split(pool[0].master.dtype, n_states, launch_elems)
         fused_b, _ = sizes(cfg, "separate" if args.pipeline == "separate" else "unit", args.state, n_states,
                            split)
-        bytes_per_launch = fused_b * S * units_per_launch
+        bytes_per_launch = fused_b * launch_elems
+        per_launch = ("%d units per launch" % plan_units if launch_elems == plan_units * S else
+                      "one %d-element slice of a unit per launch" % launch_elems)
         achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
         tag = args.pipeline if args.optimizer == "adamw" else "%s-%s" % (args.pipeline, args.optimizer)
         traffic = traffic_from_profiles("%s_%s" % (tag, cfg.name), kernel_source_hash())
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": (("k_units<GATHER> (fused reduce-scatter + optimizer + cast + all-gather, %g units "
-                            "per launch)" if not split else
-                            "k_units (fused reduce-scatter + optimizer + cast + own-slot write, %g units per "
-                            "launch; the peers' slots follow in one batched copy launch)") % units_per_launch
-                           if unit_pipe else "k_units (fused reduce-scatter + optimizer + cast)"),
+                "kernel": (("k_units<GATHER> (fused reduce-scatter + optimizer + cast + all-gather, %s)"
+                            if not split else
+                            "k_units (fused reduce-scatter + optimizer + cast + own-slot write, %s; the peers' "
+                            "slots follow in one batched copy launch)") % per_launch
+                           if unit_pipe else "k_units (fused reduce-scatter + optimizer + cast, %s)" % per_launch),
+                "shard_elements_per_launch": int(launch_elems),
                 "peer_copies_in_own_launch": bool(split),
                 "bytes_per_launch": int(bytes_per_launch), "avg_launch_ms": round(avg_ms, 5),
                 "timed_launches": len(durs),

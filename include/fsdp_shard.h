@@ -51,7 +51,7 @@ extern "C" {
 
 #define FSDP_API __attribute__((visibility("default")))
 
-#define FSDP_ABI_VERSION 7
+#define FSDP_ABI_VERSION 8
 #define FSDP_MAX_WORLD 128
 
 typedef enum fsdp_dtype {
@@ -242,8 +242,8 @@ typedef struct fsdp_unit {
  * (compute_shard NULL), and with full_out the gather copies it.
  * Units are packed in order into launches of up to 40 (world <= 2), 24
  * (world 4) or 16 (world 8) units, other world sizes one unit per launch, and
- * at most 2^26 shard elements per launch (a larger unit takes a launch of its
- * own); fsdp_units_in_launch gives the count.  With
+ * at most 2^26 shard elements per launch (a larger unit is stepped in slices
+ * of 2^26 elements, a launch each); fsdp_units_in_launch gives the plan.  With
  * full_out, a launch copies the peers' shards of its units in its own trip, or,
  * where fsdp_unit_gather_split says so for its units' shard elements, is
  * followed by one launch that copies them (up to 128 copies).  No output
@@ -321,9 +321,14 @@ FSDP_API int fsdp_unit_gather_split(fsdp_dtype state_dt, int32_t n_states, int64
 /* Launch plan, continued (host only): how many of the units with shard sizes
  * shard_numels[0 .. n_units) the next step launch of fsdp_step_units /
  * fsdp_step_units_optim takes (at least 1 when n_units > 0; 0 when n_units is
- * 0).  FSDP_E_INVAL for world outside [1, FSDP_MAX_WORLD], n_units < 0, a NULL
- * array with n_units > 0 or a negative size. */
-FSDP_API int fsdp_units_in_launch(int32_t world, const int64_t* shard_numels, int32_t n_units);
+ * 0), and in *shard_elements_out (may be NULL) the shard elements that launch
+ * covers.  A launch covers at most 2^26 shard elements: units are packed up to
+ * that, and a larger unit is stepped in slices of 2^26 elements, a launch each
+ * (then the answer is 1 unit and 2^26 elements).  FSDP_E_INVAL for world outside
+ * [1, FSDP_MAX_WORLD], n_units < 0, a NULL array with n_units > 0 or a
+ * negative size. */
+FSDP_API int fsdp_units_in_launch(int32_t world, const int64_t* shard_numels, int32_t n_units,
+                                  int64_t* shard_elements_out);
 
 /* Per-tensor views of the full buffer.  [P3] "The FSDP Unit" (use_orig_params):
  * tensor k is full[off_k : off_k + numel_k]; the padding belongs to no view.

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libfsdp_shard.so")
 F32, F16, BF16 = 0, 1, 2
 OK, E_INVAL, E_DTYPE, E_SIZE, E_ALIAS, E_HIP, E_IO, E_FORMAT = 0, -1, -2, -3, -4, -5, -6, -7
 MAX_WORLD = 128
-ABI_VERSION = 7
+ABI_VERSION = 8
 OPT_ADAMW, OPT_SGD, OPT_ADAMAX, OPT_ADADELTA = 0, 1, 2, 3
 
 
@@ -136,7 +136,7 @@ def lib():
     L.fsdp_unit_gather_split.restype = ctypes.c_int
     L.fsdp_unit_gather_split.argtypes = [i32, i32, i64]
     L.fsdp_units_in_launch.restype = ctypes.c_int
-    L.fsdp_units_in_launch.argtypes = [i32, i64p, i32]
+    L.fsdp_units_in_launch.argtypes = [i32, i64p, i32, i64p]
     L.fsdp_layout.restype = ctypes.c_int
     L.fsdp_layout.argtypes = [i64p, i32, i32, i64p, i64p, i64p]
     L.fsdp_flatten_pad.restype = ctypes.c_int

@@ -66,12 +66,15 @@ def unit_gather_split(state_dtype, n_states, shard_elements):
 
 
 def units_in_launch(world, shard_numels):
-    """How many of the units with these shard sizes, in order, the next step
-    launch of fsdp_step_units takes (0 for none)."""
-    rc = N.lib().fsdp_units_in_launch(int(world), i64_array(shard_numels), len(shard_numels))
+    """(units, shard elements) of the next step launch of fsdp_step_units over
+    units with these shard sizes, in order: how many units it takes (0 for
+    none) and how many shard elements it covers (a unit above 2^26 elements is
+    stepped in 2^26-element slices, a launch each)."""
+    elems = ctypes.c_int64()
+    rc = N.lib().fsdp_units_in_launch(int(world), i64_array(shard_numels), len(shard_numels), ctypes.byref(elems))
     if rc < 0:
         check("fsdp_units_in_launch", rc)
-    return rc
+    return rc, elems.value
 
 
 def fsdp_flatten_pad(tensors, world, flat=None, stream=None):

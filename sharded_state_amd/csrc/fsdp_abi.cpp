@@ -338,14 +338,17 @@ int fsdp_unit_gather_split(fsdp_dtype state_dt, int32_t n_states, int64_t shard_
     return fsdp::split_gather(state_dt, n_states, shard_elements) ? 1 : 0;
 }
 
-int fsdp_units_in_launch(int32_t world, const int64_t* shard_numels, int32_t n_units) {
+int fsdp_units_in_launch(int32_t world, const int64_t* shard_numels, int32_t n_units, int64_t* shard_elements_out) {
     if (world < 1 || world > FSDP_MAX_WORLD || n_units < 0 || (n_units > 0 && !shard_numels))
         return fail(FSDP_E_INVAL, "fsdp_units_in_launch: world %d / n_units %d / shard_numels out of range", world,
                     n_units);
     for (int32_t k = 0; k < n_units; ++k)
         if (shard_numels[k] < 0) return fail(FSDP_E_INVAL, "fsdp_units_in_launch: shard_numels[%d] < 0", k);
+    int64_t elems = 0;
+    const int c = n_units == 0 ? 0 : fsdp::units_in_launch(world, shard_numels, n_units, &elems);
+    if (shard_elements_out) *shard_elements_out = elems;
     ok();
-    return n_units == 0 ? 0 : fsdp::units_in_launch(world, shard_numels, n_units);
+    return c;
 }
 
 int fsdp_time_next_launch(void* start_event, void* stop_event) {

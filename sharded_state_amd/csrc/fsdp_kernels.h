@@ -163,25 +163,35 @@ hipError_t launch_copies(const CopyBatch& b, int cus, void* stream);
 
 // Packing of a unit-step call into launches: up to UnitBatch<NW>::kMax units
 // (unit_table_max) and at most kLaunchShardElems shard elements in all per
-// launch (a larger unit takes a launch of its own).  The element cap was
+// launch; a larger unit is stepped in slices of kLaunchShardElems elements, a
+// launch each (launch_units).  The element cap was
 // measured faster than one launch per table on every shape (same box, two
 // repetitions, % of 8 TB/s: GPT-2 Large x36 75.3 -> 76.9 with AdamW, +1.4
 // Adamax, +1.3 SGD, +0.6 bf16 state; 13B +0.3; 70B +1.0); a cap of 2^25 gained
 // less, 5e7 about the same.
 constexpr int64_t kLaunchShardElems = int64_t(1) << 26;
+static_assert(kLaunchShardElems % 512 == 0, "slices keep whole groups");
+inline int64_t slices_of(int64_t S) { return (S + kLaunchShardElems - 1) / kLaunchShardElems; }
+inline int64_t dt_bytes(int dt) { return dt == FSDP_F32 ? 4 : 2; }
 inline int unit_table_max(int world) {
     return world == 1 || world == 2 ? UnitBatch<2>::kMax : world == 4 ? UnitBatch<4>::kMax
          : world == 8 ? UnitBatch<8>::kMax : UnitBatch<0>::kMax;
 }
-// Units (of shard sizes S[0..n)) the next launch takes: at least one.
-inline int units_in_launch(int world, const int64_t* S, int n) {
+// Units (of shard sizes S[0..n), n >= 1) the next launch takes, at least one,
+// and the shard elements it covers (the first slice of a unit larger than the cap).
+inline int units_in_launch(int world, const int64_t* S, int n, int64_t* elems) {
+    if (S[0] > kLaunchShardElems) {
+        *elems = kLaunchShardElems;
+        return 1;
+    }
     const int cap = unit_table_max(world);
     int64_t packed = 0;
     int c = 0;
     for (; c < cap && c < n; ++c) {
-        if (c > 0 && packed + S[c] > kLaunchShardElems) break;
+        if (S[c] > kLaunchShardElems || (c > 0 && packed + S[c] > kLaunchShardElems)) break;
         packed += S[c];
     }
+    *elems = packed;
     return c;
 }
 

@@ -26,6 +26,9 @@
 // "Mixed Precision and FSDP"; "fairseq 中的 Fully Sharded Data Parallel (FSDP)
 // 实战指南" (zskr.cn) -- flag table (--fp32-reduce-scatter) and "工作原理".
 
+#include <algorithm>
+#include <vector>
+
 #include "fsdp_device.h"
 
 #pragma clang fp contract(off)
@@ -138,7 +141,7 @@ void take_launch_events(hipEvent_t* start, hipEvent_t* stop) {
     t_ev_start = t_ev_stop = nullptr;
 }
 
-hipError_t launch_units(const UnitArgs* units, int n, const UnitLaunch& L) {
+static hipError_t launch_units_policy(const UnitArgs* units, int n, const UnitLaunch& L) {
     switch (L.opt.kind) {
     case kOptAdamW: return launch_units_adamw(units, n, L);
     case kOptSgd:
@@ -147,6 +150,61 @@ hipError_t launch_units(const UnitArgs* units, int n, const UnitLaunch& L) {
     case kOptAdadelta: return launch_units_adadelta(units, n, L);
     default: return hipErrorInvalidValue;
     }
+}
+
+// Units of more than kLaunchShardElems shard elements are stepped as slices
+// of that many (a multiple of 512, so every slice keeps 16-byte alignment and
+// whole groups): the step is pointwise, so a slice is a unit of its own whose
+// pointers start lo elements in.  Measured: GPT-2 XL (one 778.8M-element
+// shard) 75.2 -> 77.1% of 8 TB/s, 70B (106.9M) 77.7 -> 78.2% in 2^26-element
+// slices; 2^25-element slices gained less and lost on 13B.
+hipError_t launch_units(const UnitArgs* units, int n, const UnitLaunch& L) {
+    int64_t pieces = 0;
+    for (int k = 0; k < n; ++k) pieces += units[k].S > kLaunchShardElems ? slices_of(units[k].S) : 1;
+    if (pieces == n) return launch_units_policy(units, n, L);
+    const int64_t part = kLaunchShardElems;
+    const int64_t gs = dt_bytes(L.grad_dt), ss = dt_bytes(L.state_dt), cs = dt_bytes(L.compute_dt);
+    const int np = L.gather ? L.world - 1 : 0;
+    std::vector<UnitArgs> out;
+    std::vector<std::vector<const void*>> grads, srcs;   // per-slice pointer tables (stable: reserved)
+    std::vector<std::vector<void*>> dsts;
+    out.reserve(pieces);
+    grads.reserve(pieces);
+    srcs.reserve(pieces);
+    dsts.reserve(pieces);
+    for (int k = 0; k < n; ++k) {
+        const UnitArgs& a = units[k];
+        if (a.S <= part) {
+            out.push_back(a);
+            continue;
+        }
+        for (int64_t lo = 0; lo < a.S; lo += part) {
+            const int64_t cnt = a.S - lo < part ? a.S - lo : part;
+            UnitArgs b = a;
+            grads.emplace_back(L.world);
+            for (int q = 0; q < L.world; ++q) grads.back()[q] = (const char*)a.grads[q] + lo * gs;
+            b.grads = grads.back().data();
+            if (np > 0) {
+                srcs.emplace_back(np);
+                dsts.emplace_back(np);
+                for (int q = 0; q < np; ++q) {
+                    srcs.back()[q] = (const char*)a.peer_src[q] + lo * cs;
+                    dsts.back()[q] = (char*)a.peer_dst[q] + lo * cs;
+                }
+                b.peer_src = srcs.back().data();
+                b.peer_dst = dsts.back().data();
+            }
+            b.p = (char*)a.p + lo * ss;
+            b.m = a.m ? (char*)a.m + lo * ss : nullptr;
+            b.v = a.v ? (char*)a.v + lo * ss : nullptr;
+            b.out = a.out ? (char*)a.out + lo * cs : nullptr;
+            b.out2 = a.out2 ? (char*)a.out2 + lo * cs : nullptr;
+            b.S = cnt;
+            b.nvec = a.nvec > 0 ? std::min(a.nvec - lo / 8, cnt / 8) : 0;
+            out.push_back(b);
+        }
+    }
+    return launch_units_policy(out.data(), (int)out.size(), L);
 }
 
 template <int NW, int GF, bool FP32R>

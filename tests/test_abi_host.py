@@ -224,20 +224,21 @@ def test_unit_gather_split_launch_plan():
 
 def test_units_in_launch_packing():
     """Packing of a unit-step call: at most 40 / 24 / 16 units (N <= 2 / 4 / 8,
-    one unit otherwise) and at most 2^26 shard elements per launch, a larger
-    unit alone."""
+    one unit otherwise) and at most 2^26 shard elements per launch; a larger
+    unit is stepped in 2^26-element slices."""
     cap = 1 << 26
-    assert ss.units_in_launch(2, []) == 0
-    assert ss.units_in_launch(2, [100] * 50) == 40
-    assert ss.units_in_launch(1, [100] * 50) == 40
-    assert ss.units_in_launch(4, [100] * 50) == 24
-    assert ss.units_in_launch(8, [100] * 50) == 16
-    assert ss.units_in_launch(3, [100] * 50) == 1
-    assert ss.units_in_launch(2, [9_838_720] * 36) == 6          # GPT-2 Large block shards
-    assert ss.units_in_launch(8, [106_954_752] * 2) == 1         # 70B block shard: one per launch
-    assert ss.units_in_launch(2, [cap + 1, 1]) == 1              # a larger unit takes a launch alone
-    assert ss.units_in_launch(2, [cap - 10, 10, 1]) == 2         # exactly at the cap
-    assert ss.units_in_launch(2, [5, cap]) == 1
+    assert ss.units_in_launch(2, []) == (0, 0)
+    assert ss.units_in_launch(2, [100] * 50) == (40, 4000)
+    assert ss.units_in_launch(1, [100] * 50) == (40, 4000)
+    assert ss.units_in_launch(4, [100] * 50) == (24, 2400)
+    assert ss.units_in_launch(8, [100] * 50) == (16, 1600)
+    assert ss.units_in_launch(3, [100] * 50) == (1, 100)
+    assert ss.units_in_launch(2, [9_838_720] * 36) == (6, 6 * 9_838_720)     # GPT-2 Large block shards
+    assert ss.units_in_launch(8, [106_954_752] * 2) == (1, cap)             # 70B block shard: slices
+    assert ss.units_in_launch(2, [778_804_000]) == (1, cap)                 # GPT-2 XL model shard
+    assert ss.units_in_launch(2, [cap, 1]) == (1, cap)                      # exactly at the cap: alone
+    assert ss.units_in_launch(2, [cap - 10, 10, 1]) == (2, cap)
+    assert ss.units_in_launch(2, [5, cap + 1]) == (1, 5)                    # a larger unit is not packed
     for bad in ((0, [1]), (129, [1]), (2, [-1])):
         with pytest.raises(ss.FsdpError):
             ss.units_in_launch(*bad)

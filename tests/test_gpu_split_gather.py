@@ -132,3 +132,31 @@ def test_one_call_with_a_split_launch_and_a_fused_launch():
     for k, (ua, ub) in enumerate(zip(a, b)):
         for key in ("master", "exp_avg", "exp_avg_sq", "full"):
             assert torch.equal(_bits(ua[key]), _bits(ub[key])), (k, key)
+
+
+def test_unit_above_the_launch_cap_is_stepped_in_slices():
+    """A shard of 2^26 + 1003 elements is stepped as a 2^26-element slice and a
+    ragged remainder, each a launch (with its peers' copies); sampled outputs
+    around the slice boundary, at both ends and at random positions match the
+    oracle bit for bit, and the peers' slots are whole."""
+    import numpy as np
+    import oracle
+    from parity import assert_bitexact
+    world, rank = 2, 0
+    S = (1 << 26) + 1003
+    assert ss.units_in_launch(world, [S]) == (1, 1 << 26)
+    u = _units(world, rank, [S], torch.float16, torch.float16, 31)[0]
+    idx = np.unique(np.concatenate([np.arange(600), np.arange((1 << 26) - 600, (1 << 26) + 600),
+                                    np.arange(S - 600, S), np.random.default_rng(3).integers(0, S, 5000)]))
+    sel = torch.from_numpy(idx).cuda()
+    gs = [np_of(g[sel]) for g in u["rank_grads"]]          # rank 0's block is the first S elements
+    p, m, v = (np_of(u[k][sel]) for k in ("master", "exp_avg", "exp_avg_sq"))
+    h = oracle.hp(1e-3, 0.9, 0.999, 1e-8, 0.01, 2)
+    ss.fsdp_step_units([u], rank, True, ss.AdamWHP(1e-3, 0.9, 0.999, 1e-8, 0.01, 2))
+    torch.cuda.synchronize()
+    _, comp = oracle.elementwise_step(gs, p, m, v, h, "f16", True, "f16")
+    assert_bitexact(np_of(u["master"][sel]), p, "master")
+    assert_bitexact(np_of(u["exp_avg"][sel]), m, "exp_avg")
+    assert_bitexact(np_of(u["exp_avg_sq"][sel]), v, "exp_avg_sq")
+    assert_bitexact(np_of(u["full"][:S][sel]), comp, "own slot")
+    assert torch.equal(_bits(u["full"][S:]), _bits(u["peer_shards"][1]))
