@@ -160,3 +160,36 @@ def test_unit_above_the_launch_cap_is_stepped_in_slices():
     assert_bitexact(np_of(u["exp_avg_sq"][sel]), v, "exp_avg_sq")
     assert_bitexact(np_of(u["full"][:S][sel]), comp, "own slot")
     assert torch.equal(_bits(u["full"][S:]), _bits(u["peer_shards"][1]))
+
+
+def test_sixteen_bit_state_unit_above_the_launch_cap():
+    """The same slicing with bf16 parameter, m and v (the copies in the step's
+    trip): sampled outputs match the oracle's 16-bit AdamW bit for bit."""
+    import numpy as np
+    import oracle
+    from parity import assert_bitexact
+    world, rank = 2, 1
+    S = (1 << 26) + 517
+    g = torch.Generator(device="cuda")
+    g.manual_seed(41)
+    bf = torch.bfloat16
+    grads = [(torch.randn(world * S, device="cuda", generator=g) * 1e-3).half() for _ in range(world)]
+    u = dict(master=(torch.randn(S, device="cuda", generator=g) * 0.02).to(bf),
+             exp_avg=(torch.randn(S, device="cuda", generator=g) * 1e-3).to(bf),
+             exp_avg_sq=(torch.rand(S, device="cuda", generator=g) * 1e-6).to(bf), rank_grads=grads,
+             peer_shards=[(torch.randn(S, device="cuda", generator=g) * 0.02).to(bf), None],
+             full=torch.empty(world * S, dtype=bf, device="cuda"))
+    idx = np.unique(np.concatenate([np.arange(300), np.arange((1 << 26) - 300, (1 << 26) + 300),
+                                    np.arange(S - 300, S), np.random.default_rng(4).integers(0, S, 5000)]))
+    sel = torch.from_numpy(idx).cuda()
+    gs = [np_of(x[rank * S:(rank + 1) * S][sel]) for x in grads]
+    p, m, v = (np_of(u[k][sel]) for k in ("master", "exp_avg", "exp_avg_sq"))
+    ss.fsdp_step_units([u], rank, True, ss.AdamWHP(1e-3, 0.9, 0.999, 1e-8, 0.01, 3))
+    torch.cuda.synchronize()
+    avg = oracle.grad_average(gs, 0, idx.size, "f16", True)
+    oracle.adamw16(p, m, v, avg, oracle.hp(1e-3, 0.9, 0.999, 1e-8, 0.01, 3), "bf16")
+    assert_bitexact(np_of(u["master"][sel]), p, "parameter")
+    assert_bitexact(np_of(u["exp_avg"][sel]), m, "exp_avg")
+    assert_bitexact(np_of(u["exp_avg_sq"][sel]), v, "exp_avg_sq")
+    assert_bitexact(np_of(u["full"][rank * S:][sel]), p, "own slot")
+    assert torch.equal(_bits(u["full"][:S]), _bits(u["peer_shards"][0]))
