@@ -146,7 +146,8 @@ FSDP_API int fsdp_reduce_scatter_local(const void* const* rank_grads, int32_t wo
                                        void* grad_shard_out, void* stream);
 
 /* Sharded AdamW, fused with the reduce-scatter and the cast, one pass over the
- * shard.  [P4] "工作原理" and "限制与兼容性说明": each rank runs the pointwise
+ * shard (a shard above 2^26 elements in 2^26-element slices, a launch each;
+ * see fsdp_units_in_launch).  [P4] "工作原理" and "限制与兼容性说明": each rank runs the pointwise
  * optimizer on its own shard only (AdamW is among the supported pointwise
  * optimizers); [P5] "The Basic Protocol": W = W - lr * Adam(G_avg, m, v);
  * [P3] "Mixed Precision and FSDP": fp32 master with a 16-bit compute copy.
@@ -185,7 +186,8 @@ FSDP_API int fsdp_unshard_gather(const void* const* shards, int32_t world, int64
  * (the all-gather then moves only the peers' shards).  The peers' shards are
  * copied in the step's own trip (one launch), or, where fsdp_unit_gather_split
  * says so, by a second launch after the step (fsdp_time_next_launch times the
- * step).  Sources as for
+ * step); a shard above 2^26 elements is stepped in 2^26-element slices, each
+ * so.  Sources as for
  * those two calls; [TR] "From all-reduce to sharded parameters": after the
  * reduce-scatter each rank updates its own shard, and the full weights are
  * gathered from every rank's shard before the next compute.
