@@ -180,10 +180,12 @@ def fsdp_sharded_adamw(master, exp_avg, exp_avg_sq, rank_grads, rank, fp32_reduc
 
 def fsdp_step_unit(master, exp_avg, exp_avg_sq, rank_grads, rank, fp32_reduce, hp, peer_shards,
                    full, compute_shard=None, stream=None):
-    """One unit's step in one launch: fused reduce-scatter + AdamW + cast of rank
-    `rank`'s shard written into its slot of `full`, and the peers' compute
-    shards (peer_shards[q], q != rank; entry `rank` may be None) copied into
-    theirs.  compute_shard, if given, also receives this rank's compute copy."""
+    """One unit's step: fused reduce-scatter + AdamW + cast of rank `rank`'s
+    shard written into its slot of `full`, and the peers' compute shards
+    (peer_shards[q], q != rank; entry `rank` may be None) copied into theirs --
+    in the step's own launch or in a copy launch right after it, and for a
+    shard above 2^26 elements slice by slice (the library's launch plan).
+    compute_shard, if given, also receives this rank's compute copy."""
     for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
         _dev(t, name)
         if t.dtype != torch.float32:
