@@ -193,3 +193,39 @@ def test_sixteen_bit_state_unit_above_the_launch_cap():
     assert_bitexact(np_of(u["exp_avg_sq"][sel]), v, "exp_avg_sq")
     assert_bitexact(np_of(u["full"][rank * S:][sel]), p, "own slot")
     assert torch.equal(_bits(u["full"][:S]), _bits(u["peer_shards"][0]))
+
+
+@pytest.mark.parametrize("opt", ["sgd", "sgd-momentum"])
+def test_stateless_and_one_state_optimizers_above_the_launch_cap(opt):
+    """SGD without momentum keeps no state (exp_avg and exp_avg_sq are NULL) and
+    its copies in the step's trip; with momentum it keeps one buffer and splits
+    them out.  A shard above 2^26 elements is stepped in slices either way and
+    matches the oracle on sampled elements."""
+    import numpy as np
+    import oracle
+    from parity import assert_bitexact
+    world, rank = 2, 0
+    S = (1 << 26) + 77
+    momentum = 0.9 if opt == "sgd-momentum" else 0.0
+    hp = ss.OptimHP.sgd(lr=1e-2, momentum=momentum, weight_decay=1e-4, step=2)
+    u = _units(world, rank, [S], torch.float16, torch.float16, 51)[0]
+    if momentum == 0.0:
+        u["exp_avg"] = u["exp_avg_sq"] = None
+    else:
+        u["exp_avg_sq"] = None
+    idx = np.unique(np.concatenate([np.arange(200), np.arange((1 << 26) - 200, (1 << 26) + 77),
+                                    np.random.default_rng(5).integers(0, S, 3000)]))
+    sel = torch.from_numpy(idx).cuda()
+    gs = [np_of(g[sel]) for g in u["rank_grads"]]
+    p = np_of(u["master"][sel])
+    buf = np_of(u["exp_avg"][sel]) if momentum else np.zeros(idx.size, np.float32)
+    ss.fsdp_step_units([u], rank, True, hp)
+    torch.cuda.synchronize()
+    g32 = oracle.grad_average(gs, 0, idx.size, "f16", True)
+    o = oracle.opt("sgd", step=2, lr=1e-2, momentum=momentum, weight_decay=1e-4)
+    oracle.sgd(p, buf, g32, o)
+    assert_bitexact(np_of(u["master"][sel]), p, "master")
+    if momentum:
+        assert_bitexact(np_of(u["exp_avg"][sel]), buf, "momentum buffer")
+    assert_bitexact(np_of(u["full"][:S][sel]), oracle.cast(p, "f16"), "own slot")
+    assert torch.equal(_bits(u["full"][S:]), _bits(u["peer_shards"][1]))
