@@ -731,6 +731,8 @@ def main():
                       "one %d-element slice of a unit per launch" % launch_elems)
         achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
         tag = args.pipeline if args.optimizer == "adamw" else "%s-%s" % (args.pipeline, args.optimizer)
+        if args.state != "f32":
+            tag += "-state-" + args.state          # another kernel: counters of its own
         traffic = traffic_from_profiles("%s_%s" % (tag, cfg.name), kernel_source_hash())
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
