@@ -146,8 +146,7 @@ __device__ __forceinline__ void load8g(const void* __restrict__ base, int64_t vi
     }
 }
 
-// NT = false: plain (write-back) stores, for an output that is read again soon.
-template <int F, bool NT = true>
+template <int F>
 __device__ __forceinline__ void store8g(void* __restrict__ base, int64_t vi, const float (&x)[8]) {
     const int64_t g = vi >> 6, l = vi & 63;
     if constexpr (F == FSDP_F32) {
@@ -157,13 +156,8 @@ __device__ __forceinline__ void store8g(void* __restrict__ base, int64_t vi, con
         a.z = __float_as_uint(x[2]); a.w = __float_as_uint(x[3]);
         b.x = __float_as_uint(x[4]); b.y = __float_as_uint(x[5]);
         b.z = __float_as_uint(x[6]); b.w = __float_as_uint(x[7]);
-        if constexpr (NT) {
-            st16(q, a);
-            st16(q + 64, b);
-        } else {
-            q[0] = a;
-            q[64] = b;
-        }
+        st16(q, a);
+        st16(q + 64, b);
     } else {
         uint32_t w[4];
 #pragma unroll
@@ -172,13 +166,8 @@ __device__ __forceinline__ void store8g(void* __restrict__ base, int64_t vi, con
         u32x2 a, b;
         a.x = w[0]; a.y = w[1];
         b.x = w[2]; b.y = w[3];
-        if constexpr (NT) {
-            st8(q, a);
-            st8(q + 64, b);
-        } else {
-            q[0] = a;
-            q[64] = b;
-        }
+        st8(q, a);
+        st8(q + 64, b);
     }
 }
 

@@ -83,11 +83,10 @@ __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t 
     } else {
         if (out) store8g<CF>(out, vi, pp);
     }
-    // the persistent own copy is read again by the next all-gather of the unit
-    // (parameters resharded after the forward): plain stores leave it in the
-    // caches on its way out (13B block x40, two gathers: +1.2 points of the
-    // whole step, same box, two repetitions)
-    if (out2) store8g<CF, false>(out2, vi, pp);
+    // non-temporal like every other output: plain stores, which keep this
+    // persistent copy in the caches, win only when the next all-gather follows
+    // the step at once and lose when it comes after other units' work
+    if (out2) store8g<CF>(out2, vi, pp);
 }
 
 // Element i of unit u, one lane (the tail past the last full vector, or every
