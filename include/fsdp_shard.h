@@ -152,8 +152,10 @@ FSDP_API int fsdp_reduce_scatter_local(const void* const* rank_grads, int32_t wo
  * optimizers); [P5] "The Basic Protocol": W = W - lr * Adam(G_avg, m, v);
  * [P3] "Mixed Precision and FSDP": fp32 master with a 16-bit compute copy.
  * The gradient of element i is the reduce-scatter average defined above,
- * converted to fp32.  Passing world = 1, rank = 0 and rank_grads = {g} steps
- * with an already reduced gradient shard g of dtype grad_dt.
+ * converted to fp32.  Passing world = 1, rank = 0 and rank_grads = {g} is the
+ * unfused form: AdamW + cast over an already reduced gradient shard g of
+ * dtype grad_dt (for instance the output of fsdp_reduce_scatter_local; a
+ * 16-bit g is taken as the 16-bit average, an fp32 g as the fp32 average).
  * Update (the published AdamW; t = hp->step; host scalars computed in double
  * and rounded once to fp32: decay = 1 - lr*wd, step_size = lr / (1 - beta1^t),
  * bc2 = sqrt(1 - beta2^t)):
@@ -162,7 +164,9 @@ FSDP_API int fsdp_reduce_scatter_local(const void* const* rank_grads, int32_t wo
  *   master = p2, exp_avg = m1, exp_avg_sq = v1, compute_shard = round(p2)
  *   master, exp_avg, exp_avg_sq  device fp32, shard_numel each, updated in place
  *   compute_shard                device, shard_numel of compute_dt, or NULL (no cast)
- *   hp                           host; hp->step >= 1 */
+ *   hp                           host; hp->step >= 1, betas in [0, 1), lr,
+ *                                weight_decay and eps >= 0 (FSDP_E_INVAL otherwise;
+ *                                every AdamW entry point checks the same) */
 FSDP_API int fsdp_sharded_adamw(float* master, float* exp_avg, float* exp_avg_sq,
                                 const void* const* rank_grads, int32_t world, int32_t rank,
                                 fsdp_dtype grad_dt, int32_t fp32_reduce,

@@ -67,6 +67,9 @@ int check_hp(const char* fn, const fsdp_adamw_hp* hp) {
     if (hp->step < 1) return fail(FSDP_E_INVAL, "%s: hp->step = %lld < 1", fn, (long long)hp->step);
     if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
         return fail(FSDP_E_INVAL, "%s: betas must lie in [0, 1)", fn);
+    // the same ranges as fsdp_step_units_optim's AdamW; NaN fails every comparison
+    if (!(hp->lr >= 0.0f) || !(hp->weight_decay >= 0.0f) || !(hp->eps >= 0.0f))
+        return fail(FSDP_E_INVAL, "%s: lr, weight_decay and eps must be >= 0", fn);
     return FSDP_OK;
 }
 

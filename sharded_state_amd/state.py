@@ -5,8 +5,8 @@ every persistent class -- fp32 master weights, AdamW's m and v, the compute
 copy and the reduce-scattered gradient -- so each class takes 1/N of the
 unsharded unit plus the tail padding ("FSDP (Fully Sharded Data Parallel)",
 section "The Sharding Scheme"; "Data Parallelism", section "ZeRO Stages").
-This class allocates those buffers (device memory through torch) and fills the
-master shard from a flat buffer; the pipeline itself runs in libfsdp_shard.so.
+This class allocates those buffers (device memory through torch); the pipeline
+itself runs in libfsdp_shard.so.
 """
 import torch
 
@@ -36,14 +36,6 @@ class RankState:
         self.compute = torch.empty(S, dtype=compute_dtype, device=device)
         self.grad_shard = (torch.empty(S, dtype=grad_shard_dtype, device=device)
                            if grad_shard_dtype is not None else None)
-
-    def load_master(self, flat):
-        """Copy this rank's block of the padded flat fp32 buffer into master."""
-        S = self.shard_numel
-        if flat.numel() != self.padded_numel or flat.dtype != torch.float32:
-            raise ValueError("flat must be the padded fp32 unit (%d elements)" % self.padded_numel)
-        self.master.copy_(flat[self.rank * S:(self.rank + 1) * S])
-        return self
 
     def nbytes(self):
         """Bytes per persistent class: {"optimizer", "compute", "grad"}."""

@@ -242,3 +242,47 @@ def test_units_in_launch_packing():
     for bad in ((0, [1]), (129, [1]), (2, [-1])):
         with pytest.raises(ss.FsdpError):
             ss.units_in_launch(*bad)
+
+
+@pytest.mark.parametrize("field,value", [("lr", -1e-3), ("weight_decay", -0.01), ("eps", -1e-8),
+                                         ("lr", float("nan")), ("eps", float("nan")),
+                                         ("weight_decay", float("nan"))])
+def test_every_adamw_entry_point_checks_the_same_hyper_parameters(field, value):
+    """lr, weight_decay and eps below 0 (or NaN) are FSDP_E_INVAL at every AdamW
+    entry point, as fsdp_step_units_optim already refused them: a negative eps
+    could make sqrt(v)/bc2 + eps vanish and turn the update into inf/NaN."""
+    L = N.lib()
+    hp = N.AdamWHP()
+    setattr(hp, field, value)
+    hpr = ctypes.byref(hp)
+    a, b, c = FAKE, FAKE + (1 << 30), FAKE + (2 << 30)
+    g = N.ptr_array([FAKE + (3 << 30), FAKE + (4 << 30)])
+    peers = N.ptr_array([0, FAKE + (5 << 30)])
+    full = ctypes.c_void_p(FAKE + (6 << 30))
+    vp = ctypes.c_void_p
+    table = (N.Unit * 1)(N.Unit(a, b, c, g, peers, FAKE + (6 << 30), None, 1000))
+    host = [np.zeros(16, np.float32) for _ in range(5)]
+    hptr = [vp(x.ctypes.data) for x in host]
+    ou = (N.OffloadUnit * 1)(N.OffloadUnit(hptr[0].value, hptr[1].value, hptr[2].value, g, FAKE + (7 << 30),
+                                           hptr[3].value, hptr[4].value, FAKE + (8 << 30), 16))
+    o = N.OptimHP.adamw()
+    setattr(o, field, value)
+    calls = {
+        "fsdp_sharded_adamw": lambda: L.fsdp_sharded_adamw(vp(a), vp(b), vp(c), g, 2, 0, N.BF16, 0, vp(FAKE + (9 << 30)),
+                                                           N.BF16, 1000, hpr, None),
+        "fsdp_step_unit": lambda: L.fsdp_step_unit(vp(a), vp(b), vp(c), g, 2, 0, N.BF16, 0, peers, full, N.BF16, 1000,
+                                                   None, hpr, None),
+        "fsdp_step_units": lambda: L.fsdp_step_units(table, 1, 2, 0, N.BF16, 0, N.F32, N.BF16, hpr, None),
+        "fsdp_step_units_optim": lambda: L.fsdp_step_units_optim(table, 1, 2, 0, N.BF16, 0, N.F32, N.BF16,
+                                                                 ctypes.byref(o), None),
+        "fsdp_host_adamw": lambda: L.fsdp_host_adamw(hptr[0], hptr[1], hptr[2], hptr[3], N.F32, hptr[4], N.F32, 16,
+                                                     hpr, 1),
+        "fsdp_offload_step": lambda: L.fsdp_offload_step(hptr[0], hptr[1], hptr[2], g, 2, 0, N.BF16, 0,
+                                                         vp(FAKE + (7 << 30)), hptr[3], hptr[4], vp(FAKE + (8 << 30)),
+                                                         N.BF16, 16, 0, hpr, 1, None, None),
+        "fsdp_offload_step_units": lambda: L.fsdp_offload_step_units(ou, 1, 2, 0, N.BF16, 0, N.BF16, 0, hpr, 1, None,
+                                                                     None),
+    }
+    for name, call in calls.items():
+        assert call() == N.E_INVAL, name
+        assert ">= 0" in L.fsdp_last_error().decode(), name
