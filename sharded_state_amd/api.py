@@ -240,24 +240,53 @@ def fsdp_step_units(units, rank, fp32_reduce, hp, stream=None):
     length of rank_grads), rank, dtypes and hp.  hp is an AdamWHP (AdamW,
     fsdp_step_units) or an OptimHP (any pointwise optimizer,
     fsdp_step_units_optim; state buffers it does not keep may be None).
-    Returns the prepared call
-    (callable with no arguments) after running it once, so a training loop can
-    re-issue it without marshalling again."""
+    Returns the prepared call after running it once, so a training loop can
+    re-issue it without marshalling again: call(step=t) takes step t, and
+    call.hp holds the hyper-parameters it reads (see prepare_step_units)."""
     call = prepare_step_units(units, rank, fp32_reduce, hp, stream)
     call()
     return call
 
 
+def _own_hp(hp):
+    """A private copy of the hyper-parameters (AdamWHP, OptimHP or an AdamWHP
+    keyword dict) that a prepared call reads at every issue."""
+    if isinstance(hp, (AdamWHP, OptimHP)):
+        return type(hp).from_buffer_copy(hp)
+    return AdamWHP(**hp)
+
+
+def _reissue(fn, name, args, hp, stream, device):
+    """The callable of a prepared call: call(step=None, stream=None) sets the
+    step being taken (t >= 1) in its own hyper-parameters (call.hp) and issues
+    the call on `stream`, else on the stream given when it was prepared, else
+    on the device's current stream at the time of the call."""
+    args = list(args)
+    bound = _stream(stream, device) if stream is not None else None
+
+    def call(step=None, stream=None):
+        if step is not None:
+            if int(step) < 1:
+                raise ValueError("step must be >= 1, got %d" % int(step))
+            hp.step = int(step)
+        args[-1] = _stream(stream, device) if stream is not None else (bound or _stream(None, device))
+        with torch.cuda.device(device):
+            check(name, fn(*args))
+
+    call.hp = hp
+    return call
+
+
 def prepare_step_units(units, rank, fp32_reduce, hp, stream=None):
-    """Marshal a fsdp_step_units call once; the returned callable issues it.
-    The state dtype is the dtype of the units' master tensors: float32 (fp32
+    """Marshal a fsdp_step_units call once; the returned callable issues it
+    (call(step=t) for step t, call(stream=s) on stream s; see _reissue).  The
+    state dtype is the dtype of the units' master tensors: float32 (fp32
     master, m, v) or bfloat16 / float16 (16-bit parameter, m, v; the parameter
     shard is the compute shard, so no compute_shard is given)."""
     if not units:
         raise ValueError("units is empty")
     optim = isinstance(hp, OptimHP)
-    if not optim and not isinstance(hp, AdamWHP):
-        hp = AdamWHP(**hp)
+    hp = _own_hp(hp)
     n_states = hp.n_states if optim else 2
     world = len(units[0]["rank_grads"])
     gather = units[0].get("full") is not None
@@ -336,14 +365,9 @@ def prepare_step_units(units, rank, fp32_reduce, hp, stream=None):
                         cs.data_ptr() if cs is not None else None, S)
     _same_device(tensors)
     args = (table, len(units), world, int(rank), dtype_code(gdt), int(bool(fp32_reduce)), dtype_code(sdt),
-            dtype_code(cdt or torch.float32), ctypes.byref(hp), _stream(stream, device))
+            dtype_code(cdt or torch.float32), ctypes.byref(hp), None)
     name = "fsdp_step_units_optim" if optim else "fsdp_step_units"
-    fn = getattr(N.lib(), name)
-
-    def call():
-        with torch.cuda.device(device):
-            check(name, fn(*args))
-
+    call = _reissue(getattr(N.lib(), name), name, args, hp, stream, device)
     call.keep = (keep, table, hp, tensors)   # the C side reads these host arrays at every call
     return call
 

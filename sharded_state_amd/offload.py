@@ -15,7 +15,7 @@ import torch
 
 from . import _native as N
 from ._native import AdamWHP, check
-from .api import _dev, _grads, _same_device, _stream, dtype_code
+from .api import _dev, _grads, _own_hp, _reissue, _same_device, _stream, dtype_code
 
 # Worker threads of the host update: the host's cores, at most 16.
 DEFAULT_THREADS = max(1, min(16, os.cpu_count() or 1))
@@ -120,9 +120,12 @@ def fsdp_offload_step(master, exp_avg, exp_avg_sq, rank_grads, rank, fp32_reduce
 
 def prepare_offload_step_units(units, rank, fp32_reduce, hp, chunk_numel=0, n_threads=None, stream=None,
                                copy_stream=None):
-    """Marshal a batch once; returns a no-argument callable that runs
-    fsdp_offload_step_units on it.  units: (OffloadState, rank_grads,
-    compute_dev) triples, each state at most once."""
+    """Marshal a batch once; returns a callable that runs
+    fsdp_offload_step_units on it: call(step=t) takes step t, call(stream=s)
+    runs on stream s (default: the stream given here, else the current
+    stream at the time of the call); call.hp holds the hyper-parameters it
+    reads.  units: (OffloadState, rank_grads, compute_dev) triples, each state
+    at most once."""
     if not units:
         raise ValueError("units is empty")
     table = (N.OffloadUnit * len(units))()
@@ -138,16 +141,17 @@ def prepare_offload_step_units(units, rank, fp32_reduce, hp, chunk_numel=0, n_th
         table[k] = u
         keep.append((gptr, st, list(grads), cdev))    # the C side reads these at every call
     world, gdt, cdt, fp32, device = meta
-    hp = _hp(hp)
+    hp = _own_hp(_hp(hp))
     L = N.lib()
+    cst = _cstream(copy_stream)
     args = (table, len(units), world, int(rank), dtype_code(gdt), int(bool(fp32)), dtype_code(cdt),
-            int(chunk_numel), ctypes.byref(hp), int(n_threads or DEFAULT_THREADS), _stream(stream, device),
-            _cstream(copy_stream))
+            int(chunk_numel), ctypes.byref(hp), int(n_threads or DEFAULT_THREADS), None, cst)
 
-    def call():
-        check("fsdp_offload_step_units", L.fsdp_offload_step_units(*args))
+    def fn(*a):   # a ends with the stream; the copy stream follows it
+        return L.fsdp_offload_step_units(*a, cst)
 
-    call.keep = (keep, table, hp)
+    call = _reissue(fn, "fsdp_offload_step_units", args[:-1], hp, stream, device)
+    call.keep = (keep, table, hp, copy_stream)
     return call
 
 
