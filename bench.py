@@ -38,6 +38,21 @@ compute element sizes:
 A unit pool of distinct blocks larger than the 256 MB Infinity Cache is cycled
 over the slots so every step streams HBM.
 
+Workloads (--workload): the five FSDP units of the workload table, or "all"
+(the default): every one of them in this process, in the order tiny,
+gpt2-large-block, gpt2-xl-model, gpt3-13b-block, llama70b-block, each with its
+own roofline and CPU-oracle baseline under "configs"; the line's own fields
+(value, config, roofline, cpu_baseline) are those of the largest workload that
+one GPU holds, the 70B-shaped block x96 (HEADLINE).
+
+CPU baseline: the oracle (single-threaded C) on rank 0's step of the same
+units, pinned to one host core, timed over whole units -- every distinct unit
+of the workload's pool once per pass, host copies of the inputs made before
+the timer, state updated in place -- and reported in GB/s on the same bytes
+per shard element as the GPU line.  Where the pool is smaller than the step
+(the 13B and 70B workloads cycle K = 4 and K = 2 distinct blocks over 40 and
+96 slots) the per-step time is the pool's extrapolated to the step, and says so.
+
 Prints one JSON line.  --gpus above 1 exits: this measures one GPU.
 """
 import argparse
@@ -51,6 +66,8 @@ import time
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "GB/s and % HBM peak for fused reduce-scatter+AdamW+unshard per FSDP unit"
+ORDER = ["tiny", "gpt2-large-block", "gpt2-xl-model", "gpt3-13b-block", "llama70b-block"]
+HEADLINE = "llama70b-block"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -59,8 +76,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gpt2-large-block",
-                    help="gpt2-large-block (default), gpt2-xl-model, gpt3-13b-block, llama70b-block, tiny")
+    ap.add_argument("--workload", default="all", choices=["all"] + ORDER,
+                    help="all (default: every workload, the 70B-shaped block x96 as the line's headline), or one "
+                         "of " + ", ".join(ORDER))
     ap.add_argument("--pipeline", choices=["units", "unit", "separate", "offload"], default="units")
     ap.add_argument("--offload-threads", type=int, default=16,
                     help="host threads of the offloaded AdamW (--pipeline offload)")
@@ -78,10 +96,11 @@ def parse():
     ap.add_argument("--checkpoint", default=None, metavar="DIR",
                     help="also time saving and loading rank 0's shard state of every resident unit as "
                          "shard files in DIR (sharded-state checkpoint), reported beside the line")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="CPU time budget of the oracle baseline sample (0 disables it)")
-    ap.add_argument("--cpu-all-cores-seconds", type=float, default=4.0,
-                    help="time budget of the oracle on every host core over disjoint chunks of the shard, "
+    ap.add_argument("--cpu-seconds", type=float, default=2.0,
+                    help="the one-core oracle baseline repeats whole passes over the workload's distinct units "
+                         "until at least this long (one pass of the large workloads takes 7-20 s; 0 disables it)")
+    ap.add_argument("--cpu-all-cores-seconds", type=float, default=1.0,
+                    help="the same for the oracle on every host core over disjoint chunks of each unit, "
                          "reported beside the baseline (0 disables it)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="skip the per-launch HIP events (the roofline figure needs them)")
@@ -212,29 +231,49 @@ def flatten_rate(cfg, ss, torch, N, lib, workloads, state="f32", reps=5):
             "tensors": len(cfg.numels), "launches": launches}
 
 
-def cpu_baseline(cfg, unit, budget_s, np_of_bytes, state="f32", ohp=None, threads=1):
-    """The oracle on rank 0's step of one resident block, repeated until the
-    budget is spent: single-threaded on one host core over the block's first
-    4 Mi shard elements (threads == 1), or on `threads` Python threads over
-    disjoint chunks of the whole shard (the oracle's C calls run outside the
-    GIL)."""
+def cpu_host_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.machine()
+
+
+class HostUnit:
+    """Host copies of rank 0's inputs of one unit, made before any timing:
+    block 0 of each rank's gradient, the parameter/state shards (updated in
+    place by the oracle) and the peers' compute shards."""
+
+    def __init__(self, unit, np_of_bytes):
+        S = unit.S
+        self.S = S
+        self.grads = [np_of_bytes(x[:S]).copy() for x in unit.grads]
+        self.peers = [np_of_bytes(q).copy() for q in unit.peers]
+        self.p, self.m, self.v = (np_of_bytes(t).copy() for t in (unit.master, unit.m, unit.v))
+
+
+def cpu_baseline(cfg, hosts, per_elt, state="f32", ohp=None, threads=1, min_seconds=0.0, blocks=None):
+    """The oracle on rank 0's step of every unit in `hosts` (HostUnit), in
+    unit order: reduce-scatter, the optimizer step in place, cast, and the
+    workload's G gathers.  One pass covers every unit once; passes repeat until
+    `min_seconds` (at least one).  threads == 1: on one pinned host core;
+    otherwise on `threads` Python threads over disjoint chunks of each unit
+    (the oracle's C calls run outside the GIL).  GB/s counts `per_elt` bytes per
+    shard element, the GPU line's count.  With `blocks` (> len(hosts)) slots
+    per step, the per-step time is the pass time scaled to the step."""
     import numpy as np
     import oracle
     from concurrent.futures import ThreadPoolExecutor
-    _, per_elt = sizes(cfg, "separate", state, ohp.n_states if ohp is not None else 2)
-    S = unit.S
-    cap = min(S, 4 * 1024 * 1024) if threads == 1 else S    # bounded sample: the first `cap` shard elements
-    # rank 0's block of each rank's gradient is its first S elements
-    grads = [np_of_bytes(x[:cap]) for x in unit.grads]
-    peers = [np_of_bytes(p[:cap]) for p in unit.peers]
-    p0, m0, v0 = (np_of_bytes(t[:cap]) for t in (unit.master, unit.m, unit.v))
     h = oracle.hp(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.step)
     opt = oracle_opt(oracle, ohp) if ohp is not None else None
+    cdt = cfg.compute_dt if state == "f32" else state
 
-    def step(lo, n):
-        p, m, v = p0[lo:lo + n].copy(), m0[lo:lo + n].copy(), v0[lo:lo + n].copy()
-        avg = oracle.grad_average(grads, lo, n, cfg.grad_dt, cfg.fp32_reduce)
+    def step(u, lo, n):
+        avg = oracle.grad_average(u.grads, lo, n, cfg.grad_dt, cfg.fp32_reduce)
         g32 = avg if avg.dtype == np.float32 else oracle.to_f32(avg, cfg.grad_dt)
+        p, m, v = u.p[lo:lo + n], u.m[lo:lo + n], u.v[lo:lo + n]
         if opt is not None:
             oracle.opt_step(opt[0], p, m, v, g32, opt[1])
             comp = oracle.cast(p, cfg.compute_dt)
@@ -245,8 +284,14 @@ def cpu_baseline(cfg, unit, budget_s, np_of_bytes, state="f32", ohp=None, thread
             oracle.adamw16(p, m, v, g32, h, state)
             comp = p
         for _ in range(cfg.gathers):
-            oracle.gather([comp] + [q[lo:lo + n] for q in peers], cfg.compute_dt if state == "f32" else state)
+            oracle.gather([comp] + [q[lo:lo + n] for q in u.peers], cdt)
 
+    items = []
+    for u in hosts:
+        parts = threads if threads > 1 else 1
+        bounds = [u.S * k // parts for k in range(parts + 1)]
+        items += [(u, a, b - a) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+    elems_per_pass = sum(u.S for u in hosts)
     cores_before = None
     if threads == 1:
         try:
@@ -254,42 +299,49 @@ def cpu_baseline(cfg, unit, budget_s, np_of_bytes, state="f32", ohp=None, thread
             os.sched_setaffinity(0, {sorted(cores_before)[0]})
         except (AttributeError, OSError):
             cores_before = None
-    t0 = time.perf_counter()
-
-    def worker(lo, n):
-        done = 0
-        while True:
-            step(lo, n)
-            done += n
-            if time.perf_counter() - t0 >= budget_s:
-                return done
-
-    if threads == 1:
-        elems = worker(0, cap)
-    else:
-        bounds = [cap * k // threads for k in range(threads + 1)]
-        with ThreadPoolExecutor(threads) as ex:
-            elems = sum(ex.map(worker, bounds[:-1], [b - a for a, b in zip(bounds[:-1], bounds[1:])]))
-    dt = time.perf_counter() - t0
-    if cores_before is not None:
-        os.sched_setaffinity(0, cores_before)
-    model = ""
+    passes = 0
+    ex = ThreadPoolExecutor(threads) if threads > 1 else None
     try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
+        t0 = time.perf_counter()
+        while True:
+            if ex is None:
+                for it in items:
+                    step(*it)
+            else:
+                list(ex.map(lambda it: step(*it), items))
+            passes += 1
+            if time.perf_counter() - t0 >= min_seconds:
                 break
-    except OSError:
-        pass
-    what = ("the first %d shard elements" % cap) if threads == 1 else (
-        "all %d shard elements in %d disjoint chunks on %d threads" % (cap, threads, threads))
+        dt = time.perf_counter() - t0
+    finally:
+        if ex is not None:
+            ex.shutdown()
+        if cores_before is not None:
+            os.sched_setaffinity(0, cores_before)
+    eps = passes * elems_per_pass / dt
+    pass_s = dt / passes
+    opt_name = ohp.name if ohp is not None else ("AdamW" if state == "f32" else "AdamW on %s state" % state)
+    where = ("one pinned core" if threads == 1 else
+             "%d threads over %d disjoint chunks of each unit" % (threads, threads))
+    extrap = blocks is not None and blocks > len(hosts)
+    if extrap:
+        what = ("the K = %d distinct blocks of the pool (%d shard elements), extrapolated from K = %d to the "
+                "%d-block step" % (len(hosts), elems_per_pass, len(hosts), blocks))
+        step_s = pass_s * blocks / len(hosts)
+    else:
+        what = ("whole units: all %d block%s of the step (%d shard elements)"
+                % (len(hosts), "s" if len(hosts) > 1 else "", elems_per_pass))
+        step_s = pass_s
     return {
-        "value": round(elems * per_elt / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-        "sample": "rank 0's step (reduce-scatter, %s, cast, %d gather) on %s of one %s block, %.1f passes "
-                  "in %.1f s; host %s (%s cpus)"
-                  % (ohp.name if ohp is not None else "AdamW", cfg.gathers, what, cfg.name, elems / cap, dt,
-                     model or platform.machine(), os.cpu_count()),
-        "elements_per_s": round(elems / dt, 1),
+        "value": round(eps * per_elt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": "rank 0's step (reduce-scatter, %s, cast, %d gather%s) on %s, on %s; %d pass%s in %.1f s; "
+                  "%d B per shard element as the GPU line; host copies made before the timer; host %s (%s cpus)"
+                  % (opt_name, cfg.gathers, "s" if cfg.gathers > 1 else "", what, where, passes,
+                     "es" if passes > 1 else "", dt, per_elt, cpu_host_model(), os.cpu_count()),
+        "elements_per_s": round(eps, 1),
+        "bytes_per_shard_element": per_elt,
+        "seconds_per_step": round(step_s, 4),
+        "extrapolated": bool(extrap),
     }
 
 
@@ -552,41 +604,15 @@ def bench_offload(args, cfg, torch, ss, N, workloads):
         "shard_elements_per_s": round(S * cfg.blocks / (ms_step * 1e-3), 1),
         "roofline": roof, "offload": off, "cpu_baseline": None,
     }
-    print(json.dumps(out))
+    return out
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures the one-GPU hot path only; --gpus %d is not supported "
-              "(run with --gpus 1)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import sharded_state_amd as ss
-    from sharded_state_amd import _native as N
-    import workloads
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a HIP device", file=sys.stderr)
-        sys.exit(1)
-    lib = N.lib()
-    torch.cuda.set_device(0)
-
-    if args.probe == "copy":
-        print(json.dumps(dict(probe="copy", **copy_ceiling(torch, N, lib))))
-        return
-
-    cfg = workloads.CONFIGS[args.workload]
-    if args.state != "f32" and args.pipeline in ("separate", "offload"):
-        print("--state %s needs --pipeline units or unit" % args.state, file=sys.stderr)
-        sys.exit(2)
+def run_workload(args, cfg, torch, ss, N, lib, workloads):
+    """One workload: set-up, warm-up, K timed steps, the roofline of the
+    dominant launch, the CPU-oracle baselines and the flatten rate."""
     if args.pipeline == "offload":
-        bench_offload(args, cfg, torch, ss, N, workloads)
-        return
+        return bench_offload(args, cfg, torch, ss, N, workloads)
     ohp = optimizer_hp(args.optimizer, cfg, N)
-    if ohp is not None and (args.pipeline != "units" or args.state != "f32"):
-        print("--optimizer %s needs --pipeline units and fp32 state" % args.optimizer, file=sys.stderr)
-        sys.exit(2)
     n_states = ohp.n_states if ohp is not None else 2
     fused_b, per_elt = sizes(cfg, "separate" if args.pipeline == "separate" else "unit", args.state, n_states)
     pool = [Unit(cfg, b, ss, torch, workloads, args.state) for b in range(cfg.pool)]
@@ -756,15 +782,17 @@ def main():
             if t.dtype in (torch.float16, torch.bfloat16):
                 return t.view(torch.int16).numpy().view(np.uint16)
             return t.numpy()
-        cpu = cpu_baseline(cfg, pool[0], args.cpu_seconds, np_of_bytes, args.state, ohp)
+        hosts = [HostUnit(u, np_of_bytes) for u in pool]
+        cpu = cpu_baseline(cfg, hosts, per_elt, args.state, ohp, min_seconds=args.cpu_seconds, blocks=cfg.blocks)
         if args.cpu_all_cores_seconds > 0:
             try:
                 host_threads = len(os.sched_getaffinity(0))
             except (AttributeError, OSError):
                 host_threads = os.cpu_count() or 1
             if host_threads > 1:
-                cpu_all = cpu_baseline(cfg, pool[0], args.cpu_all_cores_seconds, np_of_bytes, args.state, ohp,
-                                       threads=host_threads)
+                cpu_all = cpu_baseline(cfg, hosts, per_elt, args.state, ohp, threads=host_threads,
+                                       min_seconds=args.cpu_all_cores_seconds, blocks=cfg.blocks)
+        del hosts
 
     ckpt = None
     if args.checkpoint:
@@ -790,10 +818,11 @@ def main():
                 "note": "blocking calls: device-to-host through pinned staging, CRC32C, file write + fsync "
                         "(load: read, CRC32C, host-to-device)"}
 
+    P = pool[0].P
+    del per_unit, groups, pool
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     flat = flatten_rate(cfg, ss, torch, N, lib, workloads, args.state)
-    ceil = copy_ceiling(torch, N, lib)
-    ceil["frac_of_peak"] = round(ceil["gbps"] / HBM_PEAK_GBPS, 4)
-    ceil["step_frac_of_copy"] = round(gbps / ceil["gbps"], 4)
     out = {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
@@ -803,7 +832,7 @@ def main():
                    "optimizer": args.optimizer, "state_dtype": args.state,
                    "streams": len(streams),
                    "world": cfg.world, "rank": 0,
-                   "shard_numel": S, "unit_numel": pool[0].P, "blocks_per_step": cfg.blocks,
+                   "shard_numel": S, "unit_numel": P, "blocks_per_step": cfg.blocks,
                    "distinct_blocks": cfg.pool, "grad_dtype": cfg.grad_dt,
                    "fp32_reduce_scatter": cfg.fp32_reduce, "compute_dtype": cfg.compute_dt,
                    "gathers_per_step": G, "bytes_per_shard_element": per_elt,
@@ -813,11 +842,64 @@ def main():
         "wall_s_timed": round(wall, 3),
         "flatten": flat,
         "roofline": roof,
-        "copy_ceiling": ceil,
         "cpu_baseline": cpu,
         "cpu_all_cores": cpu_all,
         "checkpoint": ckpt,
     }
+    return out
+
+
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures the one-GPU hot path only; --gpus %d is not supported "
+              "(run with --gpus 1)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.state != "f32" and args.pipeline in ("separate", "offload"):
+        print("--state %s needs --pipeline units or unit" % args.state, file=sys.stderr)
+        sys.exit(2)
+    if args.optimizer != "adamw" and (args.pipeline != "units" or args.state != "f32"):
+        print("--optimizer %s needs --pipeline units and fp32 state" % args.optimizer, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sharded_state_amd as ss
+    from sharded_state_amd import _native as N
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    lib = N.lib()
+    torch.cuda.set_device(0)
+
+    if args.probe == "copy":
+        print(json.dumps(dict(probe="copy", **copy_ceiling(torch, N, lib))))
+        return
+
+    names = ORDER if args.workload == "all" else [args.workload]
+    results = {}
+    for name in names:
+        t0 = time.perf_counter()
+        results[name] = run_workload(args, workloads.CONFIGS[name], torch, ss, N, lib, workloads)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        r = results[name]
+        print("bench: %s done in %.1f s: %.1f GB/s (%s)" % (r["config"]["workload"], time.perf_counter() - t0,
+                                                          r["value"], r.get("pct_hbm_peak", "-")),
+              file=sys.stderr, flush=True)
+    head = results[HEADLINE if args.workload == "all" else args.workload]
+    out = dict(head)
+    if args.pipeline != "offload":
+        ceil = copy_ceiling(torch, N, lib)
+        ceil["frac_of_peak"] = round(ceil["gbps"] / HBM_PEAK_GBPS, 4)
+        ceil["step_frac_of_copy"] = round(head["value"] / ceil["gbps"], 4)
+        out["copy_ceiling"] = ceil
+    if args.workload == "all":
+        keep = ("value", "unit", "ms_per_step", "pct_hbm_peak", "config", "shard_elements_per_s", "roofline",
+                "cpu_baseline", "cpu_all_cores", "flatten")
+        out["configs"] = {n: {k: r.get(k) for k in keep} for n, r in results.items()}
     print(json.dumps(out))
 
 

@@ -83,18 +83,22 @@ def test_more_than_one_gpu_is_refused():
     assert "one-GPU" in r.stderr and not r.stdout
 
 
-def test_cpu_baseline_single_core_and_all_cores():
-    """The oracle baseline runs on the host alone: one pinned core over the
-    first elements, or several threads over disjoint chunks of the shard."""
+def test_cpu_baseline_whole_units_and_extrapolation():
+    """The oracle baseline runs on the host alone over whole units (every unit
+    of the pool once per pass), on one pinned core or on several threads over
+    disjoint chunks, and counts the GPU line's bytes per shard element; with
+    fewer distinct units than slots per step it says it extrapolates."""
     import types
     import torch
     cfg = CONFIGS["gpt2-large-block"]           # N = 2, fp16 grads reduced in fp32, fp16 compute
     S = 8192
     g = torch.Generator().manual_seed(0)
-    unit = types.SimpleNamespace(
-        S=S, grads=[(torch.randn(2 * S, generator=g) * 1e-3).half() for _ in range(2)],
-        peers=[torch.randn(S, generator=g).half()], master=torch.randn(S, generator=g) * 0.02,
-        m=torch.zeros(S), v=torch.zeros(S))
+
+    def unit():
+        return types.SimpleNamespace(
+            S=S, grads=[(torch.randn(2 * S, generator=g) * 1e-3).half() for _ in range(2)],
+            peers=[torch.randn(S, generator=g).half()], master=torch.randn(S, generator=g) * 0.02,
+            m=torch.zeros(S), v=torch.zeros(S))
 
     def np_of_bytes(t):
         import numpy as np
@@ -102,9 +106,21 @@ def test_cpu_baseline_single_core_and_all_cores():
             return t.view(torch.int16).numpy().view(np.uint16)
         return t.numpy()
 
-    one = bench.cpu_baseline(cfg, unit, 0.2, np_of_bytes)
-    many = bench.cpu_baseline(cfg, unit, 0.2, np_of_bytes, threads=4)
+    units = [unit(), unit()]
+    hosts = [bench.HostUnit(u, np_of_bytes) for u in units]
+    per_elt = bench.sizes(cfg, "unit", "f32", 2)[1]
+    assert per_elt == 34
+    one = bench.cpu_baseline(cfg, hosts, per_elt, min_seconds=0.1, blocks=2)
+    many = bench.cpu_baseline(cfg, hosts, per_elt, threads=4, min_seconds=0.1, blocks=36)
     assert one["cores"] == 1 and many["cores"] == 4
     for r in (one, many):
         assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0 and r["elements_per_s"] > 0
-    assert "disjoint chunks on 4 threads" in many["sample"]
+        assert r["bytes_per_shard_element"] == 34
+        assert abs(r["value"] - r["elements_per_s"] * 34 / 1e9) <= 1e-3 * r["value"] + 1e-4
+    assert not one["extrapolated"] and "whole units: all 2 blocks" in one["sample"]
+    assert many["extrapolated"] and "extrapolated from K = 2" in many["sample"]
+    assert "disjoint chunks" in many["sample"]
+    # the per-step time scales the pool's pass to the step's 36 slots
+    assert many["seconds_per_step"] > 0
+    # the device inputs were copied before timing: the host state moved, the device state did not
+    assert not (units[0].master.numpy() == hosts[0].p).all()
