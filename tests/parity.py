@@ -201,3 +201,73 @@ class UnitRun:
             assert tuple(v.shape) == tuple(o.shape)
             assert_bitexact(np_of(m).reshape(-1), np_of(v).reshape(-1), "unflatten copy %d" % k)
             compare_compute(np_of(v).reshape(-1), o.reshape(-1), c.compute_dt, "view %d" % k)
+
+
+def host_threads(cap=16):
+    """Host threads this process may use (at most `cap`)."""
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(cap, n))
+
+
+def oracle_rank_step_threaded(grads, p, m, v, h, grad_dt, fp32_reduce, compute_dt, threads=None):
+    """One rank's step by the oracle on whole shards, over disjoint chunks on
+    several host threads (the oracle's C calls run outside the GIL; the step is
+    pointwise, so chunking changes no value).  grads[q] holds rank q's gradient
+    block of this rank (storage arrays); p, m, v (fp32) are updated in place.
+    Returns (averaged gradient shard, compute shard)."""
+    from concurrent.futures import ThreadPoolExecutor
+    oracle.lib()
+    S = p.size
+    avg_dt = "f32" if (fp32_reduce or grad_dt == "f32") else grad_dt
+    avg = np.empty(S, dtype=oracle.NP_STORAGE[avg_dt])
+    comp = np.empty(S, dtype=oracle.NP_STORAGE[compute_dt])
+    threads = threads or host_threads()
+    parts = max(1, min(S // 4096, 4 * threads)) if S else 0
+    bounds = [S * k // parts for k in range(parts + 1)] if parts else [0]
+
+    def work(k):
+        lo, hi = bounds[k], bounds[k + 1]
+        if hi <= lo:
+            return
+        a = oracle.grad_average(grads, lo, hi - lo, grad_dt, fp32_reduce)
+        avg[lo:hi] = a
+        g32 = a if a.dtype == np.float32 else oracle.to_f32(a, grad_dt)
+        oracle.adamw(p[lo:hi], m[lo:hi], v[lo:hi], g32, h)
+        comp[lo:hi] = oracle.cast(p[lo:hi], compute_dt)
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(work, range(parts)))
+    return avg, comp
+
+
+def assert_compute_close(got, ref, dt, what):
+    """The compute-copy bar on whole buffers: equal encodings pass at once;
+    otherwise only the differing positions are checked (<= 1 ulp, fp32 rel)."""
+    got, ref = np.asarray(got), np.asarray(ref)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    if dt == "f32":
+        if np.array_equal(got.view(np.uint32), ref.view(np.uint32)):
+            return
+        diff = np.nonzero(got.view(np.uint32) != ref.view(np.uint32))[0]
+        assert_rel(got[diff], ref[diff], what)
+        return
+    if np.array_equal(got, ref):
+        return
+    diff = np.nonzero(got != ref)[0]
+    assert_ulp16(got[diff], ref[diff], dt, what)
+
+
+def assert_bits_equal(got, ref, what):
+    """Whole-buffer bit equality without float temporaries (NaN payloads included)."""
+    got, ref = np.asarray(got), np.asarray(ref)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    view = np.uint32 if got.dtype.itemsize == 4 else np.uint16
+    a, b = got.view(view), ref.view(view)
+    if not np.array_equal(a, b):
+        bad = np.nonzero(a != b)[0]
+        raise AssertionError("%s: %d of %d differ, first at %d: 0x%x vs 0x%x"
+                             % (what, bad.size, a.size, bad[0], int(a[bad[0]]), int(b[bad[0]])))
