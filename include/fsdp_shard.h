@@ -51,8 +51,10 @@ extern "C" {
 
 #define FSDP_API __attribute__((visibility("default")))
 
-#define FSDP_ABI_VERSION 8
+#define FSDP_ABI_VERSION 9
 #define FSDP_MAX_WORLD 128
+/* Bytes of the device scratch of fsdp_offload_step_units_noalloc (per device). */
+#define FSDP_OFFLOAD_SCRATCH_BYTES (32 << 20)
 
 typedef enum fsdp_dtype {
     FSDP_F32 = 0,   /* IEEE binary32 */
@@ -413,6 +415,29 @@ FSDP_API int fsdp_offload_step_units(const fsdp_offload_unit* units, int32_t n_u
                                      fsdp_dtype compute_dt, int64_t chunk_numel,
                                      const fsdp_adamw_hp* hp, int32_t n_threads, void* stream,
                                      void* copy_stream);
+
+/* fsdp_offload_step_units for callers that cannot allocate device memory
+ * (harnesses that forbid hipMalloc during steps, serving loops with a fixed
+ * memory budget), and which cannot spare a device gradient shard per unit.
+ * Same arguments, results and blocking behaviour as fsdp_offload_step_units,
+ * except that every unit's grad_shard_dev must be NULL: each chunk of a unit's
+ * gradient shard is reduce-scattered into a device scratch array of
+ * FSDP_OFFLOAD_SCRATCH_BYTES (32 MiB) that the library holds per device until
+ * the process ends, and copied to grad_shard_host from there.  Limit: a chunk
+ * must fit the scratch, chunk_numel * (4 bytes when fp32_reduce or fp32
+ * gradients, else 2) <= FSDP_OFFLOAD_SCRATCH_BYTES after rounding chunk_numel
+ * up to a multiple of 8 (<= 0 means 4 Mi elements, which fits); FSDP_E_SIZE
+ * otherwise, before anything is enqueued.  Its first call on a device, with
+ * that device current, looks up the scratch's device address and creates 258
+ * events for that device; later calls call no hipMalloc, hipFree, event or
+ * stream creation (host-side bookkeeping uses the C++ heap).  Calls that
+ * overlap in time on one device (two host threads, or two streams before the
+ * first call has returned) share the scratch and race; calls on different
+ * devices do not. */
+FSDP_API int fsdp_offload_step_units_noalloc(const fsdp_offload_unit* units, int32_t n_units, int32_t world,
+                                             int32_t rank, fsdp_dtype grad_dt, int32_t fp32_reduce,
+                                             fsdp_dtype compute_dt, int64_t chunk_numel, const fsdp_adamw_hp* hp,
+                                             int32_t n_threads, void* stream, void* copy_stream);
 
 /* fsdp_offload_step_units for one unit, its fields passed one by one. */
 FSDP_API int fsdp_offload_step(float* master, float* exp_avg, float* exp_avg_sq,

@@ -30,6 +30,7 @@ from .offload import (  # noqa: F401
     fsdp_host_adamw,
     fsdp_offload_step,
     fsdp_offload_step_units,
+    fsdp_offload_step_units_noalloc,
     prepare_offload_step_units,
 )
 from .checkpoint import consolidate, load_shard, save_shard, shard_info, shard_path  # noqa: F401
@@ -39,5 +40,5 @@ __all__ = [
     "fsdp_reduce_scatter_local", "fsdp_sharded_adamw", "fsdp_step_unit", "fsdp_step_units", "prepare_step_units", "fsdp_unshard_gather",
     "fsdp_unflatten_views", "view_table", "RankState", "save_shard", "load_shard", "shard_info",
     "shard_path", "consolidate", "fsdp_host_adamw", "fsdp_offload_step", "fsdp_offload_step_units",
-    "prepare_offload_step_units", "OffloadState", "unit_gather_split", "units_in_launch",
+    "fsdp_offload_step_units_noalloc", "prepare_offload_step_units", "OffloadState", "unit_gather_split", "units_in_launch",
 ]

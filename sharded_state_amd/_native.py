@@ -13,7 +13,8 @@ LIB_PATH = os.path.join(_HERE, "libfsdp_shard.so")
 F32, F16, BF16 = 0, 1, 2
 OK, E_INVAL, E_DTYPE, E_SIZE, E_ALIAS, E_HIP, E_IO, E_FORMAT = 0, -1, -2, -3, -4, -5, -6, -7
 MAX_WORLD = 128
-ABI_VERSION = 8
+ABI_VERSION = 9
+OFFLOAD_SCRATCH_BYTES = 32 << 20
 OPT_ADAMW, OPT_SGD, OPT_ADAMAX, OPT_ADADELTA = 0, 1, 2, 3
 
 
@@ -175,6 +176,8 @@ def lib():
     L.fsdp_offload_step_units.restype = ctypes.c_int
     L.fsdp_offload_step_units.argtypes = [ctypes.POINTER(OffloadUnit), i32, i32, i32, ctypes.c_int, i32,
                                           ctypes.c_int, i64, ctypes.POINTER(AdamWHP), i32, vp, vp]
+    L.fsdp_offload_step_units_noalloc.restype = ctypes.c_int
+    L.fsdp_offload_step_units_noalloc.argtypes = L.fsdp_offload_step_units.argtypes
     v = L.fsdp_abi_version()
     if v != ABI_VERSION:
         raise ImportError("libfsdp_shard.so ABI version %d, binding expects %d" % (v, ABI_VERSION))

@@ -62,6 +62,28 @@ AdamScalars adam_scalars(const fsdp_adamw_hp& hp) {
     return s;
 }
 
+static std::atomic<int> g_cus[64];
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < 64) {
+        int c = g_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev >= 0 && dev < 64) g_cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+ReduceScalars reduce_scalars(int world) {
+    ReduceScalars r;
+    r.n = (float)world;
+    r.inv_n = (float)(1.0 / (double)world);
+    return r;
+}
+
 int check_hp(const char* fn, const fsdp_adamw_hp* hp) {
     if (!hp) return fail(FSDP_E_INVAL, "%s: hp is NULL", fn);
     if (hp->step < 1) return fail(FSDP_E_INVAL, "%s: hp->step = %lld < 1", fn, (long long)hp->step);
@@ -84,6 +106,8 @@ using fsdp::ok;
 using fsdp::valid_dtype;
 using fsdp::adam_scalars;
 using fsdp::check_hp;
+using fsdp::cu_count;
+using fsdp::reduce_scalars;
 
 // Byte range [lo, lo + n) of device memory.
 struct Range {
@@ -98,30 +122,7 @@ bool overlaps(Range a, Range b) {
     return a.lo < b.lo + b.n && b.lo < a.lo + a.n;
 }
 
-// Compute units of the current device (cached per device).
-std::atomic<int> g_cus[64];
-int cu_count() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (dev >= 0 && dev < 64) {
-        int c = g_cus[dev].load(std::memory_order_relaxed);
-        if (c > 0) return c;
-    }
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-        n = 256;
-    if (dev >= 0 && dev < 64) g_cus[dev].store(n, std::memory_order_relaxed);
-    return n;
-}
-
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
-
-fsdp::ReduceScalars reduce_scalars(int world) {
-    fsdp::ReduceScalars r;
-    r.n = (float)world;
-    r.inv_n = (float)(1.0 / (double)world);
-    return r;
-}
 
 // Shared validation of world / rank / shard size.
 int check_world(int32_t world, int32_t rank, int64_t S) {

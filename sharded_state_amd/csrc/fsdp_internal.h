@@ -23,6 +23,10 @@ const char* last_error();
 // AdamW constants of step hp->step, computed in double and rounded once to fp32
 // (decay = 1 - lr*wd, step_size = lr / (1 - beta1^t), bc2_sqrt = sqrt(1 - beta2^t)).
 AdamScalars adam_scalars(const fsdp_adamw_hp& hp);
+// Compute units of the current device (cached per device; 256 if unknown).
+int cu_count();
+// The divisor of the reduce-scatter average: N, and 1/N for the specialised kernels.
+ReduceScalars reduce_scalars(int world);
 // FSDP_E_INVAL (message prefixed with fn) unless hp is non-NULL, step >= 1,
 // both betas lie in [0, 1) and lr, weight_decay and eps are >= 0 (not NaN).
 int check_hp(const char* fn, const fsdp_adamw_hp* hp);

@@ -293,12 +293,15 @@ bool apart(const std::vector<Span>& outs, const std::vector<Span>& ins) {
 }
 
 int check_unit(const fsdp_offload_unit& u, int k, int32_t world, int32_t rank, int grad_dt, int64_t as, int64_t cs,
-               std::vector<Span>& host, std::vector<Span>& dev_out, std::vector<Span>& dev_in) {
+               bool scratch, std::vector<Span>& host, std::vector<Span>& dev_out, std::vector<Span>& dev_in) {
     if (u.shard_numel < 0) return fsdp::fail(FSDP_E_INVAL, "unit %d: shard_numel < 0", k);
     if (u.shard_numel == 0) return FSDP_OK;
     const int64_t S = u.shard_numel;
-    if (!u.master || !u.exp_avg || !u.exp_avg_sq || !u.rank_grads || !u.grad_shard_dev || !u.grad_shard_host ||
-        !u.compute_host || !u.compute_dev)
+    if (scratch && u.grad_shard_dev)
+        return fsdp::fail(FSDP_E_INVAL, "unit %d: grad_shard_dev must be NULL (the gradient chunks live in the "
+                                        "library's scratch)", k);
+    if (!u.master || !u.exp_avg || !u.exp_avg_sq || !u.rank_grads || (!scratch && !u.grad_shard_dev) ||
+        !u.grad_shard_host || !u.compute_host || !u.compute_dev)
         return fsdp::fail(FSDP_E_INVAL, "unit %d: every buffer must be non-NULL", k);
     for (int q = 0; q < world; ++q) {
         if (!u.rank_grads[q]) return fsdp::fail(FSDP_E_INVAL, "unit %d: rank_grads[%d] is NULL", k, q);
@@ -310,8 +313,51 @@ int check_unit(const fsdp_offload_unit& u, int k, int32_t world, int32_t rank, i
     host.push_back(span(u.exp_avg_sq, 4 * S));
     host.push_back(span(u.grad_shard_host, as * S));
     host.push_back(span(u.compute_host, cs * S));
-    dev_out.push_back(span(u.grad_shard_dev, as * S));
+    if (!scratch) dev_out.push_back(span(u.grad_shard_dev, as * S));
     dev_out.push_back(span(u.compute_dev, cs * S));
+    return FSDP_OK;
+}
+
+// ------------------------------------------------------------------ scratch
+// The no-allocation variant (fsdp_offload_step_units_noalloc) reduces each
+// chunk of a gradient shard into this file-scope device array and copies it to
+// the host from there, instead of a caller's device gradient shard.  Every
+// device holds its own copy until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: kernels and copies take the
+// address that scratch_setup obtained for the current device.
+constexpr int64_t kScratchBytes = FSDP_OFFLOAD_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Per device: the address of `scratch`, and events for the chunk copies (chunk
+// c records ev[c % kScratchEvents]; a reused event only makes a worker wait for
+// a later copy of the same stream) plus two that order the copy stream.
+constexpr int kScratchEvents = 256;
+constexpr int kMaxDevices = 64;
+struct ScratchDevice {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    void* ptr = nullptr;
+    hipEvent_t ev[kScratchEvents + 2] = {};
+};
+ScratchDevice g_scratch[kMaxDevices];
+
+// Set-up, once per device with that device current (the first call of the
+// variant on it): hipGetSymbolAddress for the device's copy of `scratch`, and
+// the events.  Later calls create nothing.
+int scratch_setup(ScratchDevice** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fsdp::hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fsdp::fail(FSDP_E_INVAL, "device %d: the scratch is kept for devices 0-%d only", dev, kMaxDevices - 1);
+    ScratchDevice& d = g_scratch[dev];
+    std::call_once(d.once, [&d] {
+        d.err = hipGetSymbolAddress(&d.ptr, HIP_SYMBOL(scratch));
+        for (int i = 0; i < kScratchEvents + 2 && d.err == hipSuccess; ++i)
+            d.err = hipEventCreateWithFlags(&d.ev[i], hipEventDisableTiming);
+    });
+    if (d.err != hipSuccess) return fsdp::hip_fail(d.err, "scratch set-up (hipGetSymbolAddress / events)");
+    *out = &d;
     return FSDP_OK;
 }
 
@@ -327,7 +373,7 @@ constexpr int64_t kPart = 1 << 15;   // elements per work item at most (128 KB o
 
 int offload_units(const fsdp_offload_unit* units, int32_t n_units, int32_t world, int32_t rank, int grad_dt,
                   int32_t fp32_reduce, int compute_dt, int64_t chunk_numel, const fsdp_adamw_hp* hp,
-                  int32_t n_threads, void* stream, void* copy_stream, const char* fn) {
+                  int32_t n_threads, void* stream, void* copy_stream, const char* fn, bool use_scratch) {
     if (n_units < 0) return fsdp::fail(FSDP_E_INVAL, "%s: n_units < 0", fn);
     if (n_units > 0 && !units) return fsdp::fail(FSDP_E_INVAL, "%s: units is NULL", fn);
     if (world < 1 || world > FSDP_MAX_WORLD || rank < 0 || rank >= world)
@@ -337,13 +383,18 @@ int offload_units(const fsdp_offload_unit* units, int32_t n_units, int32_t world
     int rc = fsdp::check_hp(fn, hp);
     if (rc) return rc;
     if (chunk_numel <= 0) chunk_numel = 4 << 20;
+    if (chunk_numel > (int64_t(1) << 40)) return fsdp::fail(FSDP_E_INVAL, "%s: chunk_numel too large", fn);
     chunk_numel = (chunk_numel + 7) / 8 * 8;
     const int64_t part = std::min(kPart, chunk_numel);
     const int avg_dt = (fp32_reduce || grad_dt == FSDP_F32) ? FSDP_F32 : grad_dt;
     const int64_t as = fsdp::dt_size(avg_dt), cs = fsdp::dt_size(compute_dt);
+    if (use_scratch && chunk_numel * as > kScratchBytes)
+        return fsdp::fail(FSDP_E_SIZE, "%s: a chunk of %lld elements of %lld bytes exceeds the %lld-byte scratch "
+                                       "(at most %lld elements per chunk)", fn, (long long)chunk_numel, (long long)as,
+                          (long long)kScratchBytes, (long long)(kScratchBytes / as / 8 * 8));
     std::vector<Span> host, dev_out, dev_in;
     for (int k = 0; k < n_units; ++k) {
-        rc = check_unit(units[k], k, world, rank, grad_dt, as, cs, host, dev_out, dev_in);
+        rc = check_unit(units[k], k, world, rank, grad_dt, as, cs, use_scratch, host, dev_out, dev_in);
         if (rc) return rc;
     }
     if (!disjoint(host)) return fsdp::fail(FSDP_E_ALIAS, "%s: two host buffers overlap", fn);
@@ -366,11 +417,24 @@ int offload_units(const fsdp_offload_unit* units, int32_t n_units, int32_t world
 
     std::vector<hipEvent_t> ready(chunks.size(), nullptr);
     hipEvent_t entry = nullptr, done = nullptr;
+    ScratchDevice* sd = nullptr;
+    if (use_scratch) {
+        // the device's scratch and its events: nothing is created after set-up
+        rc = scratch_setup(&sd);
+        if (rc) return rc;
+        for (size_t c = 0; c < chunks.size(); ++c) ready[c] = sd->ev[c % kScratchEvents];
+        if (cst != st) {
+            entry = sd->ev[kScratchEvents];
+            done = sd->ev[kScratchEvents + 1];
+        }
+    }
     struct Cleanup {
         std::vector<hipEvent_t>& ev;
         hipEvent_t& a;
         hipEvent_t& b;
+        bool owned;
         ~Cleanup() {
+            if (!owned) return;   // the scratch's events stay with their device
             for (hipEvent_t x : ev)
                 if (x) {
                     (void)hipEventSynchronize(x);
@@ -379,31 +443,64 @@ int offload_units(const fsdp_offload_unit* units, int32_t n_units, int32_t world
             if (a) (void)hipEventDestroy(a);
             if (b) (void)hipEventDestroy(b);
         }
-    } cleanup{ready, entry, done};
+    } cleanup{ready, entry, done, !use_scratch};
     hipError_t e = hipSuccess;
-    for (size_t c = 0; c < chunks.size() && e == hipSuccess; ++c)
-        e = hipEventCreateWithFlags(&ready[c], hipEventDisableTiming);
-    if (e != hipSuccess) return fsdp::hip_fail(e, "event creation");
+    if (!use_scratch) {
+        for (size_t c = 0; c < chunks.size() && e == hipSuccess; ++c)
+            e = hipEventCreateWithFlags(&ready[c], hipEventDisableTiming);
+        if (e != hipSuccess) return fsdp::hip_fail(e, "event creation");
+        if (cst != st && ((e = hipEventCreateWithFlags(&entry, hipEventDisableTiming)) != hipSuccess ||
+                          (e = hipEventCreateWithFlags(&done, hipEventDisableTiming)) != hipSuccess))
+            return fsdp::hip_fail(e, "event creation");
+    }
     if (cst != st) {
         // the copy stream starts after the work already on `stream` (a reader of compute_dev)
-        if ((e = hipEventCreateWithFlags(&entry, hipEventDisableTiming)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&done, hipEventDisableTiming)) != hipSuccess ||
-            (e = hipEventRecord(entry, st)) != hipSuccess || (e = hipStreamWaitEvent(cst, entry, 0)) != hipSuccess)
+        if ((e = hipEventRecord(entry, st)) != hipSuccess || (e = hipStreamWaitEvent(cst, entry, 0)) != hipSuccess)
             return fsdp::hip_fail(e, "copy stream ordering");
     }
 
     // 1. every unit's reduce-scatter and gradient copies to the host, in order
     size_t c = 0;
+    const int64_t gs = fsdp::dt_size(grad_dt);
+    std::vector<const void*> gp(world);
+    (void)hipGetLastError();
     for (int k = 0; k < n_units; ++k) {
         const fsdp_offload_unit& u = units[k];
         if (u.shard_numel == 0) continue;
-        rc = fsdp_reduce_scatter_local(u.rank_grads, world, rank, u.shard_numel, (fsdp_dtype)grad_dt, fp32_reduce,
-                                       u.grad_shard_dev, stream);
-        if (rc) return rc;
+        if (!use_scratch) {
+            rc = fsdp_reduce_scatter_local(u.rank_grads, world, rank, u.shard_numel, (fsdp_dtype)grad_dt,
+                                           fp32_reduce, u.grad_shard_dev, stream);
+            if (rc) return rc;
+        }
         for (; c < chunks.size() && chunks[c].unit == k; ++c) {
             const Chunk& ch = chunks[c];
-            e = hipMemcpyAsync((char*)u.grad_shard_host + ch.lo * as, (const char*)u.grad_shard_dev + ch.lo * as,
-                               ch.n * as, hipMemcpyDeviceToHost, st);
+            const char* src = nullptr;
+            if (!use_scratch) {
+                src = (const char*)u.grad_shard_dev + ch.lo * as;
+            } else {
+                // this chunk's reduce-scatter into the scratch; stream order keeps
+                // the next chunk's from overwriting it before its copy has run
+                bool vec = true;
+                for (int q = 0; q < world; ++q) {
+                    gp[q] = (const char*)u.rank_grads[q] + ((int64_t)rank * u.shard_numel + ch.lo) * gs;
+                    vec = vec && ((uintptr_t)gp[q] & 15) == 0;
+                }
+                fsdp::ReduceArgs a{};
+                a.grads = gp.data();
+                a.world = world;
+                a.grad_dt = grad_dt;
+                a.fp32_reduce = fp32_reduce != 0;
+                a.S = ch.n;
+                a.nvec = vec ? ch.n / 8 : 0;
+                a.out = sd->ptr;
+                a.rs = fsdp::reduce_scalars(world);
+                a.cus = fsdp::cu_count();
+                a.stream = stream;
+                e = fsdp::launch_reduce_scatter(a);
+                if (e != hipSuccess) return fsdp::hip_fail(e, "reduce-scatter launch");
+                src = (const char*)sd->ptr;
+            }
+            e = hipMemcpyAsync((char*)u.grad_shard_host + ch.lo * as, src, ch.n * as, hipMemcpyDeviceToHost, st);
             if (e == hipSuccess) e = hipEventRecord(ready[c], st);
             if (e != hipSuccess) return fsdp::hip_fail(e, "device-to-host copy of a gradient shard");
         }
@@ -500,7 +597,15 @@ int fsdp_offload_step_units(const fsdp_offload_unit* units, int32_t n_units, int
                             fsdp_dtype grad_dt, int32_t fp32_reduce, fsdp_dtype compute_dt, int64_t chunk_numel,
                             const fsdp_adamw_hp* hp, int32_t n_threads, void* stream, void* copy_stream) {
     return offload_units(units, n_units, world, rank, grad_dt, fp32_reduce, compute_dt, chunk_numel, hp, n_threads,
-                         stream, copy_stream, "fsdp_offload_step_units");
+                         stream, copy_stream, "fsdp_offload_step_units", false);
+}
+
+int fsdp_offload_step_units_noalloc(const fsdp_offload_unit* units, int32_t n_units, int32_t world, int32_t rank,
+                                    fsdp_dtype grad_dt, int32_t fp32_reduce, fsdp_dtype compute_dt,
+                                    int64_t chunk_numel, const fsdp_adamw_hp* hp, int32_t n_threads, void* stream,
+                                    void* copy_stream) {
+    return offload_units(units, n_units, world, rank, grad_dt, fp32_reduce, compute_dt, chunk_numel, hp, n_threads,
+                         stream, copy_stream, "fsdp_offload_step_units_noalloc", true);
 }
 
 int fsdp_offload_step(float* master, float* exp_avg, float* exp_avg_sq, const void* const* rank_grads,
@@ -511,7 +616,7 @@ int fsdp_offload_step(float* master, float* exp_avg, float* exp_avg_sq, const vo
     const fsdp_offload_unit u{master, exp_avg, exp_avg_sq, rank_grads, grad_shard_dev, grad_shard_host,
                               compute_host, compute_dev, shard_numel};
     return offload_units(&u, 1, world, rank, grad_dt, fp32_reduce, compute_dt, chunk_numel, hp, n_threads, stream,
-                         copy_stream, "fsdp_offload_step");
+                         copy_stream, "fsdp_offload_step", false);
 }
 
 }  // extern "C"

@@ -63,8 +63,9 @@ def fsdp_host_adamw(master, exp_avg, exp_avg_sq, grad, hp, compute=None, n_threa
 
 
 def _unit(master, exp_avg, exp_avg_sq, rank_grads, grad_shard_dev, grad_shard_host, compute_host, compute_dev,
-          fp32_reduce):
-    """Check one unit's tensors; returns (OffloadUnit, grad dtype, compute dtype, keep-alive)."""
+          fp32_reduce, device_grad=True):
+    """Check one unit's tensors; returns (OffloadUnit, grad dtype, compute dtype, keep-alive).
+    Without device_grad (the no-allocation call) grad_shard_dev must be None."""
     S = master.numel()
     for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
         _host(t, name, torch.float32)
@@ -72,20 +73,24 @@ def _unit(master, exp_avg, exp_avg_sq, rank_grads, grad_shard_dev, grad_shard_ho
             raise ValueError("%s has %d elements, master %d" % (name, t.numel(), S))
     rank_grads, world, gdt = _grads(rank_grads, S)
     odt = torch.float32 if (fp32_reduce or gdt == torch.float32) else gdt
-    _dev(grad_shard_dev, "grad_shard_dev")
+    if device_grad:
+        _dev(grad_shard_dev, "grad_shard_dev")
+        if grad_shard_dev.dtype != odt:
+            raise TypeError("grad_shard_dev must be %s, got %s" % (odt, grad_shard_dev.dtype))
+    elif grad_shard_dev is not None:
+        raise ValueError("the no-allocation call takes no grad_shard_dev (its chunks live in the library's scratch)")
     _dev(compute_dev, "compute_dev")
     _host(grad_shard_host, "grad_shard_host", odt)
     _host(compute_host, "compute_host", compute_dev.dtype)
-    if grad_shard_dev.dtype != odt:
-        raise TypeError("grad_shard_dev must be %s, got %s" % (odt, grad_shard_dev.dtype))
     for name, t in (("grad_shard_dev", grad_shard_dev), ("grad_shard_host", grad_shard_host),
                     ("compute_host", compute_host), ("compute_dev", compute_dev)):
-        if t.numel() != S:
+        if t is not None and t.numel() != S:
             raise ValueError("%s has %d elements, need %d" % (name, t.numel(), S))
-    _same_device(rank_grads + [grad_shard_dev, compute_dev])
+    _same_device(rank_grads + [compute_dev] + ([grad_shard_dev] if device_grad else []))
     gptr = N.ptr_array([g.data_ptr() for g in rank_grads])
-    u = N.OffloadUnit(master.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), gptr, grad_shard_dev.data_ptr(),
-                      grad_shard_host.data_ptr(), compute_host.data_ptr(), compute_dev.data_ptr(), S)
+    u = N.OffloadUnit(master.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), gptr,
+                      grad_shard_dev.data_ptr() if device_grad else None, grad_shard_host.data_ptr(),
+                      compute_host.data_ptr(), compute_dev.data_ptr(), S)
     return u, world, gdt, compute_dev.dtype, gptr
 
 
@@ -155,6 +160,35 @@ def prepare_offload_step_units(units, rank, fp32_reduce, hp, chunk_numel=0, n_th
     return call
 
 
+def fsdp_offload_step_units_noalloc(units, rank, fp32_reduce, hp, chunk_numel=0, n_threads=None, stream=None,
+                                    copy_stream=None):
+    """fsdp_offload_step_units without a device gradient shard: each chunk is
+    reduce-scattered into the library's fixed per-device scratch
+    (OFFLOAD_SCRATCH_BYTES) and copied to the host from there; no device
+    memory is allocated.  units: (OffloadState made with device_grad=False,
+    rank_grads, compute_dev) triples.  Calls that overlap on one device race."""
+    if not units:
+        raise ValueError("units is empty")
+    table = (N.OffloadUnit * len(units))()
+    keep, meta = [], None
+    for k, (st, grads, cdev) in enumerate(units):
+        u, world, gdt, cdt, gptr = _unit(st.master, st.exp_avg, st.exp_avg_sq, grads, st.grad_dev, st.grad_host,
+                                         st.compute_host, cdev, st.fp32_reduce, device_grad=False)
+        if meta is None:
+            meta = (world, gdt, cdt, st.fp32_reduce, cdev.device)
+        elif meta != (world, gdt, cdt, st.fp32_reduce, cdev.device):
+            raise ValueError("unit %d: world, dtypes, fp32_reduce and device must match unit 0" % k)
+        table[k] = u
+        keep.append(gptr)
+    world, gdt, cdt, fp32, device = meta
+    hp = _hp(hp)
+    with torch.cuda.device(device):
+        check("fsdp_offload_step_units_noalloc", N.lib().fsdp_offload_step_units_noalloc(
+            table, len(units), world, int(rank), dtype_code(gdt), int(bool(fp32)), dtype_code(cdt), int(chunk_numel),
+            ctypes.byref(hp), int(n_threads or DEFAULT_THREADS), _stream(stream, device), _cstream(copy_stream)))
+    del keep
+
+
 def fsdp_offload_step_units(units, rank, fp32_reduce, hp, chunk_numel=0, n_threads=None, stream=None,
                             copy_stream=None):
     """Offloaded step of a batch of units: (OffloadState, rank_grads,
@@ -170,10 +204,11 @@ class OffloadState:
     """One rank's offloaded shard state for one unit: pinned host master, m, v,
     pinned staging for the gradient and compute shards, and a device buffer for
     the reduce-scatter output.  Device memory held: S elements of the gradient
-    shard dtype (the fp32 state, 12 bytes per element, stays on the host)."""
+    shard dtype (the fp32 state, 12 bytes per element, stays on the host), none
+    with device_grad=False (for fsdp_offload_step_units_noalloc)."""
 
     def __init__(self, master_shard, grad_dtype, fp32_reduce, compute_dtype, device, exp_avg=None,
-                 exp_avg_sq=None):
+                 exp_avg_sq=None, device_grad=True):
         S = master_shard.numel()
         pin = dict(pin_memory=True)
         self.master = torch.empty(S, dtype=torch.float32, **pin)
@@ -186,7 +221,7 @@ class OffloadState:
             self.exp_avg_sq.copy_(exp_avg_sq.reshape(-1).cpu())
         odt = torch.float32 if (fp32_reduce or grad_dtype == torch.float32) else grad_dtype
         self.fp32_reduce = fp32_reduce
-        self.grad_dev = torch.empty(S, dtype=odt, device=device)
+        self.grad_dev = torch.empty(S, dtype=odt, device=device) if device_grad else None
         self.grad_host = torch.empty(S, dtype=odt, **pin)
         self.compute_host = torch.empty(S, dtype=compute_dtype, **pin)
         self.S = S

@@ -286,3 +286,27 @@ def test_every_adamw_entry_point_checks_the_same_hyper_parameters(field, value):
     for name, call in calls.items():
         assert call() == N.E_INVAL, name
         assert ">= 0" in L.fsdp_last_error().decode(), name
+
+
+def test_noalloc_offload_checks_the_scratch_limit_before_any_device_work():
+    """The no-allocation offload step refuses a chunk larger than its
+    FSDP_OFFLOAD_SCRATCH_BYTES scratch (FSDP_E_SIZE) and a unit that brings its
+    own device gradient shard (FSDP_E_INVAL), before touching the device."""
+    L = N.lib()
+    hp = N.AdamWHP()
+    g = N.ptr_array([FAKE + (3 << 30), FAKE + (4 << 30)])
+    host = [FAKE + (k << 34) for k in range(1, 6)]
+
+    def call(chunk, fp32_reduce=1, grad_dev=None):
+        u = (N.OffloadUnit * 1)(N.OffloadUnit(host[0], host[1], host[2], g, grad_dev, host[3], host[4],
+                                              FAKE + (8 << 30), 1000))
+        return L.fsdp_offload_step_units_noalloc(u, 1, 2, 0, N.F16, fp32_reduce, N.F16, chunk, ctypes.byref(hp), 1,
+                                                 None, None)
+
+    limit = N.OFFLOAD_SCRATCH_BYTES
+    assert call(limit // 4 + 8) == N.E_SIZE                  # fp32 average: 4 bytes per element
+    assert "scratch" in L.fsdp_last_error().decode()
+    assert call(limit // 4 + 1) == N.E_SIZE                  # rounded up to a multiple of 8 first
+    assert call(limit // 2 + 8, fp32_reduce=0) == N.E_SIZE   # 16-bit average: 2 bytes per element
+    assert call(0, grad_dev=FAKE + (9 << 30)) == N.E_INVAL
+    assert "grad_shard_dev must be NULL" in L.fsdp_last_error().decode()
