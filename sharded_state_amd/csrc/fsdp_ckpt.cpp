@@ -12,8 +12,10 @@
 //   [256, 256 + 8*T)    the unit's tensor sizes (int64 numels, flat order)
 //   [payload_offset..)  master, exp_avg, exp_avg_sq shards, S elements each of the
 //                       state dtype, back to back; payload_offset is 4096-aligned
-// The header carries CRC32C (Castagnoli) checksums of the size table and of the
-// payload.  A file is written to "<path>.tmp", flushed, synced and renamed, so a
+//                       and the file ends with the payload
+// The header carries CRC32C (Castagnoli) checksums of itself (with its own
+// checksum field zero), of the size table and of the payload; a reader checks
+// every size and offset against the file's length before it allocates or seeks.  A file is written to "<path>.tmp", flushed, synced and renamed, so a
 // reader never sees a partial file under the final name.  Device buffers move
 // through two pinned host staging buffers: the copy of chunk k+1 overlaps the
 // file write of chunk k, and each chunk's checksum runs on a helper thread
@@ -30,6 +32,7 @@
 #include <vector>
 
 #include <fcntl.h>
+#include <sys/stat.h>
 #include <unistd.h>
 
 #include "fsdp_internal.h"
@@ -38,7 +41,7 @@
 namespace {
 
 constexpr char kMagic[8] = {'F', 'S', 'D', 'P', 'S', 'H', 'R', 'D'};
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 2;   // 2: the header checksums itself
 constexpr uint64_t kAlign = 4096;
 constexpr size_t kChunk = 32u << 20;   // staging chunk
 
@@ -60,7 +63,8 @@ struct FileHeader {
     uint64_t payload_bytes;
     uint32_t crc_table;
     uint32_t crc_payload;
-    uint8_t reserved[256 - 112];
+    uint32_t crc_header;   // CRC32C of the 256 header bytes with this field zero
+    uint8_t reserved[256 - 116];
 };
 static_assert(sizeof(FileHeader) == 256, "header is 256 bytes");
 
@@ -68,7 +72,6 @@ static_assert(sizeof(FileHeader) == 256, "header is 256 bytes");
 // Castagnoli polynomial 0x1EDC6F41 (reflected 0x82F63B78), initial value and
 // final xor 0xFFFFFFFF.  SSE4.2 has the instruction; a table covers other hosts.
 uint32_t g_crc_table[8][256];
-bool g_crc_ready = false;
 
 void crc_init_table() {
     for (uint32_t i = 0; i < 256; ++i) {
@@ -79,11 +82,12 @@ void crc_init_table() {
     for (int t = 1; t < 8; ++t)
         for (uint32_t i = 0; i < 256; ++i)
             g_crc_table[t][i] = (g_crc_table[t - 1][i] >> 8) ^ g_crc_table[0][g_crc_table[t - 1][i] & 0xff];
-    g_crc_ready = true;
 }
 
 uint32_t crc_soft(uint32_t crc, const unsigned char* p, size_t n) {
-    if (!g_crc_ready) crc_init_table();
+    // thread-safe one-time set-up: a save's helper thread and its caller may both get here first
+    static const bool ready = (crc_init_table(), true);
+    (void)ready;
     while (n >= 8) {
         uint64_t w;
         memcpy(&w, p, 8);
@@ -230,17 +234,81 @@ struct Piece {
     uint64_t bytes;
 };
 
+// Largest shard a file may describe: three shards of 4-byte elements stay far
+// inside 64-bit byte counts.
+constexpr int64_t kMaxShard = INT64_MAX / 64;
+
 int check_info(const fsdp_ckpt_info* in) {
     if (!in) return fsdp::fail(FSDP_E_INVAL, "info is NULL");
     if (in->world < 1 || in->rank < 0 || in->rank >= in->world)
         return fsdp::fail(FSDP_E_INVAL, "world %d / rank %d out of range", in->world, in->rank);
-    if (in->numel < 0 || in->padded_numel < in->numel || in->padded_numel % in->world ||
-        in->shard_numel * (int64_t)in->world != in->padded_numel)
+    if (in->numel < 0 || in->padded_numel < in->numel || in->shard_numel < 0 || in->shard_numel > kMaxShard ||
+        in->padded_numel % in->world || in->padded_numel / in->world != in->shard_numel)
         return fsdp::fail(FSDP_E_SIZE, "inconsistent sizes: numel %lld, padded %lld, shard %lld, world %d",
                           (long long)in->numel, (long long)in->padded_numel, (long long)in->shard_numel, in->world);
     if (!fsdp::valid_dtype(in->state_dt) || !fsdp::valid_dtype(in->compute_dt))
         return fsdp::fail(FSDP_E_DTYPE, "state dtype %d / compute dtype %d unsupported", in->state_dt, in->compute_dt);
     if (in->n_tensors < 0) return fsdp::fail(FSDP_E_INVAL, "n_tensors < 0");
+    return FSDP_OK;
+}
+
+uint32_t crc32c(const void* data, uint64_t n) {
+    return n ? crc_update(0xFFFFFFFFu, data, (size_t)n) ^ 0xFFFFFFFFu : 0u;
+}
+
+// Open a shard file and check its header and size table: magic, version, the
+// header's own checksum, consistent sizes, a payload that ends the file
+// exactly, the size table's checksum and sum.  Every count read from the file
+// is bounded by the file's length before anything is allocated from it.  On
+// success the file is open in `in`, positioned after the size table.
+int read_header(const char* path, File& in, FileHeader& h, fsdp_ckpt_info& info, std::vector<int64_t>* numels_out) {
+    in.f = fopen(path, "rb");
+    if (!in.f) return fsdp::fail(FSDP_E_IO, "cannot open %s: %s", path, strerror(errno));
+    struct stat sb;
+    if (fstat(fileno(in.f), &sb) != 0) return fsdp::fail(FSDP_E_IO, "cannot stat %s: %s", path, strerror(errno));
+    const uint64_t file_bytes = (uint64_t)sb.st_size;
+    if (!read_all(in.f, &h, sizeof h)) return fsdp::fail(FSDP_E_FORMAT, "%s: truncated header", path);
+    if (memcmp(h.magic, kMagic, 8) != 0) return fsdp::fail(FSDP_E_FORMAT, "%s: not a shard file", path);
+    if (h.version != kVersion || h.header_bytes != sizeof(FileHeader))
+        return fsdp::fail(FSDP_E_FORMAT, "%s: unsupported version %u", path, h.version);
+    FileHeader z = h;
+    z.crc_header = 0;
+    if (crc32c(&z, sizeof z) != h.crc_header) return fsdp::fail(FSDP_E_FORMAT, "%s: header checksum mismatch", path);
+    memset(&info, 0, sizeof info);
+    info.world = h.world;
+    info.rank = h.rank;
+    info.numel = h.numel;
+    info.padded_numel = h.padded_numel;
+    info.shard_numel = h.shard_numel;
+    info.state_dt = (fsdp_dtype)h.state_dt;
+    info.compute_dt = (fsdp_dtype)h.compute_dt;
+    info.step = h.step;
+    info.hp.lr = h.lr;
+    info.hp.beta1 = h.beta1;
+    info.hp.beta2 = h.beta2;
+    info.hp.eps = h.eps;
+    info.hp.weight_decay = h.weight_decay;
+    info.hp.step = h.step;
+    info.n_tensors = h.n_tensors;
+    if (check_info(&info) != FSDP_OK) return fsdp::fail(FSDP_E_FORMAT, "%s: inconsistent header", path);
+    const uint64_t sbytes = (uint64_t)h.shard_numel * (uint64_t)fsdp::dt_size(h.state_dt);   // < 2^58
+    const uint64_t table_bytes = 8ull * (uint64_t)h.n_tensors;                                  // < 2^34
+    if (h.payload_bytes != 3 * sbytes || h.payload_offset % kAlign != 0 ||
+        h.payload_offset < sizeof(FileHeader) + table_bytes || h.payload_offset > file_bytes ||
+        file_bytes - h.payload_offset != h.payload_bytes)
+        return fsdp::fail(FSDP_E_FORMAT, "%s: payload layout does not match the file's %llu bytes", path,
+                          (unsigned long long)file_bytes);
+    std::vector<int64_t> numels(h.n_tensors);   // the table lies inside the file: bounded by its length
+    if (h.n_tensors && !read_all(in.f, numels.data(), table_bytes))
+        return fsdp::fail(FSDP_E_FORMAT, "%s: truncated size table", path);
+    if (crc32c(numels.data(), table_bytes) != h.crc_table)
+        return fsdp::fail(FSDP_E_FORMAT, "%s: size table checksum mismatch", path);
+    int64_t total = 0;
+    for (int64_t n : numels)
+        if (n < 0 || __builtin_add_overflow(total, n, &total))
+            return fsdp::fail(FSDP_E_FORMAT, "%s: invalid size table", path);
+    if (total != h.numel) return fsdp::fail(FSDP_E_FORMAT, "%s: size table does not sum to numel", path);
+    if (numels_out) numels_out->swap(numels);
     return FSDP_OK;
 }
 
@@ -262,7 +330,7 @@ int fsdp_save_shard(const char* path, const fsdp_ckpt_info* info, const int64_t*
     int64_t total = 0;
     for (int32_t k = 0; k < info->n_tensors; ++k) {
         if (numels[k] < 0) return fsdp::fail(FSDP_E_INVAL, "numels[%d] < 0", k);
-        total += numels[k];
+        if (__builtin_add_overflow(total, numels[k], &total)) return fsdp::fail(FSDP_E_SIZE, "tensor sizes overflow");
     }
     if (total != info->numel)
         return fsdp::fail(FSDP_E_SIZE, "tensor sizes sum to %lld, info->numel is %lld", (long long)total,
@@ -346,6 +414,8 @@ int fsdp_save_shard(const char* path, const fsdp_ckpt_info* info, const int64_t*
         }
     }
     h.crc_payload = crc ^ 0xFFFFFFFFu;
+    h.crc_header = 0;
+    h.crc_header = fsdp_crc32c(&h, sizeof h);
     if (fseek(out.f, 0, SEEK_SET) != 0 || !write_all(out.f, &h, sizeof h) || fflush(out.f) != 0 ||
         fsync(fileno(out.f)) != 0)
         return fsdp::fail(FSDP_E_IO, "finishing %s failed: %s", tmp.c_str(), strerror(errno));
@@ -359,46 +429,15 @@ int fsdp_save_shard(const char* path, const fsdp_ckpt_info* info, const int64_t*
 int fsdp_shard_info(const char* path, fsdp_ckpt_info* info_out, int64_t* numels_out, int32_t numels_capacity) {
     if (!path || !info_out) return fsdp::fail(FSDP_E_INVAL, "path and info_out must be non-NULL");
     File in;
-    in.f = fopen(path, "rb");
-    if (!in.f) return fsdp::fail(FSDP_E_IO, "cannot open %s: %s", path, strerror(errno));
     FileHeader h;
-    if (!read_all(in.f, &h, sizeof h)) return fsdp::fail(FSDP_E_FORMAT, "%s: truncated header", path);
-    if (memcmp(h.magic, kMagic, 8) != 0) return fsdp::fail(FSDP_E_FORMAT, "%s: not a shard file", path);
-    if (h.version != kVersion || h.header_bytes != sizeof(FileHeader))
-        return fsdp::fail(FSDP_E_FORMAT, "%s: unsupported version %u", path, h.version);
     fsdp_ckpt_info info;
-    memset(&info, 0, sizeof info);
-    info.world = h.world;
-    info.rank = h.rank;
-    info.numel = h.numel;
-    info.padded_numel = h.padded_numel;
-    info.shard_numel = h.shard_numel;
-    info.state_dt = (fsdp_dtype)h.state_dt;
-    info.compute_dt = (fsdp_dtype)h.compute_dt;
-    info.step = h.step;
-    info.hp.lr = h.lr;
-    info.hp.beta1 = h.beta1;
-    info.hp.beta2 = h.beta2;
-    info.hp.eps = h.eps;
-    info.hp.weight_decay = h.weight_decay;
-    info.hp.step = h.step;
-    info.n_tensors = h.n_tensors;
-    if (check_info(&info) != FSDP_OK) return fsdp::fail(FSDP_E_FORMAT, "%s: inconsistent header", path);
-    const uint64_t sbytes = (uint64_t)h.shard_numel * (uint64_t)fsdp::dt_size(h.state_dt);
-    if (h.payload_bytes != 3 * sbytes || h.payload_offset < sizeof(FileHeader) + 8ull * (uint64_t)h.n_tensors)
-        return fsdp::fail(FSDP_E_FORMAT, "%s: inconsistent payload layout", path);
-    std::vector<int64_t> numels(h.n_tensors);
-    if (h.n_tensors && !read_all(in.f, numels.data(), 8ull * h.n_tensors))
-        return fsdp::fail(FSDP_E_FORMAT, "%s: truncated size table", path);
-    if (fsdp_crc32c(numels.data(), 8ll * h.n_tensors) != h.crc_table)
-        return fsdp::fail(FSDP_E_FORMAT, "%s: size table checksum mismatch", path);
-    int64_t total = 0;
-    for (int64_t n : numels) total += n;
-    if (total != h.numel) return fsdp::fail(FSDP_E_FORMAT, "%s: size table does not sum to numel", path);
+    std::vector<int64_t> numels;
+    int rc = read_header(path, in, h, info, &numels);
+    if (rc) return rc;
     if (numels_out) {
         if (numels_capacity < h.n_tensors)
             return fsdp::fail(FSDP_E_SIZE, "%s: %d tensors, numels_capacity %d", path, h.n_tensors, numels_capacity);
-        memcpy(numels_out, numels.data(), 8ull * h.n_tensors);
+        if (h.n_tensors) memcpy(numels_out, numels.data(), 8ull * h.n_tensors);
     }
     *info_out = info;
     return fsdp::ok();
@@ -406,8 +445,11 @@ int fsdp_shard_info(const char* path, fsdp_ckpt_info* info_out, int64_t* numels_
 
 int fsdp_load_shard(const char* path, fsdp_ckpt_info* info_out, void* master, void* exp_avg, void* exp_avg_sq,
                     int64_t shard_capacity, int32_t on_device, void* stream) {
+    if (!path) return fsdp::fail(FSDP_E_INVAL, "path is NULL");
+    File in;
+    FileHeader h;
     fsdp_ckpt_info info;
-    int rc = fsdp_shard_info(path, &info, nullptr, 0);
+    int rc = read_header(path, in, h, info, nullptr);
     if (rc) return rc;
     if (info.shard_numel > shard_capacity)
         return fsdp::fail(FSDP_E_SIZE, "%s: shard of %lld elements, capacity %lld", path,
@@ -415,12 +457,7 @@ int fsdp_load_shard(const char* path, fsdp_ckpt_info* info_out, void* master, vo
     const uint64_t sbytes = (uint64_t)info.shard_numel * (uint64_t)fsdp::dt_size(info.state_dt);
     if (sbytes > 0 && (!master || !exp_avg || !exp_avg_sq))
         return fsdp::fail(FSDP_E_INVAL, "master, exp_avg and exp_avg_sq must be non-NULL");
-    File in;
-    in.f = fopen(path, "rb");
-    if (!in.f) return fsdp::fail(FSDP_E_IO, "cannot open %s: %s", path, strerror(errno));
-    FileHeader h;
-    if (!read_all(in.f, &h, sizeof h) || fseek(in.f, (long)h.payload_offset, SEEK_SET) != 0)
-        return fsdp::fail(FSDP_E_FORMAT, "%s: truncated", path);
+    if (fseeko(in.f, (off_t)h.payload_offset, SEEK_SET) != 0) return fsdp::fail(FSDP_E_FORMAT, "%s: truncated", path);
     const Piece pieces[3] = {{nullptr, (char*)master, sbytes},
                              {nullptr, (char*)exp_avg, sbytes},
                              {nullptr, (char*)exp_avg_sq, sbytes}};

@@ -149,3 +149,72 @@ def test_argument_errors(tmp_path):
                              None, None, None, 0, None) == N.E_SIZE                # sizes do not sum to numel
     assert L.fsdp_save_shard(str(tmp_path / "no" / "dir" / "x").encode(), ctypes.byref(info),
                              N.i64_array([10]), None, None, None, 0, None) in (N.E_INVAL, N.E_IO)
+
+
+def test_every_header_and_table_byte_is_checked(tmp_path):
+    """A flipped bit anywhere in the 256-byte header (its own checksum covers
+    it) or the size table makes the file unreadable, never a silently different
+    step, hyper-parameter or size; bytes of the unused gap between the table and
+    the 4096-aligned payload change nothing.  Runs through both the header query
+    and the load."""
+    path, S = _save(tmp_path, S=2053)
+    raw = bytearray(open(path, "rb").read())
+    table_end = 256 + 8 * 1
+    for where in list(range(0, table_end)) + [table_end, 1000, 4095]:
+        for bit in (0x01, 0x80):
+            bad = bytearray(raw)
+            bad[where] ^= bit
+            open(path, "wb").write(bad)
+            code = _load_code(path, S)
+            if where < table_end:
+                assert code == N.E_FORMAT, (where, bit)
+                with pytest.raises(ss.FsdpError) as e:
+                    ss.shard_info(path)
+                assert e.value.code == N.E_FORMAT
+            else:
+                assert code == 0, (where, bit)      # padding before the payload is not data
+    open(path, "wb").write(raw)
+    assert _load_code(path, S) == 0
+
+
+def test_payload_flips_and_truncations_at_every_boundary(tmp_path):
+    """Payload flips (first, middle and last byte of each of the three state
+    shards) fail the payload checksum; a file cut at any length short of the
+    whole, or with bytes appended, fails before anything is read into the
+    destinations' full size."""
+    path, S = _save(tmp_path, S=1031)
+    raw = bytes(open(path, "rb").read())
+    sb = 4 * S
+    for k in range(3):
+        for off in (0, sb // 2, sb - 1):
+            bad = bytearray(raw)
+            bad[4096 + k * sb + off] ^= 0x04
+            open(path, "wb").write(bad)
+            assert _load_code(path, S) == N.E_FORMAT, (k, off)
+    cuts = sorted(set(list(range(0, 300, 7)) + [255, 256, 257, 263, 264, 265, 4095, 4096, 4097, 4096 + sb,
+                                                  4096 + 2 * sb + 1, len(raw) - 8, len(raw) - 1]))
+    for n in cuts:
+        open(path, "wb").write(raw[:n])
+        assert _load_code(path, S) == N.E_FORMAT, n
+    open(path, "wb").write(raw + b"\0" * 8)
+    assert _load_code(path, S) == N.E_FORMAT
+    open(path, "wb").write(raw)
+    assert _load_code(path, S) == 0
+
+
+def test_a_consistently_forged_header_cannot_make_the_reader_allocate(tmp_path):
+    """A header rewritten with a huge tensor count and a matching header
+    checksum still fails: the table must lie inside the file."""
+    import struct
+    path, S = _save(tmp_path, S=515)
+    raw = bytearray(open(path, "rb").read())
+    # n_tensors sits after the five hyper-parameter floats; recompute the header's checksum
+    off = 8 + 4 + 4 + 4 + 4 + 8 * 3 + 4 + 4 + 8 + 4 * 5
+    for n in (1 << 30, (1 << 31) - 1):
+        bad = bytearray(raw)
+        bad[off:off + 4] = struct.pack("<i", n)
+        bad[112:116] = b"\0\0\0\0"
+        bad[112:116] = struct.pack("<I", _crc(bytes(bad[:256])))
+        open(path, "wb").write(bad)
+        assert _load_code(path, S) == N.E_FORMAT, n
+        assert "payload layout" in N.lib().fsdp_last_error().decode()
