@@ -56,11 +56,15 @@ extern "C" {
 /* Bytes of the device scratch of fsdp_offload_step_units_noalloc (per device). */
 #define FSDP_OFFLOAD_SCRATCH_BYTES (32 << 20)
 
-typedef enum fsdp_dtype {
+/* Element formats.  A plain 32-bit integer rather than an enum type, so that
+ * any value a caller passes is well defined; values other than these three
+ * are refused with FSDP_E_DTYPE. */
+typedef int32_t fsdp_dtype;
+enum {
     FSDP_F32 = 0,   /* IEEE binary32 */
     FSDP_F16 = 1,   /* IEEE binary16 */
     FSDP_BF16 = 2   /* bfloat16 */
-} fsdp_dtype;
+};
 
 enum {
     FSDP_OK = 0,
@@ -285,12 +289,14 @@ FSDP_API int fsdp_step_units(const fsdp_unit* units, int32_t n_units, int32_t wo
  *                        (state: exp_avg = v, exp_avg_sq = acc)
  *   AdamW:               as fsdp_sharded_adamw (exp_avg = m, exp_avg_sq = v)
  * ------------------------------------------------------------------------ */
-typedef enum fsdp_optimizer {
+/* A 32-bit integer for the same reason as fsdp_dtype (others: FSDP_E_INVAL). */
+typedef int32_t fsdp_optimizer;
+enum {
     FSDP_OPT_ADAMW = 0,
     FSDP_OPT_SGD = 1,
     FSDP_OPT_ADAMAX = 2,
     FSDP_OPT_ADADELTA = 3
-} fsdp_optimizer;
+};
 
 typedef struct fsdp_optim_hp {
     fsdp_optimizer kind;
