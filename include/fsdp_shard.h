@@ -436,10 +436,13 @@ FSDP_API int fsdp_offload_step_units(const fsdp_offload_unit* units, int32_t n_u
  * otherwise, before anything is enqueued.  Its first call on a device, with
  * that device current, looks up the scratch's device address and creates 258
  * events for that device; later calls call no hipMalloc, hipFree, event or
- * stream creation (host-side bookkeeping uses the C++ heap).  Calls that
- * overlap in time on one device (two host threads, or two streams before the
- * first call has returned) share the scratch and race; calls on different
- * devices do not. */
+ * stream creation (host-side bookkeeping uses the C++ heap).  Every call on a
+ * device uses that device's one scratch, which keeps the previous call's bytes
+ * (each chunk is written whole before it is read, so nothing needs clearing);
+ * calls that overlapped in time on one device would race on it, so the library
+ * serializes them with a per-device lock held for the whole call (the call
+ * returns only after every copy out of the scratch has landed).  Calls on
+ * different devices run independently. */
 FSDP_API int fsdp_offload_step_units_noalloc(const fsdp_offload_unit* units, int32_t n_units, int32_t world,
                                              int32_t rank, fsdp_dtype grad_dt, int32_t fp32_reduce,
                                              fsdp_dtype compute_dt, int64_t chunk_numel, const fsdp_adamw_hp* hp,

@@ -262,14 +262,17 @@ def _reissue(fn, name, args, hp, stream, device):
     the call on `stream`, else on the stream given when it was prepared, else
     on the device's current stream at the time of the call."""
     args = list(args)
-    bound = _stream(stream, device) if stream is not None else None
+    bound = _stream(stream, device) if stream is not None else None   # the null stream's handle is 0
 
     def call(step=None, stream=None):
         if step is not None:
             if int(step) < 1:
                 raise ValueError("step must be >= 1, got %d" % int(step))
             hp.step = int(step)
-        args[-1] = _stream(stream, device) if stream is not None else (bound or _stream(None, device))
+        if stream is not None:
+            args[-1] = _stream(stream, device)
+        else:
+            args[-1] = bound if bound is not None else _stream(None, device)
         with torch.cuda.device(device):
             check(name, fn(*args))
 

@@ -335,6 +335,7 @@ constexpr int kScratchEvents = 256;
 constexpr int kMaxDevices = 64;
 struct ScratchDevice {
     std::once_flag once;
+    std::mutex mu;   // held for a whole call: calls on one device take the scratch in turn
     hipError_t err = hipSuccess;
     void* ptr = nullptr;
     hipEvent_t ev[kScratchEvents + 2] = {};
@@ -418,10 +419,15 @@ int offload_units(const fsdp_offload_unit* units, int32_t n_units, int32_t world
     std::vector<hipEvent_t> ready(chunks.size(), nullptr);
     hipEvent_t entry = nullptr, done = nullptr;
     ScratchDevice* sd = nullptr;
+    std::unique_lock<std::mutex> scratch_lock;
     if (use_scratch) {
-        // the device's scratch and its events: nothing is created after set-up
+        // the device's scratch and its events: nothing is created after set-up.  The
+        // lock is held until this call returns, by which time every chunk's copy out
+        // of the scratch has landed (the host work waited for each), so a call from
+        // another thread never finds the scratch or the events in use.
         rc = scratch_setup(&sd);
         if (rc) return rc;
+        scratch_lock = std::unique_lock<std::mutex>(sd->mu);
         for (size_t c = 0; c < chunks.size(); ++c) ready[c] = sd->ev[c % kScratchEvents];
         if (cst != st) {
             entry = sd->ev[kScratchEvents];

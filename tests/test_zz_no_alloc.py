@@ -95,3 +95,49 @@ def test_noalloc_offload_refuses_oversized_chunks_and_a_device_gradient_shard():
                                            stream, None)
     assert rc == N.E_INVAL and "grad_shard_dev must be NULL" in L.fsdp_last_error().decode()
     torch.cuda.synchronize()
+
+
+def test_noalloc_offload_calls_from_two_threads_take_the_scratch_in_turn():
+    """Two host threads call the no-allocation step on one device at once, on
+    two streams, with different units: the library's per-device lock serializes
+    them, so each gets the same bytes as the allocating entry point."""
+    import threading
+    L = N.lib()
+    hp = N.AdamWHP(step=3)
+    world, rank, gdt, fp32r, cdt = 2, 1, "bf16", False, "bf16"
+    avg_dt = DT[gdt]
+    jobs = []
+    for t in range(2):
+        S = 2_000_003 + 5 * t
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(50 + t)
+        grads = [(torch.randn(world * S, device="cuda", generator=gen) * 1e-3).to(DT[gdt]) for _ in range(world)]
+        gp = N.ptr_array([g.data_ptr() for g in grads])
+        ref = _state(S, 60 + t, avg_dt, DT[cdt], True)
+        got = _state(S, 60 + t, avg_dt, DT[cdt], False)
+        jobs.append(dict(S=S, grads=grads, gp=gp, ref=ref, got=got, stream=torch.cuda.Stream()))
+    stream0 = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for j in jobs:
+        N.check("fsdp_offload_step_units", L.fsdp_offload_step_units(
+            _table([j["ref"]], [j["gp"]]), 1, world, rank, ss.dtype_code(DT[gdt]), int(fp32r), ss.dtype_code(DT[cdt]),
+            65536, ctypes.byref(hp), 4, stream0, None))
+    torch.cuda.synchronize()
+    rcs = [None, None]
+
+    def run(k):
+        j = jobs[k]
+        with torch.cuda.device(0):
+            rcs[k] = L.fsdp_offload_step_units_noalloc(
+                _table([j["got"]], [j["gp"]]), 1, world, rank, ss.dtype_code(DT[gdt]), int(fp32r),
+                ss.dtype_code(DT[cdt]), 65536, ctypes.byref(hp), 4, ctypes.c_void_p(j["stream"].cuda_stream), None)
+
+    threads = [threading.Thread(target=run, args=(k,)) for k in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert rcs == [N.OK, N.OK], rcs
+    for k, j in enumerate(jobs):
+        for key in ("master", "exp_avg", "exp_avg_sq", "grad_host", "compute_host", "compute_dev"):
+            assert_bits_equal(np_of(j["got"][key]), np_of(j["ref"][key]), "thread %d %s" % (k, key))
