@@ -271,3 +271,16 @@ def assert_bits_equal(got, ref, what):
         bad = np.nonzero(a != b)[0]
         raise AssertionError("%s: %d of %d differ, first at %d: 0x%x vs 0x%x"
                              % (what, bad.size, a.size, bad[0], int(a[bad[0]]), int(b[bad[0]])))
+
+
+def oracle_chunks(S, fn, threads=None):
+    """fn(lo, hi) over disjoint chunks of [0, S) on several host threads (the
+    oracle's C calls run outside the GIL; every step here is pointwise, so the
+    chunking changes no value)."""
+    from concurrent.futures import ThreadPoolExecutor
+    oracle.lib()
+    threads = threads or host_threads()
+    parts = max(1, min(S // 4096, 4 * threads)) if S else 0
+    bounds = [S * k // parts for k in range(parts + 1)] if parts else [0]
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda k: fn(bounds[k], bounds[k + 1]), range(parts)))

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import sharded_state_amd as ss
-from parity import UnitRun, assert_bitexact, assert_rel, compare_compute, np_of
+from parity import assert_bits_equal, oracle_rank_step_threaded, UnitRun, assert_bitexact, assert_rel, compare_compute, np_of
 from workloads import CONFIGS, gpt_block, llama_block, rank_grad, scaled
 
 pytestmark = pytest.mark.gpu
@@ -135,10 +135,11 @@ def test_offload_two_steps_then_device_step_agree():
     assert_bitexact(np_of(co), np_of(cd), "compute")
 
 
-def test_offload_full_size_70b_block_sampled():
+def test_offload_full_size_70b_block_every_element():
     """The 70B-shaped block at full size, rank 0 and rank 7, offloaded with the
-    default 8 Mi-element chunks and 16 threads; sampled elements against the
-    oracle, the whole compute shard against the host master's rounding."""
+    default chunks and 16 threads: every element of the host master, m and v
+    and of the device compute shard against the oracle (run over disjoint
+    chunks on all host threads)."""
     cfg = CONFIGS["llama70b-block"]
     world = cfg.world
     P, Pp, S = ss.fsdp_layout(cfg.numels, world)
@@ -150,22 +151,16 @@ def test_offload_full_size_70b_block_sampled():
         print("rank", r, flush=True)
         master = (torch.randn(S, device="cuda", generator=g) * 0.02)
         st = ss.OffloadState(master, grads[0].dtype, cfg.fp32_reduce, torch.bfloat16, "cuda")
-        p0 = np_of(st.master)
+        p, m, v = np_of(st.master), np.zeros(S, np.float32), np.zeros(S, np.float32)
+        gs = [np_of(x[r * S:(r + 1) * S]) for x in grads]
         out = torch.empty(S, dtype=torch.bfloat16, device="cuda")
         st.step(grads, r, ss.AdamWHP(), out)
         torch.cuda.synchronize()
-        rng = np.random.default_rng(r)
-        idx = np.unique(np.concatenate([np.arange(4096), np.arange(S - 4096, S), rng.integers(0, S, 100_000)]))
-        pos = torch.from_numpy(r * S + idx).cuda()
-        gs = [np_of(x[pos]) for x in grads]
-        avg = oracle.grad_average(gs, 0, idx.size, "bf16", cfg.fp32_reduce)
-        g32 = avg if avg.dtype == np.float32 else oracle.to_f32(avg, "bf16")
-        p, m, v = p0[idx].copy(), np.zeros(idx.size, np.float32), np.zeros(idx.size, np.float32)
-        oracle.adamw(p, m, v, g32, h)
-        assert_bitexact(np_of(st.master)[idx], p, "master rank %d" % r)
-        assert_bitexact(np_of(st.exp_avg)[idx], m, "exp_avg rank %d" % r)
-        assert_bitexact(np_of(st.exp_avg_sq)[idx], v, "exp_avg_sq rank %d" % r)
-        assert_bitexact(np_of(out), oracle.cast(np_of(st.master), "bf16"), "compute shard rank %d" % r)
+        _, comp = oracle_rank_step_threaded(gs, p, m, v, h, "bf16", cfg.fp32_reduce, "bf16")
+        assert_bits_equal(np_of(st.master), p, "master rank %d" % r)
+        assert_bits_equal(np_of(st.exp_avg), m, "exp_avg rank %d" % r)
+        assert_bits_equal(np_of(st.exp_avg_sq), v, "exp_avg_sq rank %d" % r)
+        assert_bits_equal(np_of(out), comp, "compute shard rank %d" % r)
         del st
 
 

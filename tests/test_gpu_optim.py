@@ -7,7 +7,7 @@ and without the fused all-gather; the oracle runs the same steps.  Parameter,
 state and compute copy must match bit for bit (the bar for fp32 outputs is
 1e-6 relative, for 16-bit outputs 1 ulp; the arithmetic is the same operation
 sequence, so the result is exact).  State buffers an optimizer does not keep
-are never touched.  At full size, sampled outputs of rank 0 are checked.
+are never touched.  At full size, every output element of rank 0 is checked.
 """
 import numpy as np
 import pytest
@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import sharded_state_amd as ss
-from parity import assert_bitexact, assert_rel, compare_compute, dt_name, np_of
+from parity import assert_bits_equal, oracle_chunks, assert_bitexact, assert_rel, compare_compute, dt_name, np_of
 from workloads import CONFIGS, TORCH_DTYPE, gpt_block, llama_block, moments, param_tensors, rank_grad, scaled
 
 pytestmark = pytest.mark.gpu
@@ -149,10 +149,11 @@ def test_batch_of_units_matches_single_units():
 
 @pytest.mark.parametrize("opt,name", [("adadelta", "llama70b-block"), ("sgd-nesterov", "gpt3-13b-block"),
                                       ("adamax", "gpt2-xl-model")])
-def test_full_size_sampled(opt, name):
+def test_full_size_every_element(opt, name):
     """Rank 0 of the full-size unit with the fused gather, step 2 from the
-    workload's state: sampled outputs against the oracle, the gather's peer
-    slots against the peer shards."""
+    workload's state: every element of the parameter and state shards and of
+    the full buffer against the oracle (run over disjoint chunks on all host
+    threads)."""
     print("case", opt, name, "full size", flush=True)
     cfg = CONFIGS[name]
     hp = OPTS[opt].at_step(2)
@@ -166,24 +167,26 @@ def test_full_size_sampled(opt, name):
     v = (torch.randn(S, device="cuda", generator=g) * 1e-6).abs()
     grads = [rank_grad(cfg, 0, q, Pp, "cuda") for q in range(world)]
     peers = [(torch.randn(S, device="cuda", generator=g) * 0.02).to(cdt) for _ in range(world)]
-    rng = np.random.default_rng(0)
-    idx = np.unique(np.concatenate([np.arange(4096), np.arange(S - 4096, S), rng.integers(0, S, 100_000)]))
-    sel = torch.from_numpy(idx).cuda()
-    gs = [np_of(x[sel]) for x in grads]
-    p0, m0, v0 = np_of(master[sel]), np_of(m[sel]), np_of(v[sel])
+    gs = [np_of(x[:S]) for x in grads]
+    p0, m0, v0 = np_of(master), np_of(m), np_of(v)
     full = torch.empty(world * S, dtype=cdt, device="cuda")
     ss.fsdp_step_units([dict(master=master, exp_avg=m, exp_avg_sq=v, rank_grads=grads, full=full,
                              peer_shards=[None] + peers[1:])], 0, cfg.fp32_reduce, hp)
     torch.cuda.synchronize()
-    avg = oracle.grad_average(gs, 0, idx.size, cfg.grad_dt, cfg.fp32_reduce)
-    g32 = avg if avg.dtype == np.float32 else oracle.to_f32(avg, cfg.grad_dt)
     kind, o = orc_opt(hp, 2)
-    oracle.opt_step(kind, p0, m0, v0, g32, o)
-    assert_bitexact(np_of(master[sel]), p0, "param")
+    comp = np.empty(S, dtype=np.uint16 if cfg.compute_dt != "f32" else np.float32)
+
+    def step(lo, hi):
+        avg = oracle.grad_average(gs, lo, hi - lo, cfg.grad_dt, cfg.fp32_reduce)
+        g32 = avg if avg.dtype == np.float32 else oracle.to_f32(avg, cfg.grad_dt)
+        oracle.opt_step(kind, p0[lo:hi], m0[lo:hi], v0[lo:hi], g32, o)
+        comp[lo:hi] = oracle.cast(p0[lo:hi], cfg.compute_dt)
+
+    oracle_chunks(S, step)
+    assert_bits_equal(np_of(master), p0, "param")
     if hp.n_states >= 1:
-        assert_bitexact(np_of(m[sel]), m0, "state 1")
+        assert_bits_equal(np_of(m), m0, "state 1")
     if hp.n_states >= 2:
-        assert_bitexact(np_of(v[sel]), v0, "state 2")
-    assert_bitexact(np_of(full[sel]), oracle.cast(p0, cfg.compute_dt), "own slot")
-    for q in range(1, world):
-        assert torch.equal(full[q * S:(q + 1) * S].view(torch.int16), peers[q].view(torch.int16)), q
+        assert_bits_equal(np_of(v), v0, "state 2")
+    ref = oracle.gather([comp] + [np_of(x) for x in peers[1:]], cfg.compute_dt)
+    assert_bits_equal(np_of(full), ref, "full buffer")

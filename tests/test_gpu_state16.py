@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import sharded_state_amd as ss
-from parity import assert_bitexact, assert_ulp16, dt_name, np_of
+from parity import assert_bits_equal, oracle_chunks, assert_bitexact, assert_ulp16, dt_name, np_of
 from workloads import CONFIGS, TORCH_DTYPE, gpt_block, llama_block, moments, param_tensors, rank_grad, scaled
 
 pytestmark = pytest.mark.gpu
@@ -87,10 +87,11 @@ def test_state16_later_step_and_odd_world():
     _run(scaled(CONFIGS["llama70b-block"], gpt_block(40), world=3), "bf16", step=100, block=3)
 
 
-def test_state16_full_size_70b_block_sampled():
+def test_state16_full_size_70b_block_every_element():
     """The 70B-shaped block at full size with bf16 state, rank 0 and rank 7,
-    through the batched unit step with the fused gather; sampled outputs
-    against the oracle, the gather against the updated shards."""
+    through the batched unit step with the fused gather: every element of the
+    parameter, m and v shards and of the full buffer against the oracle (run
+    over disjoint chunks on all host threads)."""
     cfg = CONFIGS["llama70b-block"]
     world = cfg.world
     P, Pp, S = ss.fsdp_layout(cfg.numels, world)
@@ -106,24 +107,23 @@ def test_state16_full_size_70b_block_sampled():
     peers = [(torch.randn(S, device="cuda", generator=g) * 0.02).to(sd) for _ in range(world)]
     h = oracle.hp()
     for r in (0, world - 1):
-        rng = np.random.default_rng(r)
-        idx = np.unique(np.concatenate([np.arange(4096), np.arange(S - 4096, S), rng.integers(0, S, 100_000)]))
-        sel = torch.from_numpy(idx).cuda()
-        pos = torch.from_numpy(r * S + idx).cuda()
-        gs = [np_of(x[pos]) for x in grads]
-        p0, m0, v0 = np_of(flat[pos]), np_of(m[pos]), np_of(v[pos])
+        print("rank", r, flush=True)
         sl = slice(r * S, (r + 1) * S)
+        gs = [np_of(x[sl]) for x in grads]
+        p0, m0, v0 = np_of(flat[sl]), np_of(m[sl]), np_of(v[sl])
         full = torch.empty(world * S, dtype=sd, device="cuda")
         u = dict(master=flat[sl], exp_avg=m[sl], exp_avg_sq=v[sl], rank_grads=grads,
                  peer_shards=[None if q == r else peers[q] for q in range(world)], full=full)
         ss.fsdp_step_units([u], r, cfg.fp32_reduce, hp)
         torch.cuda.synchronize()
-        avg = oracle.grad_average(gs, 0, idx.size, "bf16", False)
-        oracle.adamw16(p0, m0, v0, oracle.to_f32(avg, "bf16"), h, "bf16")
-        assert_bitexact(np_of(flat[sl][sel]), p0, "param rank %d" % r)
-        assert_bitexact(np_of(m[sl][sel]), m0, "exp_avg rank %d" % r)
-        assert_bitexact(np_of(v[sl][sel]), v0, "exp_avg_sq rank %d" % r)
-        assert torch.equal(full[r * S:(r + 1) * S].view(torch.int16), flat[sl].view(torch.int16))
-        for q in range(world):
-            if q != r:
-                assert torch.equal(full[q * S:(q + 1) * S].view(torch.int16), peers[q].view(torch.int16))
+
+        def step(lo, hi):
+            avg = oracle.grad_average(gs, lo, hi - lo, "bf16", False)
+            oracle.adamw16(p0[lo:hi], m0[lo:hi], v0[lo:hi], oracle.to_f32(avg, "bf16"), h, "bf16")
+
+        oracle_chunks(S, step)
+        assert_bits_equal(np_of(flat[sl]), p0, "param rank %d" % r)
+        assert_bits_equal(np_of(m[sl]), m0, "exp_avg rank %d" % r)
+        assert_bits_equal(np_of(v[sl]), v0, "exp_avg_sq rank %d" % r)
+        ref = oracle.gather([p0 if q == r else np_of(peers[q]) for q in range(world)], "bf16")
+        assert_bits_equal(np_of(full), ref, "full buffer rank %d" % r)
