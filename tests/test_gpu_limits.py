@@ -3,8 +3,7 @@
 * world = FSDP_MAX_WORLD (128) simulated ranks through the generic kernel, with
   the fused all-gather (127 peer copies) and through the separate reduce-scatter;
 * a shard of more than 2**31 elements (64-bit element indexing end to end:
-  tile numbers, vector and byte offsets), sampled against the oracle, with the
-  last elements and the elements around 2**31 always in the sample.
+  tile numbers, vector and byte offsets), every element against the oracle.
 """
 import numpy as np
 import pytest
@@ -12,7 +11,7 @@ import torch
 
 import oracle
 import sharded_state_amd as ss
-from parity import assert_bitexact, np_of
+from parity import assert_bitexact, assert_bits_equal, np_of, oracle_chunks
 from sharded_state_amd import _native as N
 
 pytestmark = pytest.mark.gpu
@@ -76,20 +75,23 @@ def test_shard_of_more_than_2_31_elements():
         master[lo:hi] = torch.randn(hi - lo, device="cuda", generator=g) * 0.02
     m = torch.zeros(S, device="cuda")
     v = torch.zeros(S, device="cuda")
-    rng = np.random.default_rng(0)
-    two31 = 1 << 31
-    idx = np.unique(np.concatenate([np.arange(2048), np.arange(two31 - 2048, two31 + 2048),
-                                    np.arange(S - 4096, S), rng.integers(0, S, 200_000)]))
-    sel = torch.from_numpy(idx).cuda()
-    g0, p0 = np_of(grad[sel]), np_of(master[sel])
+    g0, pm = np_of(grad), np_of(master)
     full = torch.empty(S, dtype=torch.bfloat16, device="cuda")
     ss.fsdp_step_units([dict(master=master, exp_avg=m, exp_avg_sq=v, rank_grads=[grad], full=full,
                              peer_shards=[None])], 0, True, ss.AdamWHP(step=1))
     torch.cuda.synchronize()
+    print("step done; oracle on every element", flush=True)
     h = oracle.hp(step=1)
-    pm, mm, vm = p0.copy(), np.zeros(idx.size, np.float32), np.zeros(idx.size, np.float32)
-    oracle.adamw(pm, mm, vm, oracle.to_f32(g0, "f16"), h)
-    assert_bitexact(np_of(master[sel]), pm, "master")
-    assert_bitexact(np_of(m[sel]), mm, "exp_avg")
-    assert_bitexact(np_of(v[sel]), vm, "exp_avg_sq")
-    assert_bitexact(np_of(full[sel]), oracle.cast(pm, "bf16"), "compute copy in the full buffer")
+    mm, vm = np.zeros(S, np.float32), np.zeros(S, np.float32)
+    comp = np.empty(S, np.uint16)
+
+    def step(lo, hi):
+        oracle.adamw(pm[lo:hi], mm[lo:hi], vm[lo:hi], oracle.to_f32(g0[lo:hi], "f16"), h)
+        comp[lo:hi] = oracle.cast(pm[lo:hi], "bf16")
+
+    oracle_chunks(S, step)
+    del g0
+    assert_bits_equal(np_of(master), pm, "master")
+    assert_bits_equal(np_of(m), mm, "exp_avg")
+    assert_bits_equal(np_of(v), vm, "exp_avg_sq")
+    assert_bits_equal(np_of(full), comp, "compute copy in the full buffer")

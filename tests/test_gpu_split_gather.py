@@ -136,38 +136,33 @@ def test_one_call_with_a_split_launch_and_a_fused_launch():
 
 def test_unit_above_the_launch_cap_is_stepped_in_slices():
     """A shard of 2^26 + 1003 elements is stepped as a 2^26-element slice and a
-    ragged remainder, each a launch (with its peers' copies); sampled outputs
-    around the slice boundary, at both ends and at random positions match the
-    oracle bit for bit, and the peers' slots are whole."""
+    ragged remainder, each a launch (with its peers' copies); every element of
+    master, m, v and the full buffer matches the oracle bit for bit."""
     import numpy as np
     import oracle
-    from parity import assert_bitexact
+    from parity import assert_bits_equal, oracle_rank_step_threaded
     world, rank = 2, 0
     S = (1 << 26) + 1003
     assert ss.units_in_launch(world, [S]) == (1, 1 << 26)
     u = _units(world, rank, [S], torch.float16, torch.float16, 31)[0]
-    idx = np.unique(np.concatenate([np.arange(600), np.arange((1 << 26) - 600, (1 << 26) + 600),
-                                    np.arange(S - 600, S), np.random.default_rng(3).integers(0, S, 5000)]))
-    sel = torch.from_numpy(idx).cuda()
-    gs = [np_of(g[sel]) for g in u["rank_grads"]]          # rank 0's block is the first S elements
-    p, m, v = (np_of(u[k][sel]) for k in ("master", "exp_avg", "exp_avg_sq"))
+    gs = [np_of(g[:S]) for g in u["rank_grads"]]              # rank 0's block is the first S elements
+    p, m, v = (np_of(u[k]) for k in ("master", "exp_avg", "exp_avg_sq"))
     h = oracle.hp(1e-3, 0.9, 0.999, 1e-8, 0.01, 2)
     ss.fsdp_step_units([u], rank, True, ss.AdamWHP(1e-3, 0.9, 0.999, 1e-8, 0.01, 2))
     torch.cuda.synchronize()
-    _, comp = oracle.elementwise_step(gs, p, m, v, h, "f16", True, "f16")
-    assert_bitexact(np_of(u["master"][sel]), p, "master")
-    assert_bitexact(np_of(u["exp_avg"][sel]), m, "exp_avg")
-    assert_bitexact(np_of(u["exp_avg_sq"][sel]), v, "exp_avg_sq")
-    assert_bitexact(np_of(u["full"][:S][sel]), comp, "own slot")
-    assert torch.equal(_bits(u["full"][S:]), _bits(u["peer_shards"][1]))
+    _, comp = oracle_rank_step_threaded(gs, p, m, v, h, "f16", True, "f16")
+    assert_bits_equal(np_of(u["master"]), p, "master")
+    assert_bits_equal(np_of(u["exp_avg"]), m, "exp_avg")
+    assert_bits_equal(np_of(u["exp_avg_sq"]), v, "exp_avg_sq")
+    assert_bits_equal(np_of(u["full"]), np.concatenate([comp, np_of(u["peer_shards"][1])]), "full buffer")
 
 
 def test_sixteen_bit_state_unit_above_the_launch_cap():
     """The same slicing with bf16 parameter, m and v (the copies in the step's
-    trip): sampled outputs match the oracle's 16-bit AdamW bit for bit."""
+    trip): every element matches the oracle's 16-bit AdamW bit for bit."""
     import numpy as np
     import oracle
-    from parity import assert_bitexact
+    from parity import assert_bits_equal, oracle_chunks
     world, rank = 2, 1
     S = (1 << 26) + 517
     g = torch.Generator(device="cuda")
@@ -179,20 +174,21 @@ def test_sixteen_bit_state_unit_above_the_launch_cap():
              exp_avg_sq=(torch.rand(S, device="cuda", generator=g) * 1e-6).to(bf), rank_grads=grads,
              peer_shards=[(torch.randn(S, device="cuda", generator=g) * 0.02).to(bf), None],
              full=torch.empty(world * S, dtype=bf, device="cuda"))
-    idx = np.unique(np.concatenate([np.arange(300), np.arange((1 << 26) - 300, (1 << 26) + 300),
-                                    np.arange(S - 300, S), np.random.default_rng(4).integers(0, S, 5000)]))
-    sel = torch.from_numpy(idx).cuda()
-    gs = [np_of(x[rank * S:(rank + 1) * S][sel]) for x in grads]
-    p, m, v = (np_of(u[k][sel]) for k in ("master", "exp_avg", "exp_avg_sq"))
+    gs = [np_of(x[rank * S:(rank + 1) * S]) for x in grads]
+    p, m, v = (np_of(u[k]) for k in ("master", "exp_avg", "exp_avg_sq"))
     ss.fsdp_step_units([u], rank, True, ss.AdamWHP(1e-3, 0.9, 0.999, 1e-8, 0.01, 3))
     torch.cuda.synchronize()
-    avg = oracle.grad_average(gs, 0, idx.size, "f16", True)
-    oracle.adamw16(p, m, v, avg, oracle.hp(1e-3, 0.9, 0.999, 1e-8, 0.01, 3), "bf16")
-    assert_bitexact(np_of(u["master"][sel]), p, "parameter")
-    assert_bitexact(np_of(u["exp_avg"][sel]), m, "exp_avg")
-    assert_bitexact(np_of(u["exp_avg_sq"][sel]), v, "exp_avg_sq")
-    assert_bitexact(np_of(u["full"][rank * S:][sel]), p, "own slot")
-    assert torch.equal(_bits(u["full"][:S]), _bits(u["peer_shards"][0]))
+    h = oracle.hp(1e-3, 0.9, 0.999, 1e-8, 0.01, 3)
+
+    def step(lo, hi):
+        avg = oracle.grad_average(gs, lo, hi - lo, "f16", True)
+        oracle.adamw16(p[lo:hi], m[lo:hi], v[lo:hi], avg, h, "bf16")
+
+    oracle_chunks(S, step)
+    assert_bits_equal(np_of(u["master"]), p, "parameter")
+    assert_bits_equal(np_of(u["exp_avg"]), m, "exp_avg")
+    assert_bits_equal(np_of(u["exp_avg_sq"]), v, "exp_avg_sq")
+    assert_bits_equal(np_of(u["full"]), np.concatenate([np_of(u["peer_shards"][0]), p]), "full buffer")
 
 
 @pytest.mark.parametrize("opt", ["sgd", "sgd-momentum"])
@@ -200,10 +196,10 @@ def test_stateless_and_one_state_optimizers_above_the_launch_cap(opt):
     """SGD without momentum keeps no state (exp_avg and exp_avg_sq are NULL) and
     its copies in the step's trip; with momentum it keeps one buffer and splits
     them out.  A shard above 2^26 elements is stepped in slices either way and
-    matches the oracle on sampled elements."""
+    matches the oracle on every element."""
     import numpy as np
     import oracle
-    from parity import assert_bitexact
+    from parity import assert_bits_equal, oracle_chunks
     world, rank = 2, 0
     S = (1 << 26) + 77
     momentum = 0.9 if opt == "sgd-momentum" else 0.0
@@ -213,19 +209,21 @@ def test_stateless_and_one_state_optimizers_above_the_launch_cap(opt):
         u["exp_avg"] = u["exp_avg_sq"] = None
     else:
         u["exp_avg_sq"] = None
-    idx = np.unique(np.concatenate([np.arange(200), np.arange((1 << 26) - 200, (1 << 26) + 77),
-                                    np.random.default_rng(5).integers(0, S, 3000)]))
-    sel = torch.from_numpy(idx).cuda()
-    gs = [np_of(g[sel]) for g in u["rank_grads"]]
-    p = np_of(u["master"][sel])
-    buf = np_of(u["exp_avg"][sel]) if momentum else np.zeros(idx.size, np.float32)
+    gs = [np_of(g[:S]) for g in u["rank_grads"]]
+    p = np_of(u["master"])
+    buf = np_of(u["exp_avg"]) if momentum else None
     ss.fsdp_step_units([u], rank, True, hp)
     torch.cuda.synchronize()
-    g32 = oracle.grad_average(gs, 0, idx.size, "f16", True)
     o = oracle.opt("sgd", step=2, lr=1e-2, momentum=momentum, weight_decay=1e-4)
-    oracle.sgd(p, buf, g32, o)
-    assert_bitexact(np_of(u["master"][sel]), p, "master")
+    comp = np.empty(S, np.uint16)
+
+    def step(lo, hi):
+        g32 = oracle.grad_average(gs, lo, hi - lo, "f16", True)
+        oracle.sgd(p[lo:hi], buf[lo:hi] if momentum else None, g32, o)
+        comp[lo:hi] = oracle.cast(p[lo:hi], "f16")
+
+    oracle_chunks(S, step)
+    assert_bits_equal(np_of(u["master"]), p, "master")
     if momentum:
-        assert_bitexact(np_of(u["exp_avg"][sel]), buf, "momentum buffer")
-    assert_bitexact(np_of(u["full"][:S][sel]), oracle.cast(p, "f16"), "own slot")
-    assert torch.equal(_bits(u["full"][S:]), _bits(u["peer_shards"][1]))
+        assert_bits_equal(np_of(u["exp_avg"]), buf, "momentum buffer")
+    assert_bits_equal(np_of(u["full"]), np.concatenate([comp, np_of(u["peer_shards"][1])]), "full buffer")
