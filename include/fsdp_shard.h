@@ -70,7 +70,8 @@ enum {
     FSDP_OK = 0,
     FSDP_E_INVAL = -1,  /* null pointer, world/rank out of range, negative size, bad step */
     FSDP_E_DTYPE = -2,  /* unsupported dtype or dtype combination */
-    FSDP_E_SIZE = -3,   /* output capacity too small or inconsistent sizes */
+    FSDP_E_SIZE = -3,   /* output capacity too small, inconsistent sizes, or an element count
+                           (unit, shard x world, buffer) above INT64_MAX / 16 */
     FSDP_E_ALIAS = -4,  /* an output overlaps an input or another output */
     FSDP_E_HIP = -5,    /* HIP runtime error while enqueueing */
     FSDP_E_IO = -6,     /* a file could not be opened, written or renamed */

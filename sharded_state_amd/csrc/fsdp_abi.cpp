@@ -130,6 +130,8 @@ int check_world(int32_t world, int32_t rank, int64_t S) {
         return fail(FSDP_E_INVAL, "world = %d outside [1, %d]", world, FSDP_MAX_WORLD);
     if (rank < 0 || rank >= world) return fail(FSDP_E_INVAL, "rank = %d outside [0, %d)", rank, world);
     if (S < 0) return fail(FSDP_E_INVAL, "shard_numel = %lld < 0", (long long)S);
+    if (S > fsdp::kMaxElems / world)
+        return fail(FSDP_E_SIZE, "shard_numel = %lld times world = %d is too large", (long long)S, world);
     return FSDP_OK;
 }
 
@@ -372,7 +374,7 @@ int layout_impl(const int64_t* numels, int32_t n_tensors, int32_t world, int64_t
     int64_t total = 0;
     for (int32_t k = 0; k < n_tensors; ++k) {
         if (numels[k] < 0) return fail(FSDP_E_INVAL, "numels[%d] < 0", k);
-        if (total > INT64_MAX / 16 - numels[k]) return fail(FSDP_E_SIZE, "unit too large");
+        if (total > fsdp::kMaxElems - numels[k]) return fail(FSDP_E_SIZE, "unit too large");
         total += numels[k];
     }
     const int64_t padded = (total + world - 1) / world * world;
@@ -588,6 +590,8 @@ int fsdp_unshard_gather(const void* const* shards, int32_t world, int64_t shard_
     if (world < 1 || world > FSDP_MAX_WORLD)
         return fail(FSDP_E_INVAL, "world = %d outside [1, %d]", world, FSDP_MAX_WORLD);
     if (shard_numel < 0) return fail(FSDP_E_INVAL, "shard_numel = %lld < 0", (long long)shard_numel);
+    if (shard_numel > fsdp::kMaxElems / world)
+        return fail(FSDP_E_SIZE, "shard_numel = %lld times world = %d is too large", (long long)shard_numel, world);
     if (!valid_dtype(dt)) return fail(FSDP_E_DTYPE, "dtype %d unsupported", (int)dt);
     if (shard_numel == 0) return ok();
     if (!shards) return fail(FSDP_E_INVAL, "shards is NULL");
@@ -618,8 +622,8 @@ int fsdp_unflatten_views(const int64_t* numels, int32_t n_tensors, int64_t padde
     int64_t total = 0;
     int rc = layout_impl(numels, n_tensors, 1, &total, nullptr, nullptr);
     if (rc) return rc;
-    if (total > padded_numel)
-        return fail(FSDP_E_SIZE, "tensors hold %lld elements, more than padded_numel %lld",
+    if (total > padded_numel || padded_numel > fsdp::kMaxElems)
+        return fail(FSDP_E_SIZE, "tensors hold %lld elements; padded_numel %lld is smaller or too large",
                     (long long)total, (long long)padded_numel);
     if (n_tensors > 0 && !views_out) return fail(FSDP_E_INVAL, "views_out is NULL");
     if (dsts) {

@@ -11,6 +11,12 @@
 
 namespace fsdp {
 
+// Largest element count of a unit, a shard times the world, or any buffer the
+// library addresses: below it, an element count times 16 bytes still fits an
+// int64, so no byte offset or alias check can wrap.  Larger sizes are refused
+// with FSDP_E_SIZE.
+constexpr int64_t kMaxElems = INT64_MAX / 16;
+
 // Record a message for fsdp_last_error() and return `code` (negative).
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 // Clear the message and return FSDP_OK.

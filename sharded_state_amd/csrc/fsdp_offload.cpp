@@ -295,6 +295,8 @@ bool apart(const std::vector<Span>& outs, const std::vector<Span>& ins) {
 int check_unit(const fsdp_offload_unit& u, int k, int32_t world, int32_t rank, int grad_dt, int64_t as, int64_t cs,
                bool scratch, std::vector<Span>& host, std::vector<Span>& dev_out, std::vector<Span>& dev_in) {
     if (u.shard_numel < 0) return fsdp::fail(FSDP_E_INVAL, "unit %d: shard_numel < 0", k);
+    if (u.shard_numel > fsdp::kMaxElems / world)
+        return fsdp::fail(FSDP_E_SIZE, "unit %d: shard_numel times world is too large", k);
     if (u.shard_numel == 0) return FSDP_OK;
     const int64_t S = u.shard_numel;
     if (scratch && u.grad_shard_dev)
@@ -439,8 +441,17 @@ int offload_units(const fsdp_offload_unit* units, int32_t n_units, int32_t world
         hipEvent_t& a;
         hipEvent_t& b;
         bool owned;
+        hipStream_t st;
+        bool finished = false;
         ~Cleanup() {
-            if (!owned) return;   // the scratch's events stay with their device
+            if (!owned) {
+                // the scratch's events stay with their device.  A call that ends in
+                // an error may leave reduce-scatters into the scratch or copies out of
+                // it on the stream: let them finish before the lock (released after
+                // this) lets another call in
+                if (!finished) (void)hipStreamSynchronize(st);
+                return;
+            }
             for (hipEvent_t x : ev)
                 if (x) {
                     (void)hipEventSynchronize(x);
@@ -449,7 +460,7 @@ int offload_units(const fsdp_offload_unit* units, int32_t n_units, int32_t world
             if (a) (void)hipEventDestroy(a);
             if (b) (void)hipEventDestroy(b);
         }
-    } cleanup{ready, entry, done, !use_scratch};
+    } cleanup{ready, entry, done, !use_scratch, st};
     hipError_t e = hipSuccess;
     if (!use_scratch) {
         for (size_t c = 0; c < chunks.size() && e == hipSuccess; ++c)
@@ -569,6 +580,7 @@ int offload_units(const fsdp_offload_unit* units, int32_t n_units, int32_t world
         if ((e = hipEventRecord(done, cst)) != hipSuccess || (e = hipStreamWaitEvent(st, done, 0)) != hipSuccess)
             return fsdp::hip_fail(e, "copy stream ordering");
     }
+    cleanup.finished = true;
     return fsdp::ok();
 }
 

@@ -310,3 +310,31 @@ def test_noalloc_offload_checks_the_scratch_limit_before_any_device_work():
     assert call(limit // 2 + 8, fp32_reduce=0) == N.E_SIZE   # 16-bit average: 2 bytes per element
     assert call(0, grad_dev=FAKE + (9 << 30)) == N.E_INVAL
     assert "grad_shard_dev must be NULL" in L.fsdp_last_error().decode()
+
+
+def test_element_counts_whose_byte_offsets_would_wrap_are_refused():
+    """A shard times the world, or any buffer, above INT64_MAX / 16 elements is
+    refused with FSDP_E_SIZE before any byte offset is formed (fake pointers)."""
+    L = N.lib()
+    cap = (2 ** 63 - 1) // 16
+    g = [FAKE + (1 << 36), FAKE + (2 << 36)]
+    a, b, c = FAKE, FAKE + (1 << 30), FAKE + (2 << 30)
+    assert _adamw(a, b, c, g, 2, 0, S=cap // 2 + 1) == N.E_SIZE
+    assert "too large" in L.fsdp_last_error().decode()
+    assert _adamw(a, b, c, g, 2, 0, S=cap // 2, step=0) == N.E_INVAL   # at the bound: the next check speaks
+    rc = L.fsdp_reduce_scatter_local(N.ptr_array(g), 2, 1, cap // 2 + 1, N.F16, 0, ctypes.c_void_p(FAKE), None)
+    assert rc == N.E_SIZE
+    rc = L.fsdp_unshard_gather(N.ptr_array(g), 2, cap // 2 + 1, N.F16, ctypes.c_void_p(FAKE), None)
+    assert rc == N.E_SIZE
+    views = (N.View * 1)()
+    rc = L.fsdp_unflatten_views(N.i64_array([5]), 1, cap + 1, views, None, N.F32, None, None)
+    assert rc == N.E_SIZE
+    rc = L.fsdp_flatten_pad(N.ptr_array([FAKE, FAKE]), N.i64_array([cap, 1]), 2, N.F32, 1,
+                            ctypes.c_void_p(FAKE), 2 ** 62, None, None)
+    assert rc == N.E_SIZE
+    hp = N.AdamWHP()
+    host = [FAKE + (k << 34) for k in range(1, 6)]
+    u = (N.OffloadUnit * 1)(N.OffloadUnit(host[0], host[1], host[2], N.ptr_array(g), FAKE + (9 << 30), host[3],
+                                          host[4], FAKE + (8 << 30), cap // 2 + 1))
+    rc = L.fsdp_offload_step_units(u, 1, 2, 0, N.F16, 1, N.F16, 0, ctypes.byref(hp), 1, None, None)
+    assert rc == N.E_SIZE
