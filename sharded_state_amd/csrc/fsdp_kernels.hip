@@ -6,8 +6,12 @@
 //    elements of the shard per step (one dwordx4 of 16-bit data, two of fp32),
 //    except in the unit kernel, whose group layout (load8g in fsdp_device.h)
 //    gives each wave access instruction one contiguous span;
-//  * grid-stride loops over a grid sized to a multiple of the CU count, so a
-//    launch is a few thousand workgroups regardless of the unit size;
+//  * one-shot grids: a lane takes one 16-byte vector (8 elements) and the grid
+//    has as many workgroups as that needs, up to 2048 per CU; the grid-stride
+//    loops of the copy and reduce-scatter kernels make a second trip only
+//    beyond that (about 1e9 elements), and the unit kernel, whose launches
+//    hold at most 2^26 shard elements, has none (one-shot grids measured 3 to
+//    9 points above grid-stride grids of 4 to 16 workgroups per CU);
 //  * the N simulated ranks' gradient blocks are accumulated in registers, all N
 //    loads issued before the first add (N is a template parameter for
 //    N in {1, 2, 4, 8});
