@@ -20,10 +20,16 @@ constexpr int kBlocksPerCU = FSDP_BLOCKS_PER_CU;       // grid cap = CUs * kBloc
 // streams through HBM measurably faster (+1.5 to +3 points of peak on every
 // workload, same-process A/B); the copy and reduce kernels, with one or two
 // loads per lane, need full occupancy instead and reserve none.
-constexpr unsigned kUnitLdsBytes = 81920;
+#ifndef FSDP_UNIT_LDS
+#define FSDP_UNIT_LDS 81920
+#endif
+constexpr unsigned kUnitLdsBytes = FSDP_UNIT_LDS;
 // 3 per CU instead: measured faster for 16-bit state with N <= 2 (+1.5 to +3.7
 // points; with N = 8 it loses 3.7), so those instantiations reserve this.
-constexpr unsigned kUnitLdsBytes3 = 53248;
+#ifndef FSDP_UNIT_LDS3
+#define FSDP_UNIT_LDS3 53248
+#endif
+constexpr unsigned kUnitLdsBytes3 = FSDP_UNIT_LDS3;
 constexpr int kSegMax = 64;             // segments per flatten/unflatten launch
 constexpr int64_t kSegChunkBytes = 8192;    // bytes per flatten/unflatten workgroup (8 KB: 6.0-6.5 TB/s; 32 KB 5.5-5.9, 4 KB 5.7-6.2)
 

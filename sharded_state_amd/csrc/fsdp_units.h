@@ -72,13 +72,14 @@ __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t 
 #pragma unroll
             for (int j = 0; j < NW - 1; ++j)
 #pragma unroll
-                for (int w = 0; w < kW; ++w) st16(reinterpret_cast<u32x4*>(B.pdst[u][j]) + pv(w), peer[j][w]);
+                for (int w = 0; w < kW; ++w)
+                    st16_wave(reinterpret_cast<u32x4*>(B.pdst[u][j]) + (pv(w) - l), (int)l, peer[j][w]);
         } else if constexpr (NW == 0) {
             for (int j = 0; j < B.npeers; ++j)
 #pragma unroll
                 for (int w = 0; w < kW; ++w)
-                    st16(reinterpret_cast<u32x4*>(B.pdst[u][j]) + pv(w),
-                         ld16<true>(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + pv(w)));
+                    st16_wave(reinterpret_cast<u32x4*>(B.pdst[u][j]) + (pv(w) - l), (int)l,
+                              ld16<true>(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + pv(w)));
         }
     } else {
         if (out) store8g<CF>(out, vi, pp);
