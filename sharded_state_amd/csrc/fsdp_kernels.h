@@ -31,7 +31,11 @@ constexpr unsigned kUnitLdsBytes = FSDP_UNIT_LDS;
 #endif
 constexpr unsigned kUnitLdsBytes3 = FSDP_UNIT_LDS3;
 constexpr int kSegMax = 64;             // segments per flatten/unflatten launch
-constexpr int64_t kSegChunkBytes = 8192;    // bytes per flatten/unflatten workgroup (8 KB: 6.0-6.5 TB/s; 32 KB 5.5-5.9, 4 KB 5.7-6.2)
+// Bytes per flatten/unflatten workgroup: one 16-byte vector per lane.  With the
+// sc1 store policy 4 KB chunks measured 6.05-6.60 TB/s on the four block shapes
+// (70B block 6.61, 13B 6.60-6.62), against 5.90-6.54 with 8 KB chunks (with or
+// without the policy); with global stores 8 KB had been best (32 KB 5.5-5.9).
+constexpr int64_t kSegChunkBytes = 4096;
 
 // Per-element AdamW constants, computed on the host (double, rounded once).
 struct AdamScalars {

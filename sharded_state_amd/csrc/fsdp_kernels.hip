@@ -61,11 +61,10 @@ __global__ __launch_bounds__(kThreads) void k_reduce_scatter(
 
 // Copy `bytes` bytes from src to dst (or write zeros when src is null) with the
 // widest access both addresses allow.  Called by every lane of a range of
-// `nthreads` lanes, lane index `lane`.  SPAN: the 16-byte stores of a wave go
-// out as one span with the sc1 policy (st16_wave), which the gathers and the
-// peers' copies gain from (1 GiB copy +2.3%); the segmented flatten/unflatten
-// copy measured 1-3% slower with it and keeps plain non-temporal stores.
-template <bool SPAN>
+// `nthreads` lanes, lane index `lane`.  The 16-byte stores of a wave go out as
+// one span with the sc1 policy (st16_wave): a 1 GiB copy +2.3%, the segmented
+// flatten/unflatten copy +2 to +8% (with 4 KB chunks; with 8 KB chunks it had
+// measured 1-3% slower).
 __device__ __forceinline__ void copy_range(char* __restrict__ dst, const char* __restrict__ src,
                                            int64_t bytes, int64_t lane, int64_t nthreads) {
     const uintptr_t a = (uintptr_t)dst | (src ? (uintptr_t)src : 0);
@@ -76,15 +75,11 @@ __device__ __forceinline__ void copy_range(char* __restrict__ dst, const char* _
         // lane and nthreads are multiples of 64 apart from threadIdx.x % 64, so
         // each wave's lanes cover one 1 KB span per trip
         const int l = (int)(threadIdx.x & 63);
-        auto put = [&](int64_t i, u32x4 v) {
-            if constexpr (SPAN) st16_wave(d + (i - l), l, v);
-            else st16(d + i, v);
-        };
         if (src) {
-            for (int64_t i = lane; i < nv; i += nthreads) put(i, ld16<true>(s + i));
+            for (int64_t i = lane; i < nv; i += nthreads) st16_wave(d + (i - l), l, ld16<true>(s + i));
         } else {
             const u32x4 z = {0u, 0u, 0u, 0u};
-            for (int64_t i = lane; i < nv; i += nthreads) put(i, z);
+            for (int64_t i = lane; i < nv; i += nthreads) st16_wave(d + (i - l), l, z);
         }
         for (int64_t i = (nv << 4) + lane; i < bytes; i += nthreads) dst[i] = src ? src[i] : 0;
     } else if ((a & 3) == 0) {
@@ -109,7 +104,7 @@ __device__ __forceinline__ void copy_range(char* __restrict__ dst, const char* _
 template <int MAXN>
 __global__ __launch_bounds__(kThreads) void k_gather(CopyList<MAXN> L, int64_t bytes) {
     const int j = blockIdx.y;
-    copy_range<true>(L.dst[j], L.src[j], bytes, (int64_t)blockIdx.x * kThreads + threadIdx.x,
+    copy_range(L.dst[j], L.src[j], bytes, (int64_t)blockIdx.x * kThreads + threadIdx.x,
                (int64_t)gridDim.x * kThreads);
 }
 
@@ -117,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void k_gather(CopyList<MAXN> L, int64_t b
 // (copies shorter than the longest leave their surplus blocks idle).
 __global__ __launch_bounds__(kThreads) void k_copies(CopyBatch L) {
     const int j = blockIdx.y;
-    copy_range<true>(L.dst[j], L.src[j], L.bytes[j], (int64_t)blockIdx.x * kThreads + threadIdx.x,
+    copy_range(L.dst[j], L.src[j], L.bytes[j], (int64_t)blockIdx.x * kThreads + threadIdx.x,
                (int64_t)gridDim.x * kThreads);
 }
 
@@ -136,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void k_segments(SegBatch B) {
     int64_t n = B.bytes[k] - start;
     if (n > kSegChunkBytes) n = kSegChunkBytes;
     if (n <= 0) return;
-    copy_range<false>(B.dst[k] + start, B.src[k] ? B.src[k] + start : nullptr, n, threadIdx.x, kThreads);
+    copy_range(B.dst[k] + start, B.src[k] ? B.src[k] + start : nullptr, n, threadIdx.x, kThreads);
 }
 
 // ----------------------------------------------------------------- launchers
