@@ -137,10 +137,10 @@ __device__ __forceinline__ void load8(const void* __restrict__ base, int64_t vi,
     }
 }
 
-// Plain non-temporal stores.  Each fp32 instruction here writes one half of
-// every 32-byte piece of its wave's span; with the sc1 policy of st16_span the
-// reduce-scatter alone measured 35% slower with fp32 output (and tied with
-// bf16 output), so the policy stays on whole-span stores.
+// Plain non-temporal stores of 8 consecutive elements per lane (the 16-bit
+// output of the reduce-scatter alone).  An fp32 instruction here would write
+// one half of every 32-byte piece of its wave's span: with the sc1 policy that
+// measured 35% slower, so fp32 outputs take the group layout (store8g).
 template <int F>
 __device__ __forceinline__ void store8(void* __restrict__ base, int64_t vi, const float (&x)[8]) {
     if constexpr (F == FSDP_F32) {
