@@ -3,7 +3,11 @@
 * world = FSDP_MAX_WORLD (128) simulated ranks through the generic kernel, with
   the fused all-gather (127 peer copies) and through the separate reduce-scatter;
 * a shard of more than 2**31 elements (64-bit element indexing end to end:
-  tile numbers, vector and byte offsets), every element against the oracle.
+  tile numbers, vector and byte offsets), every element against the oracle;
+* the grid-stride kernels past their one-trip grid (2048 workgroups per CU):
+  a reduce-scatter of 2**30 + 12345 elements with fp32 output (group layout)
+  and a gather of one 2**29 + 4099-element fp32 shard (over 2 GiB), where
+  lanes take a second trip, every element compared.
 """
 import numpy as np
 import pytest
@@ -95,3 +99,55 @@ def test_shard_of_more_than_2_31_elements():
     assert_bits_equal(np_of(m), mm, "exp_avg")
     assert_bits_equal(np_of(v), vm, "exp_avg_sq")
     assert_bits_equal(np_of(full), comp, "compute copy in the full buffer")
+
+
+def _need(nbytes):
+    free, _ = torch.cuda.mem_get_info()
+    if free < nbytes + (1 << 30):
+        pytest.skip("needs %.1f GB of free device memory, %.1f GB free" % (nbytes / 1e9, free / 1e9))
+
+
+def test_reduce_scatter_beyond_one_trip_of_its_grid():
+    """N = 1, fp16 gradient reduced to fp32: 2**30 + 12345 elements are more
+    vectors than the capped grid has lanes (256 CUs x 2048 x 256 = 2**27), so
+    the last groups are reduced on a second trip of the grid-stride loop."""
+    S = (1 << 30) + 12345
+    _need(S * (2 + 4))
+    print("S =", S, flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    grad = torch.empty(S, dtype=torch.float16, device="cuda")
+    chunk = 1 << 28
+    for lo in range(0, S, chunk):
+        hi = min(S, lo + chunk)
+        grad[lo:hi] = (torch.randn(hi - lo, device="cuda", generator=g) * 1e-3).to(torch.float16)
+    out = ss.fsdp_reduce_scatter_local([grad], 0, True)
+    torch.cuda.synchronize()
+    g0 = np_of(grad)
+    ref = np.empty(S, np.float32)
+
+    def rs(lo, hi):
+        ref[lo:hi] = oracle.reduce_scatter([g0[lo:hi]], 0, "f16", True)
+
+    oracle_chunks(S, rs)
+    assert_bits_equal(np_of(out), ref, "reduce-scatter, two trips")
+
+
+def test_gather_beyond_one_trip_of_its_grid():
+    """One fp32 shard of 2**29 + 4099 elements (2.1 GB) gathered into a
+    one-slot full buffer: more 16-byte vectors than the grid's lanes, so the
+    copy takes a second trip; the result is the shard, byte for byte."""
+    S = (1 << 29) + 4099
+    _need(S * 8)
+    print("S =", S, flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(17)
+    shard = torch.empty(S, device="cuda")
+    chunk = 1 << 28
+    for lo in range(0, S, chunk):
+        hi = min(S, lo + chunk)
+        shard[lo:hi] = torch.randn(hi - lo, device="cuda", generator=g)
+    full = ss.fsdp_unshard_gather([shard])
+    torch.cuda.synchronize()
+    sh = np_of(shard)
+    assert_bits_equal(np_of(full), oracle.gather([sh], "f32"), "gather, two trips")
