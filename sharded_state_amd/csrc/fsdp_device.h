@@ -137,10 +137,14 @@ __device__ __forceinline__ void load8(const void* __restrict__ base, int64_t vi,
     }
 }
 
-// Plain non-temporal stores of 8 consecutive elements per lane (the 16-bit
-// output of the reduce-scatter alone).  An fp32 instruction here would write
-// one half of every 32-byte piece of its wave's span: with the sc1 policy that
-// measured 35% slower, so fp32 outputs take the group layout (store8g).
+// 8 consecutive elements per lane, stored by whole waves: lane l =
+// threadIdx.x % 64 stores vector vi with vi % 64 == l, the wave the 64
+// consecutive vectors from vi - l.  16-bit: one dwordx4 per lane, the wave's
+// 1 KB span with the sc1 policy (the reduce-scatter's 16-bit output, the
+// bf16-state unit step with N <= 2).  fp32 (two instructions, each one half of
+// every 32-byte piece of the span) keeps plain non-temporal stores: with the
+// sc1 policy that form measured 35% slower, so fp32 outputs take the group
+// layout (store8g) instead.
 template <int F>
 __device__ __forceinline__ void store8(void* __restrict__ base, int64_t vi, const float (&x)[8]) {
     if constexpr (F == FSDP_F32) {
@@ -158,7 +162,8 @@ __device__ __forceinline__ void store8(void* __restrict__ base, int64_t vi, cons
         for (int k = 0; k < 4; ++k) w[k] = from_f32<F>(x[2 * k]) | (from_f32<F>(x[2 * k + 1]) << 16);
         u32x4 a;
         a.x = w[0]; a.y = w[1]; a.z = w[2]; a.w = w[3];
-        st16(reinterpret_cast<u32x4*>(base) + vi, a);
+        const int l = (int)(threadIdx.x & 63);
+        st16_wave(reinterpret_cast<u32x4*>(base) + (vi - l), l, a);
     }
 }
 
@@ -217,6 +222,12 @@ __device__ __forceinline__ void store8g(void* __restrict__ base, int64_t vi, con
         st8_span<512>(q, 8u * (unsigned)l, a);
         st8_span<512>(q + 64, 8u * (unsigned)l, b);
     }
+}
+
+template <int F, bool GROUP>
+__device__ __forceinline__ void store8x(void* __restrict__ base, int64_t vi, const float (&x)[8]) {
+    if constexpr (GROUP) store8g<F>(base, vi, x);
+    else store8<F>(base, vi, x);
 }
 
 // The 8 elements of vector vi: consecutive (GROUP = false) or in the group layout.

@@ -24,7 +24,8 @@ namespace fsdp {
 
 // ----------------------------------------------------------------- kernels
 // One unit's step on vector vi (8 elements of a whole group in the group
-// layout, load8g): every load first (the N gradient blocks, the parameter and
+// layout, load8g; for bf16 state with N <= 2, 8 consecutive elements, load8):
+// every load first (the N gradient blocks, the parameter and
 // the optimizer's state, the peers' compute vectors), then the math, then every
 // store.  With GATHER, `out` is this rank's slot of the full buffer and the
 // peers' vectors are copied into their slots (the copy moves the group's bytes
@@ -52,22 +53,27 @@ __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t 
     // there; the hint gains 0.5 to 3 points on the fp32-state shapes and 0.7 on
     // the N = 8 bf16-state shape; same box, same bench)
     constexpr bool kNtState = SF == FSDP_F32 || NW == 0 || NW > 2;
-    load8g<SF, kNtState>(p, vi, pp);
-    if constexpr (OPT::kStates >= 1) load8g<SF, kNtState>(m, vi, mm);
-    if constexpr (OPT::kStates >= 2) load8g<SF, kNtState>(v, vi, vv);
-    reduce8<NW, GF, FP32R, true, true>(UnitGrads<NW>{B, u}, B.world, vi, acc);
+    // bf16 state with N <= 2 (every stream 16-bit): 8 consecutive elements per
+    // lane, one dwordx4 per stream (+2.1 to +2.5 points against the group layout
+    // on GPT-2 Large and XL; fp16 state lost 2.2 and N = 8 tied, so they and
+    // fp32 state keep the group layout)
+    constexpr bool kG = !(SF == FSDP_BF16 && NW >= 1 && NW <= 2);
+    load8x<SF, kNtState, kG>(p, vi, pp);
+    if constexpr (OPT::kStates >= 1) load8x<SF, kNtState, kG>(m, vi, mm);
+    if constexpr (OPT::kStates >= 2) load8x<SF, kNtState, kG>(v, vi, vv);
+    reduce8<NW, GF, FP32R, true, kG>(UnitGrads<NW>{B, u}, B.world, vi, acc);
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the math
 #pragma unroll
     for (int k = 0; k < 8; ++k) op(finish<NW, GF, FP32R>(acc[k], rs), pp[k], mm[k], vv[k]);
-    store8g<SF>(p, vi, pp);
-    if constexpr (OPT::kStates >= 1) store8g<SF>(m, vi, mm);
-    if constexpr (OPT::kStates >= 2) store8g<SF>(v, vi, vv);
+    store8x<SF, kG>(p, vi, pp);
+    if constexpr (OPT::kStates >= 1) store8x<SF, kG>(m, vi, mm);
+    if constexpr (OPT::kStates >= 2) store8x<SF, kG>(v, vi, vv);
     void* out = B.out[u];
     void* out2 = B.out2[u];
     if constexpr (GATHER) {
         // the unit step always has its own slot; keep the peer stores in the
         // same basic block as their loads so they are not sunk past the math
-        store8g<CF>(out, vi, pp);
+        store8x<CF, kG>(out, vi, pp);
         if constexpr (NW > 1) {
 #pragma unroll
             for (int j = 0; j < NW - 1; ++j)
@@ -82,12 +88,12 @@ __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t 
                               ld16<true>(reinterpret_cast<const u32x4*>(B.psrc[u][j]) + pv(w)));
         }
     } else {
-        if (out) store8g<CF>(out, vi, pp);
+        if (out) store8x<CF, kG>(out, vi, pp);
     }
     // non-temporal like every other output: plain stores, which keep this
     // persistent copy in the caches, win only when the next all-gather follows
     // the step at once and lose when it comes after other units' work
-    if (out2) store8g<CF>(out2, vi, pp);
+    if (out2) store8x<CF, kG>(out2, vi, pp);
 }
 
 // Element i of unit u, one lane (the tail past the last full vector, or every
