@@ -34,6 +34,7 @@ from .offload import (  # noqa: F401
     prepare_offload_step_units,
 )
 from .checkpoint import consolidate, load_shard, save_shard, shard_info, shard_path  # noqa: F401
+from .config import UnitConfig, from_bf16_mixed_precision, from_fairseq  # noqa: F401
 
 __all__ = [
     "AdamWHP", "OptimHP", "FsdpError", "MAX_WORLD", "lib", "dtype_code", "fsdp_layout", "fsdp_flatten_pad",
@@ -41,4 +42,5 @@ __all__ = [
     "fsdp_unflatten_views", "view_table", "RankState", "save_shard", "load_shard", "shard_info",
     "shard_path", "consolidate", "fsdp_host_adamw", "fsdp_offload_step", "fsdp_offload_step_units",
     "fsdp_offload_step_units_noalloc", "prepare_offload_step_units", "OffloadState", "unit_gather_split", "units_in_launch",
+    "UnitConfig", "from_fairseq", "from_bf16_mixed_precision",
 ]

@@ -106,3 +106,37 @@ def test_prepared_offload_call_takes_each_step():
         assert_bitexact(np_of(st.exp_avg), om, "offload exp_avg t=%d" % t)
         assert_bitexact(np_of(st.exp_avg_sq), ov, "offload exp_avg_sq t=%d" % t)
         assert np.array_equal(np_of(comp), oracle.cast(op, "bf16")), t
+
+
+def test_unit_config_step_is_the_flags_step():
+    """UnitConfig.step with fairseq's --fp16 --fp32-reduce-scatter (reshard after
+    forward: two gathers, a persistent compute shard) steps the unit as the
+    flags say: fp16 gradients reduced in fp32, fp32 master, fp16 compute copy
+    in the own slot and in the persistent shard, the peer's slot copied."""
+    cfg = scaled(CONFIGS["gpt3-13b-block"], gpt_block(64) + [("odd", (3,))], world=2)
+    rank = 1
+    c = ss.from_fairseq(cfg.world, rank, fp16=True, fp32_reduce_scatter=True)
+    print("case UnitConfig step, N=%d rank %d" % (cfg.world, rank), flush=True)
+    S, p, m, v, grads = _unit(cfg, rank)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    peers = [(torch.randn(S, device="cuda", generator=g) * 0.02).half() if q != rank else None
+             for q in range(cfg.world)]
+    full = torch.empty(cfg.world * S, dtype=torch.float16, device="cuda")
+    comp = torch.empty(S, dtype=torch.float16, device="cuda")
+    op, om, ov = np_of(p), np_of(m), np_of(v)
+    og = oracle.reduce_scatter([np_of(x) for x in grads], rank, "f16", True)
+    c.step([dict(master=p, exp_avg=m, exp_avg_sq=v, rank_grads=grads, peer_shards=peers, full=full,
+                 compute_shard=comp)], ss.AdamWHP(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, 1))
+    torch.cuda.synchronize()
+    oracle.adamw(op, om, ov, og, oracle.hp(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, 1))
+    assert_bitexact(np_of(p), op, "master")
+    assert_bitexact(np_of(m), om, "exp_avg")
+    assert_bitexact(np_of(v), ov, "exp_avg_sq")
+    own = oracle.cast(op, "f16")
+    assert_bitexact(np_of(full[rank * S:(rank + 1) * S]), own, "own slot")
+    assert_bitexact(np_of(comp), own, "persistent compute shard")
+    assert_bitexact(np_of(full[:S]), np_of(peers[0]), "peer slot")
+    with pytest.raises(ValueError, match="persistent"):
+        c.step([dict(master=p, exp_avg=m, exp_avg_sq=v, rank_grads=grads, peer_shards=peers, full=full)],
+               ss.AdamWHP())
