@@ -159,6 +159,28 @@ def test_empty_shard_is_a_no_op():
     torch.cuda.synchronize()
 
 
+def test_device_memory_exhaustion_raises_in_python_before_any_launch():
+    """With torch's allocator capped below a rank's state, RankState raises
+    torch.cuda.OutOfMemoryError in the Python layer (nothing is launched), and
+    the library works as before once the cap is lifted."""
+    print("case allocator cap", flush=True)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    total = torch.cuda.get_device_properties(0).total_memory
+    torch.cuda.set_per_process_memory_fraction((1 << 30) / total)      # about 1 GiB
+    try:
+        with pytest.raises(torch.cuda.OutOfMemoryError):
+            ss.RankState([1 << 30], 1, 0, torch.bfloat16)              # 4 GiB of fp32 master alone
+    finally:
+        torch.cuda.set_per_process_memory_fraction(1.0)
+        torch.cuda.empty_cache()
+    grads = [torch.randn(2 * 4099, device="cuda").half() for _ in range(2)]
+    out = ss.fsdp_reduce_scatter_local(grads, 1, True)
+    torch.cuda.synchronize()
+    ref = oracle.reduce_scatter([np_of(g) for g in grads], 1, "f16", True)
+    assert_bitexact(np_of(out), ref, "reduce-scatter after the cap")
+
+
 def test_run_twice_is_bitwise_deterministic():
     cfg = scaled(CONFIGS["llama70b-block"], llama_block(64, 80, 224))
     a, b = UnitRun(cfg), UnitRun(cfg)
