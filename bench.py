@@ -122,8 +122,9 @@ def sizes(cfg, pipeline, state="f32", n_states=2, split=False):
     c = 4 if cfg.compute_dt == "f32" else 2
     N, G = cfg.world, cfg.gathers
     if state != "f32":               # 16-bit parameter, m, v; the parameter is the compute copy
-        fused = N * g + 12 + c + 2 * (N - 1) * c
-        return fused, fused + (G - 1) * 2 * N * c
+        kernel = N * g + 12 + c
+        step = kernel + 2 * (N - 1) * c + (G - 1) * 2 * N * c
+        return (kernel if split else kernel + 2 * (N - 1) * c), step
     st = 8 * (1 + n_states)
     if pipeline == "separate":
         fused = N * g + st + c

@@ -66,6 +66,12 @@ def test_sixteen_bit_state_bytes():
     cfg = CONFIGS["llama70b-block"]      # N = 8, bf16 grads and compute
     kernel, step = bench.sizes(cfg, "unit", "bf16")
     assert kernel == step == 8 * 2 + 12 + 2 + 2 * 7 * 2
+    # were the launch plan to split the peers' copies out, the step launch would not carry them
+    ks, ss_ = bench.sizes(cfg, "unit", "bf16", 2, True)
+    assert (ks, ss_) == (8 * 2 + 12 + 2, step)
+    g2 = CONFIGS["gpt3-13b-block"]       # two gathers: the second one's bytes are in the step only
+    k2, s2 = bench.sizes(g2, "unit", "f16")
+    assert k2 == 8 * 2 + 12 + 2 + 2 * 7 * 2 and s2 == k2 + 2 * 8 * 2
 
 
 def test_kernel_code_ignores_comments_only():
