@@ -109,8 +109,11 @@ template <> __device__ __forceinline__ uint32_t from_f32<FSDP_F16>(float x) {
 }
 template <> __device__ __forceinline__ uint32_t from_f32<FSDP_BF16>(float x) {
     // Round the fp32 encoding at bit 16, ties to even; NaN stays a quiet NaN.
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    // The NaN test is one unordered compare (on the encoding it took a mask and
+    // a compare) and a branch a wave skips when none of its lanes holds a NaN:
+    // the rounding runs after every rank's add of a 16-bit reduce-scatter.
+    const uint32_t u = __float_as_uint(x);
+    if (__builtin_isnan(x)) return (u >> 16) | 0x40u;
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
