@@ -113,3 +113,54 @@ def test_special_values_16bit_state(sdt):
         oracle.rank_step16(grads, r, op, om, ov, h, "f32", True, sdt)
         for nm, got, ref in (("param", tp, op), ("exp_avg", tm, om), ("exp_avg_sq", tv, ov)):
             assert_ulp16(np_of(got), ref, sdt, "%s %s rank %d" % (nm, sdt, r), tol=0)
+
+
+@pytest.mark.parametrize("world", [2, 8, 3])
+def test_bf16_reduce_scatter_keeps_nan_payloads(world):
+    """bf16 gradients reduced in bf16 (no --fp32-reduce-scatter): signalling and
+    quiet NaNs with payloads, of either sign, each alone at its position across
+    the ranks, come out of the reduce-scatter as the oracle's quiet NaN with the
+    same sign and payload, bit for bit; so do infinities, overflow to infinity
+    and the numbers around them.  Where two ranks' NaNs meet or +Inf meets -Inf
+    only NaN-ness is compared (the pages fix no payload there).  Covers the
+    vector body and the scalar tail of the reduce-scatter kernel."""
+    S = 1003
+    print("case bf16 NaN payloads, N=%d" % world, flush=True)
+    rng = np.random.default_rng(world)
+    n = world * S
+    base = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for _ in range(world)]
+    bits = [oracle.f32_to(b, "bf16").copy() for b in base]       # the bf16 encodings
+    rank = world - 1
+    lo = rank * S
+    singles = [0x7F81, 0x7FC5, 0xFF82, 0xFFC3, 0x7FA0, 0xFFFF, 0x7F80, 0xFF80]   # NaNs with payloads, +-Inf
+    exact_pos = []
+    for k, val in enumerate(singles):
+        body = [lo + 5 + 61 * k]
+        tail = [lo + S - 1 - k] if k < 3 else []                     # the last 3 elements: the scalar tail
+        for pos in body + tail:
+            q = (k + pos) % world
+            bits[q][pos] = val
+            exact_pos.append(pos)
+    big = oracle.f32_to(np.array([3.3e38], np.float32), "bf16")[0]
+    for q in range(world):                                          # overflow to +Inf in the sum
+        bits[q][lo + 700] = big
+    exact_pos.append(lo + 700)
+    nan_only = []
+    if world >= 2:
+        bits[0][lo + 800], bits[1][lo + 800] = 0x7F80, 0xFF80       # +Inf + -Inf
+        bits[0][lo + 801], bits[1][lo + 801] = 0x7F81, 0xFFC7       # two NaNs meet
+        nan_only = [lo + 800, lo + 801]
+    grads = [torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).cuda() for b in bits]
+    out = ss.fsdp_reduce_scatter_local(grads, rank, False)
+    torch.cuda.synchronize()
+    got = np_of(out)
+    ref = oracle.reduce_scatter(bits, rank, "bf16", False)
+    keep = np.ones(S, bool)
+    keep[[p - lo for p in nan_only]] = False
+    bad = np.nonzero((got != ref) & keep)[0]
+    assert bad.size == 0, "bits differ at %s: %s vs %s" % (bad[:8], got[bad[:8]], ref[bad[:8]])
+    for p in nan_only:
+        isnan = lambda h: (int(h) & 0x7FFF) > 0x7F80
+        assert isnan(got[p - lo]) and isnan(ref[p - lo]), (p, hex(got[p - lo]), hex(ref[p - lo]))
+    for p in exact_pos:
+        assert got[p - lo] == ref[p - lo]
