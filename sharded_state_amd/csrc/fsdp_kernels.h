@@ -18,8 +18,9 @@ constexpr int kBlocksPerCU = FSDP_BLOCKS_PER_CU;       // grid cap = CUs * kBloc
 // with 160 KB of LDS per CU it holds residency at 2 workgroups (8 waves) per
 // CU.  Fewer tiles in flight at once streams the unit step's 8-11 address
 // streams through HBM measurably faster (+1.5 to +3 points of peak on every
-// workload, same-process A/B); the copy and reduce kernels, with one or two
-// loads per lane, need full occupancy instead and reserve none.
+// workload, same-process A/B); the copy kernels, with one load per lane, need
+// full occupancy instead and reserve none, and the reduce-scatter alone
+// reserves by its number of gradient streams (rs_lds_bytes).
 #ifndef FSDP_UNIT_LDS
 #define FSDP_UNIT_LDS 81920
 #endif

@@ -225,14 +225,29 @@ hipError_t launch_units(const UnitArgs* units, int n, const UnitLaunch& L) {
     return launch_units_policy(out.data(), (int)out.size(), L);
 }
 
+// Dynamic LDS reserved per reduce-scatter workgroup (the kernel uses none), as
+// for the unit kernel: with 4 or 8 gradient streams fewer resident workgroups
+// stream them through the DRAM faster.  Measured at block shapes (two sweeps,
+// separate processes): fp32 output with N = 4 or 8 at 2 workgroups per CU
+// +5 to +7% over full occupancy, 16-bit output with N = 8 at 3 per CU +5 to
+// +10%; N = 2, the generic kernel and 16-bit output with N = 4 lose with a cap
+// (N = 2 16-bit output falls by half: its one-vector workgroups are too short
+// for so few to keep the memory busy).
+template <int NW, bool kGroup>
+constexpr unsigned rs_lds_bytes() {
+    if (kGroup && (NW == 4 || NW == 8)) return kUnitLdsBytes;
+    if (!kGroup && NW == 8) return kUnitLdsBytes3;
+    return 0u;
+}
+
 template <int NW, int GF, bool FP32R>
 static hipError_t rs_only(const ReduceArgs& a, const GradPtrs<NW>& g) {
     constexpr bool kGroup = FP32R || GF == FSDP_F32;   // fp32 output: the group layout
     const int64_t nvec = kGroup ? a.nvec / 64 * 64 : a.nvec;   // whole groups; the rest is the element tail
     const int64_t work = nvec > 0 ? nvec : a.S;
     dim3 grid((unsigned)grid_for(work, a.cus));
-    launch(k_reduce_scatter<NW, GF, FP32R>, grid, dim3(kThreads), (hipStream_t)a.stream, g, a.world, a.S, nvec,
-           a.out, a.rs);
+    launch_lds(k_reduce_scatter<NW, GF, FP32R>, grid, dim3(kThreads), rs_lds_bytes<NW, kGroup>(),
+               (hipStream_t)a.stream, g, a.world, a.S, nvec, a.out, a.rs);
     return hipGetLastError();
 }
 

@@ -115,13 +115,14 @@ def test_special_values_16bit_state(sdt):
             assert_ulp16(np_of(got), ref, sdt, "%s %s rank %d" % (nm, sdt, r), tol=0)
 
 
-@pytest.mark.parametrize("world", [2, 8, 3])
+@pytest.mark.parametrize("world", [1, 2, 8, 3])
 def test_bf16_reduce_scatter_keeps_nan_payloads(world):
     """bf16 gradients reduced in bf16 (no --fp32-reduce-scatter): signalling and
     quiet NaNs with payloads, of either sign, each alone at its position across
     the ranks, come out of the reduce-scatter as the oracle's quiet NaN with the
     same sign and payload, bit for bit; so do infinities, overflow to infinity
-    and the numbers around them.  Where two ranks' NaNs meet or +Inf meets -Inf
+    and the numbers around them.  With one rank no add runs: the signalling NaN
+    is quieted by the division by N alone.  Where two ranks' NaNs meet or +Inf meets -Inf
     only NaN-ness is compared (the pages fix no payload there).  Covers the
     vector body and the scalar tail of the reduce-scatter kernel."""
     S = 1003
