@@ -157,7 +157,8 @@ class Unit:
             params = [t.to(sd) for t in params]
         flat = ss.fsdp_flatten_pad(params, cfg.world)
         del params
-        self.grads = [workloads.rank_grad(cfg, block, q, Pp, dev) for q in range(cfg.world)]
+        # the N ranks' gradients as the rows of one buffer (workloads.rank_grads)
+        self.grads = list(workloads.rank_grads(cfg, block, Pp, dev).unbind(0))
         cdt = workloads.TORCH_DTYPE[cfg.compute_dt] if state == "f32" else sd
         hp = ss.AdamWHP(cfg.lr, cfg.beta1, cfg.beta2, cfg.eps, cfg.weight_decay, cfg.step)
         # peers' compute shards: the other ranks' own steps on the same unit

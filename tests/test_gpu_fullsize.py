@@ -32,7 +32,7 @@ import torch
 import oracle
 import sharded_state_amd as ss
 from parity import assert_bits_equal, assert_compute_close, dt_name, np_of, oracle_rank_step_threaded
-from workloads import CONFIGS, TORCH_DTYPE, moments, param_tensors, rank_grad
+from workloads import CONFIGS, TORCH_DTYPE, moments, param_tensors, rank_grads
 
 pytestmark = pytest.mark.gpu
 
@@ -85,7 +85,7 @@ def test_full_size_every_element(name, blocks, end):
         del params
         master = flat[sl].clone()
         del flat
-        grads = [rank_grad(cfg, b, q, Pp, dev) for q in range(world)]
+        grads = list(rank_grads(cfg, b, Pp, dev).unbind(0))   # the benchmark's buffers: rows of one allocation
         m, v = moments(cfg, b, rank * S, S, P, dev)
         gen = torch.Generator(device=dev)
         gen.manual_seed(100 + 10 * b + rank)

@@ -6,7 +6,7 @@ Unit sizes are closed forms of the listed shapes: a GPT-2 block of width d holds
 8192 x (10240 + 8192 + 3 * 28672)."""
 import torch
 
-from workloads import CONFIGS, moments, param_tensors, rank_grad, scaled, gpt_block
+from workloads import CONFIGS, moments, param_tensors, rank_grad, rank_grads, scaled, gpt_block
 
 
 def test_unit_sizes():
@@ -42,3 +42,14 @@ def test_distributions():
     g5 = rank_grad(cfg5, 0, 0, cfg5.numel).float()
     frac = (g5.abs() > 20 * 5e-5).float().mean().item()
     assert 0.0007 < frac < 0.0013
+
+
+def test_stacked_gradients_are_the_ranks_gradients():
+    # one [world, length] buffer whose row q is rank q's gradient, byte for byte
+    cfg = scaled(CONFIGS["gpt3-13b-block"], gpt_block(32) + [("odd", (3,))], name="t", world=3)
+    length = cfg.numel + 2
+    st = rank_grads(cfg, 2, length)
+    assert st.shape == (3, length) and st.dtype == torch.float16 and st.is_contiguous()
+    for q in range(3):
+        assert torch.equal(st[q].view(torch.int16), rank_grad(cfg, 2, q, length).view(torch.int16))
+    assert st.stride(0) == length

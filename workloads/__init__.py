@@ -193,6 +193,17 @@ def rank_grad(cfg: UnitConfig, block: int, rank: int, length: int, device="cpu")
     return _fill(length, P, x, TORCH_DTYPE[cfg.grad_dt], device)
 
 
+def rank_grads(cfg: UnitConfig, block: int, length: int, device="cpu") -> torch.Tensor:
+    """Every simulated rank's flat gradient of the unit as the rows of one
+    [world, length] buffer: row q holds rank_grad(cfg, block, q, length).  One
+    allocation puts the N gradient streams at a fixed row stride of length
+    elements from each other, whatever the allocator does with separate buffers."""
+    out = torch.empty((cfg.world, length), dtype=TORCH_DTYPE[cfg.grad_dt], device=device)
+    for q in range(cfg.world):
+        out[q].copy_(rank_grad(cfg, block, q, length, device))
+    return out
+
+
 def moments(cfg: UnitConfig, block: int, begin: int, count: int, numel_limit: int, device="cpu"):
     """fp32 m and v for positions [begin, begin+count) of the (padded) flat unit:
     zero, or |N(0, mv_sigma)| inside the unit and +0 in the padding."""
