@@ -18,13 +18,16 @@
 // every size and offset against the file's length before it allocates or seeks.  A file is written to "<path>.tmp", flushed, synced and renamed, so a
 // reader never sees a partial file under the final name.  Device buffers move
 // through two pinned host staging buffers: the copy of chunk k+1 overlaps the
-// file write of chunk k, and each chunk's checksum runs on a helper thread
-// beside its write (save) or beside the read of the next chunk (load).
+// file write of chunk k (save) or the file read of chunk k+1 overlaps the copy
+// of chunk k (load).  A save checksums each chunk on a helper thread beside its
+// write; a load reads and checksums each chunk in parts on the worker pool.
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <future>
+#include <thread>
 #include <cerrno>
 #include <cstdio>
 #include <cstring>
@@ -36,9 +39,12 @@
 #include <unistd.h>
 
 #include "fsdp_internal.h"
+#include "fsdp_pool.h"
 #include "fsdp_shard.h"
 
 namespace {
+
+using fsdp::Pool;
 
 constexpr char kMagic[8] = {'F', 'S', 'D', 'P', 'S', 'H', 'R', 'D'};
 constexpr uint32_t kVersion = 2;   // 2: the header checksums itself
@@ -190,6 +196,75 @@ uint32_t crc_update(uint32_t state, const void* data, size_t n) {
     const unsigned char* p = (const unsigned char*)data;
     if (!hw) return crc_soft(state, p, n);
     return n >= (64u << 10) ? crc_hw3(state, p, n) : crc_hw(state, p, n);
+}
+
+// ------------------------------------------------------------------ parallel reads
+// A buffered read of one file scales with threads (a write does not: the
+// kernel serialises writes to one file), so the reader splits the payload into
+// parts of at least kPartMin bytes, each read with pread and checksummed from
+// a zero register by one worker of the pool; the parts' registers are then
+// folded in file order with the zero-bytes map: reg(s, A || B) = Z_|B|(reg(s,
+// A)) ^ reg(0, B).
+constexpr size_t kPartMin = 4u << 20;
+
+int read_threads() {
+    static const int n = [] {
+        const unsigned hc = std::thread::hardware_concurrency();
+        return (int)std::max(1u, std::min(hc ? hc : 1u, 8u));
+    }();
+    return n;
+}
+
+bool pread_all(int fd, char* dst, size_t n, uint64_t off) {
+    while (n) {
+        const ssize_t r = pread(fd, dst, n, (off_t)off);
+        if (r < 0 && errno == EINTR) continue;
+        if (r <= 0) return false;
+        dst += r;
+        n -= (size_t)r;
+        off += (uint64_t)r;
+    }
+    return true;
+}
+
+// Z_n for the part lengths of the last calls (at most two distinct lengths per call).
+const Gf2Matrix& zero_map_cached(uint64_t n) {
+    thread_local uint64_t len[2] = {~0ull, ~0ull};
+    thread_local Gf2Matrix z[2];
+    thread_local int next = 0;
+    for (int k = 0; k < 2; ++k)
+        if (len[k] == n) return z[k];
+    const int k = next;
+    next ^= 1;
+    z[k] = zero_bytes_map(n);
+    len[k] = n;
+    return z[k];
+}
+
+// Read n bytes at file offset `off` into dst and advance the running CRC32C
+// register `state` over them.  false on a short read or a read error.
+bool read_sum(int fd, uint64_t off, char* dst, size_t n, uint32_t& state) {
+    if (n == 0) return true;
+    const int parts = (int)std::max<size_t>(1, std::min<size_t>((size_t)read_threads(), n / kPartMin));
+    const size_t per = (n + parts - 1) / parts;
+    std::vector<uint32_t> reg(parts, 0u);
+    std::atomic<bool> ok{true};
+    Pool::get().run_workers(parts, [&](int w) {
+        const size_t lo = (size_t)w * per, hi = std::min(n, lo + per);
+        if (lo >= hi) return;
+        if (!pread_all(fd, dst + lo, hi - lo, off + lo)) {
+            ok.store(false);
+            return;
+        }
+        reg[w] = crc_update(0u, dst + lo, hi - lo);
+    });
+    if (!ok.load()) return false;
+    for (int w = 0; w < parts; ++w) {
+        const size_t lo = (size_t)w * per, hi = std::min(n, lo + per);
+        if (lo >= hi) break;
+        state = gf2_apply(zero_map_cached(hi - lo), state) ^ reg[w];
+    }
+    return true;
 }
 
 // ------------------------------------------------------------------ staging
@@ -457,10 +532,11 @@ int fsdp_load_shard(const char* path, fsdp_ckpt_info* info_out, void* master, vo
     const uint64_t sbytes = (uint64_t)info.shard_numel * (uint64_t)fsdp::dt_size(info.state_dt);
     if (sbytes > 0 && (!master || !exp_avg || !exp_avg_sq))
         return fsdp::fail(FSDP_E_INVAL, "master, exp_avg and exp_avg_sq must be non-NULL");
-    if (fseeko(in.f, (off_t)h.payload_offset, SEEK_SET) != 0) return fsdp::fail(FSDP_E_FORMAT, "%s: truncated", path);
     const Piece pieces[3] = {{nullptr, (char*)master, sbytes},
                              {nullptr, (char*)exp_avg, sbytes},
                              {nullptr, (char*)exp_avg_sq, sbytes}};
+    const int fd = fileno(in.f);
+    uint64_t foff = h.payload_offset;   // read_header bounded the payload by the file's length
     uint32_t crc = 0xFFFFFFFFu;
     if (on_device) {
         Staging st;
@@ -468,36 +544,28 @@ int fsdp_load_shard(const char* path, fsdp_ckpt_info* info_out, void* master, vo
         if (e != hipSuccess) return fsdp::hip_fail(e, "pinned staging allocation");
         hipStream_t s = (hipStream_t)stream;
         size_t k = 0;
-        std::future<uint32_t> sum;   // checksum of the previous chunk, running on a helper thread
         for (const Piece& p : pieces) {
             for (uint64_t off = 0; off < p.bytes; off += kChunk, ++k) {
                 const size_t n = (size_t)std::min<uint64_t>(kChunk, p.bytes - off);
-                // the staging buffer of chunk k was last used by chunk k-2's copy
-                if (k >= 2 && (e = hipEventSynchronize(st.ev[k % 2])) != hipSuccess) {
-                    if (sum.valid()) sum.wait();
+                // the staging buffer of chunk k was last used by chunk k-2's copy,
+                // which ran while chunk k-1 was read
+                if (k >= 2 && (e = hipEventSynchronize(st.ev[k % 2])) != hipSuccess)
                     return fsdp::hip_fail(e, "host-to-device copy");
-                }
-                const bool got = read_all(in.f, st.buf[k % 2], n);   // overlaps chunk k-1's checksum
-                if (sum.valid()) crc = sum.get();
-                if (!got) return fsdp::fail(FSDP_E_FORMAT, "%s: truncated payload", path);
-                const void* b = st.buf[k % 2];
-                sum = std::async(std::launch::async, [crc, b, n] { return crc_update(crc, b, n); });
+                if (!read_sum(fd, foff, (char*)st.buf[k % 2], n, crc))
+                    return fsdp::fail(FSDP_E_FORMAT, "%s: truncated payload", path);
+                foff += n;
                 e = hipMemcpyAsync(p.dst + off, st.buf[k % 2], n, hipMemcpyHostToDevice, s);
                 if (e == hipSuccess) e = hipEventRecord(st.ev[k % 2], s);
-                if (e != hipSuccess) {
-                    sum.wait();
-                    return fsdp::hip_fail(e, "host-to-device copy");
-                }
+                if (e != hipSuccess) return fsdp::hip_fail(e, "host-to-device copy");
             }
         }
-        if (sum.valid()) crc = sum.get();
         for (int i = 0; i < 2; ++i)
             if ((e = hipEventSynchronize(st.ev[i])) != hipSuccess) return fsdp::hip_fail(e, "host-to-device copy");
     } else {
         for (const Piece& p : pieces) {
-            if (!p.bytes) continue;
-            if (!read_all(in.f, p.dst, p.bytes)) return fsdp::fail(FSDP_E_FORMAT, "%s: truncated payload", path);
-            crc = crc_update(crc, p.dst, p.bytes);
+            if (!read_sum(fd, foff, p.dst, (size_t)p.bytes, crc))
+                return fsdp::fail(FSDP_E_FORMAT, "%s: truncated payload", path);
+            foff += p.bytes;
         }
     }
     if ((crc ^ 0xFFFFFFFFu) != h.crc_payload)

@@ -218,3 +218,32 @@ def test_a_consistently_forged_header_cannot_make_the_reader_allocate(tmp_path):
         open(path, "wb").write(bad)
         assert _load_code(path, S) == N.E_FORMAT, n
         assert "payload layout" in N.lib().fsdp_last_error().decode()
+
+
+def test_large_shard_read_in_parts(tmp_path):
+    """A state shard of several 4 MB parts is read and checksummed by several
+    workers whose registers are folded in file order: the round trip is exact,
+    the whole-file checksum equals the plain CRC32C of the payload bytes, and a
+    flipped byte in any part (first, a middle one, the last) is caught."""
+    S = 3 * (1 << 20) + 517                       # 12 MB of fp32 per state buffer: three parts and a tail
+    numels = [2 * S - 1]
+    p, m, v = _state(S, 9)
+    path = str(tmp_path / "big-shard1")
+    ss.save_shard(path, numels, 2, 1, p, m, v, step=3, hp=ss.AdamWHP())
+    raw = bytes(open(path, "rb").read())
+    payload = raw[4096:]
+    assert payload == p.tobytes() + m.tobytes() + v.tobytes()
+    import struct
+    assert struct.unpack("<I", raw[108:112])[0] == _crc(payload)    # crc_payload field
+    q = [np.empty(S, np.float32) for _ in range(3)]
+    ss.load_shard(path, *q)
+    for a, b in zip((p, m, v), q):
+        assert a.tobytes() == b.tobytes()
+    sb = 4 * S
+    for off in (0, 5 << 20, sb + (9 << 20), 3 * sb - 1):
+        bad = bytearray(raw)
+        bad[4096 + off] ^= 0x20
+        open(path, "wb").write(bad)
+        assert _load_code(path, S) == N.E_FORMAT, off
+    open(path, "wb").write(raw)
+    assert _load_code(path, S) == 0
