@@ -208,11 +208,15 @@ inline int units_in_launch(int world, const int64_t* S, int n, int64_t* elems) {
 
 // Whether a unit-step launch with a gather, over `elems` shard elements in
 // all, leaves the peers' copies to a launch of their own (peer_copies in
-// fsdp_units.h): fp32 state, an optimizer that keeps state, and at least 2^24
-// shard elements; otherwise the step's own trip copies them.
+// fsdp_units.h): an optimizer that keeps state and at least 2^24 shard
+// elements, for fp32 and 16-bit state alike; otherwise the step's own trip
+// copies them.  (16-bit state kept the fused form while its bf16 roundings
+// were five instructions and a branch each: its step launch alone was bound by
+// the VALU, 70% busy, and the split lost.)
 constexpr int64_t kSplitGatherElems = int64_t(1) << 24;
 inline bool split_gather(int state_dt, int n_states, int64_t elems) {
-    return state_dt == FSDP_F32 && n_states >= 1 && elems >= kSplitGatherElems;
+    (void)state_dt;
+    return n_states >= 1 && elems >= kSplitGatherElems;
 }
 hipError_t launch_gather(const void* const* srcs, void* const* dsts, int n, int64_t bytes, int cus,
                          void* stream);

@@ -212,11 +212,13 @@ static hipError_t units_batch(const UnitBatch<NW>& B, int64_t tiles, const UnitL
 // start was measured faster for fp32 state with an optimizer that keeps state
 // (same box, two repetitions, % of 8 TB/s for the whole step: GPT-2 Large x36
 // 73.1 -> 75.5, GPT-2 XL 74.7 -> 76.0, 13B x40 72.0 -> 78.7, 70B x96 69.9 ->
-// 77.2; Adamax and SGD with momentum +1.7 and +2.2 points).  The fused form
-// stays where the second launch lost: 16-bit state (1 to 11%), SGD without
-// momentum (1.9 points) and launches of fewer than 2^24 shard elements (GPT-2
-// Large, one 9.8M-element unit per launch: 2.1 points).  The copies as
-// workgroups of the same launch, after the step's tiles, lost to both forms.
+// 77.2; Adamax and SGD with momentum +1.7 and +2.2 points), and, once the bf16
+// rounding became one conversion instruction, for 16-bit state too (70B x96
+// with bf16 state 75.2-75.4 -> 77.8-78.5, 13B x40 +0.8).  The fused form stays
+// where the second launch lost: SGD without momentum (1.9 points) and launches
+// of fewer than 2^24 shard elements (GPT-2 Large, one 9.8M-element unit per
+// launch: 2.1 points).  The copies as workgroups of the same launch, after the
+// step's tiles, lost to both forms.
 template <int NW>
 static hipError_t peer_copies(const UnitBatch<NW>& B, int c, const UnitLaunch& L) {
     const int64_t cs = L.compute_dt == FSDP_F32 ? 4 : 2;

@@ -206,15 +206,17 @@ def test_step_units_optim_validation():
 
 def test_unit_gather_split_launch_plan():
     """The launch-plan query: the peers' copies get a launch of their own only
-    for fp32 state, an optimizer that keeps state, and >= 2^24 shard elements."""
+    for an optimizer that keeps state and >= 2^24 shard elements, with fp32 or
+    16-bit state alike."""
     import torch
     f32, bf16 = torch.float32, torch.bfloat16
     assert ss.unit_gather_split(f32, 2, 1 << 24)
     assert ss.unit_gather_split(f32, 1, 1 << 30)
     assert not ss.unit_gather_split(f32, 2, (1 << 24) - 1)
     assert not ss.unit_gather_split(f32, 0, 1 << 30)
-    assert not ss.unit_gather_split(bf16, 2, 1 << 30)
-    assert not ss.unit_gather_split(torch.float16, 2, 1 << 30)
+    assert ss.unit_gather_split(bf16, 2, 1 << 30)
+    assert ss.unit_gather_split(torch.float16, 2, 1 << 24)
+    assert not ss.unit_gather_split(bf16, 2, (1 << 24) - 1)
     for bad in ((f32, 3, 10), (f32, -1, 10), (f32, 2, -1)):
         with pytest.raises(ss.FsdpError):
             ss.unit_gather_split(*bad)

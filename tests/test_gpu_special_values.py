@@ -165,3 +165,41 @@ def test_bf16_reduce_scatter_keeps_nan_payloads(world):
         assert isnan(got[p - lo]) and isnan(ref[p - lo]), (p, hex(got[p - lo]), hex(ref[p - lo]))
     for p in exact_pos:
         assert got[p - lo] == ref[p - lo]
+
+
+def test_bf16_compute_copy_of_every_fp32_encoding():
+    """The bf16 cast of the step, on all 2^32 fp32 encodings of the parameter.
+    With lr = 0, zero weight decay, zero gradient and zero moments, the update
+    leaves the parameter as it is (p * 1 - 0 * 0; a NaN comes out quiet with its
+    payload), so the compute copy is the cast of the parameter itself: it must
+    equal the oracle's cast bit for bit everywhere -- ties, subnormals, both
+    zeros, infinities and every NaN payload -- and the master must come back as
+    the (quieted) input.  Runs the fp32-state unit kernel in 16 launches of 2^28
+    elements (the vector path; the tail path is covered by the other tests)."""
+    from parity import assert_bits_equal, oracle_chunks
+    n = 1 << 28
+    dev = "cuda"
+    m = torch.zeros(n, device=dev)
+    v = torch.zeros(n, device=dev)
+    g = torch.zeros(n, device=dev)
+    comp = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    hp = ss.AdamWHP(lr=0.0, weight_decay=0.0, step=1)
+    low = torch.arange(n, dtype=torch.int32, device=dev)
+    for c in range(16):
+        print("chunk", c, flush=True)
+        hi = (c << 28) - (1 << 32) if c >= 8 else c << 28
+        master = (low | hi).view(torch.float32)
+        ss.fsdp_sharded_adamw(master, m, v, [g], 0, True, hp, compute_shard=comp)
+        torch.cuda.synchronize()
+        u = (np.arange(n, dtype=np.uint32) | np.uint32(c << 28))
+        nan = ((u & 0x7F800000) == 0x7F800000) & ((u & 0x007FFFFF) != 0)
+        quiet = u | (nan.astype(np.uint32) << 22)
+        want = np.empty(n, np.uint16)
+
+        def cast(lo, hi_):
+            want[lo:hi_] = oracle.cast(quiet[lo:hi_].view(np.float32), "bf16")
+
+        oracle_chunks(n, cast)
+        assert_bits_equal(np_of(comp), want, "bf16 cast, encodings 0x%08x.." % (c << 28))
+        assert_bits_equal(np_of(master).view(np.uint32), quiet, "master, encodings 0x%08x.." % (c << 28))
+        assert not m.any() and not v.any()

@@ -1,9 +1,9 @@
 """GPU: the two forms of the unit step's all-gather give the same bytes.
 
 A step launch with a gather copies the peers' shards in its own trip, or -- for
-fp32 state, an optimizer that keeps state, and at least 2^24 shard elements in
-the launch (unit_gather_split) -- writes only the own slots and leaves the
-copies to a batched copy launch.  Here the same units are stepped once as one
+an optimizer that keeps state and at least 2^24 shard elements in the launch,
+with fp32 or 16-bit state (unit_gather_split) -- writes only the own slots and
+leaves the copies to a batched copy launch.  Here the same units are stepped once as one
 batch (past the threshold: two launches) and once one unit per call (under it:
 the fused form), from identical inputs, and every output is compared bit for
 bit; the full buffers are also checked against the concatenation of the own
@@ -93,6 +93,39 @@ def test_batched_split_gather_equals_fused(world, gdt, fp32_reduce, cdt, opt):
                 assert torch.equal(_bits(full[q * S:(q + 1) * S]), _bits(ua["peer_shards"][q])), (k, q)
 
 
+@pytest.mark.parametrize("world,state", [(2, torch.bfloat16), (8, torch.bfloat16), (4, torch.float16)])
+def test_sixteen_bit_state_split_gather_equals_fused(world, state):
+    """16-bit parameter, m and v (the parameter shard is the compute shard):
+    three units under the 2^24-element threshold stepped one per call (the
+    fused form) and together (over it: the step, then the batched copies) give
+    the same bits in every output, and the full buffer holds the new parameter
+    shard in its own slot and the peers' shards in theirs."""
+    sizes = [(SPLIT_ELEMS // 2) + 8 * 37 + 5, (SPLIT_ELEMS // 3) + 1, (SPLIT_ELEMS // 4) + 512]
+    print("case", world, state, sizes, flush=True)
+    assert all(not ss.unit_gather_split(state, 2, S) for S in sizes)
+    assert ss.unit_gather_split(state, 2, sum(sizes))
+    rank = 1
+    hp = ss.AdamWHP(1e-3, 0.9, 0.999, 1e-8, 0.01, 3)
+    gdt = torch.bfloat16 if state == torch.bfloat16 else torch.float16
+    a = _units(world, rank, sizes, gdt, state, 17)
+    for u in a:
+        for key in ("master", "exp_avg", "exp_avg_sq"):
+            u[key] = u[key].to(state)
+    b = _clone(a)
+    ss.fsdp_step_units(a, rank, False, hp)
+    for u in b:
+        ss.fsdp_step_units([u], rank, False, hp)
+    torch.cuda.synchronize()
+    for k, (ua, ub, S) in enumerate(zip(a, b, sizes)):
+        for key in ("master", "exp_avg", "exp_avg_sq", "full"):
+            assert torch.equal(_bits(ua[key]), _bits(ub[key])), (k, key)
+        full = ua["full"]
+        assert torch.equal(_bits(full[rank * S:(rank + 1) * S]), _bits(ua["master"])), k
+        for q in range(world):
+            if q != rank:
+                assert torch.equal(_bits(full[q * S:(q + 1) * S]), _bits(ua["peer_shards"][q])), (k, q)
+
+
 def test_split_gather_generic_world_one_unit_per_launch():
     """World 3 takes the generic kernel, one unit per launch: a unit of 2^24
     shard elements takes the split form and matches the two-call pipeline
@@ -158,8 +191,9 @@ def test_unit_above_the_launch_cap_is_stepped_in_slices():
 
 
 def test_sixteen_bit_state_unit_above_the_launch_cap():
-    """The same slicing with bf16 parameter, m and v (the copies in the step's
-    trip): every element matches the oracle's 16-bit AdamW bit for bit."""
+    """The same slicing with bf16 parameter, m and v (the peers' copies in a
+    launch after each slice): every element matches the oracle's 16-bit AdamW
+    bit for bit."""
     import numpy as np
     import oracle
     from parity import assert_bits_equal, oracle_chunks
