@@ -153,7 +153,7 @@ __device__ __forceinline__ void load8(const void* __restrict__ base, int64_t vi,
 // threadIdx.x % 64 stores vector vi with vi % 64 == l, the wave the 64
 // consecutive vectors from vi - l.  16-bit: one dwordx4 per lane, the wave's
 // 1 KB span with the sc1 policy (the reduce-scatter's 16-bit output, the
-// bf16-state unit step with N <= 2).  fp32 (two instructions, each one half of
+// bf16-state unit step).  fp32 (two instructions, each one half of
 // every 32-byte piece of the span) keeps plain non-temporal stores: with the
 // sc1 policy that form measured 35% slower, so fp32 outputs take the group
 // layout (store8g) instead.

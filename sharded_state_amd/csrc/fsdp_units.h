@@ -24,7 +24,7 @@ namespace fsdp {
 
 // ----------------------------------------------------------------- kernels
 // One unit's step on vector vi (8 elements of a whole group in the group
-// layout, load8g; for bf16 state with N <= 2, 8 consecutive elements, load8):
+// layout, load8g; for bf16 state, 8 consecutive elements, load8):
 // every load first (the N gradient blocks, the parameter and
 // the optimizer's state, the peers' compute vectors), then the math, then every
 // store.  With GATHER, `out` is this rank's slot of the full buffer and the
@@ -53,11 +53,12 @@ __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t 
     // there; the hint gains 0.5 to 3 points on the fp32-state shapes and 0.7 on
     // the N = 8 bf16-state shape; same box, same bench)
     constexpr bool kNtState = SF == FSDP_F32 || NW == 0 || NW > 2;
-    // bf16 state with N <= 2 (every stream 16-bit): 8 consecutive elements per
-    // lane, one dwordx4 per stream (+2.1 to +2.5 points against the group layout
-    // on GPT-2 Large and XL; fp16 state lost 2.2 and N = 8 tied, so they and
-    // fp32 state keep the group layout)
-    constexpr bool kG = !(SF == FSDP_BF16 && NW >= 1 && NW <= 2);
+    // bf16 state (every stream 16-bit): 8 consecutive elements per lane, one
+    // dwordx4 per stream (+2.1 to +2.5 points against the group layout on GPT-2
+    // Large and XL; with N = 8 once the peers' copies left the step's trip, 13B
+    // +0.7 to +0.8 and 70B +0.5 to +1.1 on two boxes; fp16 state lost 2.2 with
+    // N = 2, so it and fp32 state keep the group layout)
+    constexpr bool kG = SF != FSDP_BF16;
     load8x<SF, kNtState, kG>(p, vi, pp);
     if constexpr (OPT::kStates >= 1) load8x<SF, kNtState, kG>(m, vi, mm);
     if constexpr (OPT::kStates >= 2) load8x<SF, kNtState, kG>(v, vi, vv);
