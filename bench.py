@@ -191,6 +191,32 @@ class Unit:
 SEG_PER_LAUNCH = 64   # segments (tensors + zero tail) per flatten launch
 
 
+def call_ms(fn, name, call, launches, torch, N, lib, reps=5):
+    """Mean device time of one C-ABI call (marshalled once) over `reps` calls
+    after two warm-up calls: events on the kernel's own dispatch when the call
+    makes one launch, else two stream events around the calls back to back."""
+    for _ in range(2):
+        N.check(name, fn(*call))
+    torch.cuda.synchronize()
+    if launches == 1:   # events on the kernel's dispatch packet
+        evs = HipEvents(2 * reps)
+        for r in range(reps):
+            N.check("fsdp_time_next_launch", lib.fsdp_time_next_launch(evs.ev[2 * r], evs.ev[2 * r + 1]))
+            N.check(name, fn(*call))
+        torch.cuda.synchronize()
+        ms = statistics.fmean([evs.elapsed_ms(2 * r, 2 * r + 1) for r in range(reps)])
+        evs.close()
+    else:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            N.check(name, fn(*call))
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+    return ms
+
+
 def flatten_rate(cfg, ss, torch, N, lib, workloads, state="f32", reps=5):
     """fsdp_flatten_pad of the first block's tensors into a preallocated flat
     buffer, called through the C ABI (marshalled once): mean kernel duration
@@ -205,32 +231,38 @@ def flatten_rate(cfg, ss, torch, N, lib, workloads, state="f32", reps=5):
     call = (N.ptr_array([t.data_ptr() for t in params]), N.i64_array(cfg.numels), len(cfg.numels),
             ss.dtype_code(flat.dtype), cfg.world, ctypes.c_void_p(flat.data_ptr()), flat.numel(),
             ctypes.byref(padded), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-    for _ in range(2):
-        N.check("fsdp_flatten_pad", lib.fsdp_flatten_pad(*call))
-    torch.cuda.synchronize()
     segs = sum(1 for n in cfg.numels if n > 0) + (1 if Pp > P else 0)
     launches = (segs + SEG_PER_LAUNCH - 1) // SEG_PER_LAUNCH
-    if launches == 1:   # events on the kernel's dispatch packet
-        evs = HipEvents(2 * reps)
-        for r in range(reps):
-            N.check("fsdp_time_next_launch", lib.fsdp_time_next_launch(evs.ev[2 * r], evs.ev[2 * r + 1]))
-            N.check("fsdp_flatten_pad", lib.fsdp_flatten_pad(*call))
-        torch.cuda.synchronize()
-        ms = statistics.fmean([evs.elapsed_ms(2 * r, 2 * r + 1) for r in range(reps)])
-        evs.close()
-    else:   # several launches per call: the calls back to back between two stream events
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            N.check("fsdp_flatten_pad", lib.fsdp_flatten_pad(*call))
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+    ms = call_ms(lib.fsdp_flatten_pad, "fsdp_flatten_pad", call, launches, torch, N, lib, reps)
     es = flat.element_size()
     nbytes = P * es + Pp * es
     del params, flat
     return {"avg_ms": round(ms, 4), "bytes": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "tensors": len(cfg.numels), "launches": launches}
+
+
+def unflatten_rate(cfg, ss, torch, N, lib, workloads, state="f32", reps=5):
+    """fsdp_unflatten_views materializing the first block's tensors out of a
+    gathered full buffer of the compute dtype into preallocated per-tensor
+    destinations, called through the C ABI (marshalled once), timed as the
+    flatten; bytes: P elements read and P written (the padding is no view)."""
+    cdt = workloads.TORCH_DTYPE[cfg.compute_dt if state == "f32" else state]
+    P, Pp, _ = ss.fsdp_layout(cfg.numels, cfg.world)
+    full = torch.empty(Pp, dtype=cdt, device="cuda")
+    full.view(torch.uint8).fill_(0x3c)
+    dsts = [torch.empty(n, dtype=cdt, device="cuda") for n in cfg.numels]
+    views = (N.View * len(cfg.numels))()
+    call = (N.i64_array(cfg.numels), len(cfg.numels), Pp, views, ctypes.c_void_p(full.data_ptr()),
+            ss.dtype_code(cdt), N.ptr_array([d.data_ptr() for d in dsts]),
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    segs = sum(1 for n in cfg.numels if n > 0)
+    launches = (segs + SEG_PER_LAUNCH - 1) // SEG_PER_LAUNCH
+    ms = call_ms(lib.fsdp_unflatten_views, "fsdp_unflatten_views", call, launches, torch, N, lib, reps)
+    es = full.element_size()
+    nbytes = 2 * P * es
+    del full, dsts
+    return {"avg_ms": round(ms, 4), "bytes": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "tensors": len(cfg.numels), "launches": launches, "dtype": str(cdt).replace("torch.", "")}
 
 
 def cpu_host_model():
@@ -825,6 +857,7 @@ def run_workload(args, cfg, torch, ss, N, lib, workloads):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     flat = flatten_rate(cfg, ss, torch, N, lib, workloads, args.state)
+    unflat = unflatten_rate(cfg, ss, torch, N, lib, workloads, args.state)
     out = {
         "metric": METRIC, "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
@@ -843,6 +876,7 @@ def run_workload(args, cfg, torch, ss, N, lib, workloads):
         "unit_elements_per_s": round(cfg.world * S * cfg.blocks / (ms_step * 1e-3), 1),
         "wall_s_timed": round(wall, 3),
         "flatten": flat,
+        "unflatten": unflat,
         "roofline": roof,
         "cpu_baseline": cpu,
         "cpu_all_cores": cpu_all,
@@ -900,7 +934,7 @@ def main():
         out["copy_ceiling"] = ceil
     if args.workload == "all":
         keep = ("value", "unit", "ms_per_step", "pct_hbm_peak", "config", "shard_elements_per_s", "roofline",
-                "cpu_baseline", "cpu_all_cores", "flatten")
+                "cpu_baseline", "cpu_all_cores", "flatten", "unflatten")
         out["configs"] = {n: {k: r.get(k) for k in keep} for n, r in results.items()}
     print(json.dumps(out))
 
