@@ -643,7 +643,7 @@ def bench_offload(args, cfg, torch, ss, N, workloads):
 
 def run_workload(args, cfg, torch, ss, N, lib, workloads):
     """One workload: set-up, warm-up, K timed steps, the roofline of the
-    dominant launch, the CPU-oracle baselines and the flatten rate."""
+    dominant launch, the CPU-oracle baselines and the flatten and unflatten rates."""
     if args.pipeline == "offload":
         return bench_offload(args, cfg, torch, ss, N, workloads)
     ohp = optimizer_hp(args.optimizer, cfg, N)
