@@ -66,6 +66,7 @@ __device__ __forceinline__ void unit_vec(const UnitBatch<NW>& B, int u, int64_t 
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the math
 #pragma unroll
     for (int k = 0; k < 8; ++k) op(finish<NW, GF, FP32R>(acc[k], rs), pp[k], mm[k], vv[k]);
+    if constexpr (OPT::kStorePace > 0 && NW >= 1 && NW <= 2) __builtin_amdgcn_s_sleep(OPT::kStorePace);
     store8x<SF, kG>(p, vi, pp);
     if constexpr (OPT::kStates >= 1) store8x<SF, kG>(m, vi, mm);
     if constexpr (OPT::kStates >= 2) store8x<SF, kG>(v, vi, vv);
