@@ -49,7 +49,14 @@ def test_stacked_gradients_are_the_ranks_gradients():
     cfg = scaled(CONFIGS["gpt3-13b-block"], gpt_block(32) + [("odd", (3,))], name="t", world=3)
     length = cfg.numel + 2
     st = rank_grads(cfg, 2, length)
-    assert st.shape == (3, length) and st.dtype == torch.float16 and st.is_contiguous()
+    assert st.shape == (3, length) and st.dtype == torch.float16
     for q in range(3):
+        assert st[q].is_contiguous()
         assert torch.equal(st[q].view(torch.int16), rank_grad(cfg, 2, q, length).view(torch.int16))
-    assert st.stride(0) == length
+    # rows start on 128-byte lines whatever the length: here length is odd
+    assert length % 2 == 1 and st.stride(0) == (length + 63) // 64 * 64
+    assert all((st[q].data_ptr() - st.data_ptr()) % 128 == 0 for q in range(3))
+    # a length that is already a whole number of lines keeps the rows back to back
+    whole = (cfg.numel + 63) // 64 * 64
+    st2 = rank_grads(cfg, 2, whole)
+    assert st2.stride(0) == whole and st2.is_contiguous()

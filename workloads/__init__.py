@@ -195,10 +195,15 @@ def rank_grad(cfg: UnitConfig, block: int, rank: int, length: int, device="cpu")
 
 def rank_grads(cfg: UnitConfig, block: int, length: int, device="cpu") -> torch.Tensor:
     """Every simulated rank's flat gradient of the unit as the rows of one
-    [world, length] buffer: row q holds rank_grad(cfg, block, q, length).  One
-    allocation puts the N gradient streams at a fixed row stride of length
-    elements from each other, whatever the allocator does with separate buffers."""
-    out = torch.empty((cfg.world, length), dtype=TORCH_DTYPE[cfg.grad_dt], device=device)
+    [world, length] view: row q holds rank_grad(cfg, block, q, length).  One
+    allocation puts the N gradient streams at a fixed row stride from each other,
+    whatever the allocator does with separate buffers.  The stride is length
+    rounded up to 64 elements, so every row starts on a 128-byte line and keeps
+    the 16-byte alignment of the kernels' vector path for any world size and
+    length (a stride of an odd length of 16-bit elements would leave every other
+    row 2-byte aligned, and the kernels would take their per-element path)."""
+    stride = (length + 63) // 64 * 64
+    out = torch.empty((cfg.world, stride), dtype=TORCH_DTYPE[cfg.grad_dt], device=device)[:, :length]
     for q in range(cfg.world):
         out[q].copy_(rank_grad(cfg, block, q, length, device))
     return out
