@@ -44,9 +44,14 @@ namespace fsdp {
 // (load8g / store8g; nvec a multiple of 64, so every wave of the grid-stride
 // loop takes one whole group and each store instruction one contiguous span,
 // stored with the sc1 policy).  16-bit output: 8 consecutive elements per lane,
-// one dwordx4 per lane for every stream.  Measured on block shapes: fp32 output
-// with N = 2 fp16 gradients 5.0 -> 7.1 TB/s, with N = 8 +2% or tied; 16-bit
-// output tied (N = 8) or -2.5% (N = 2) in the group layout, so it keeps its own.
+// one dwordx4 per lane for every stream.  The gradient loads are non-temporal,
+// as in the unit step (each byte is read once).  Measured on block shapes with
+// unit pools larger than the last-level cache, TB/s: non-temporal loads +3 to
+// +8% on eight shapes (70B N = 8 bf16 -> fp32 6.07-6.14 -> 6.48-6.54); fp32
+// output in the group layout against 8 consecutive elements per lane, GPT-2
+// Large N = 2 fp16 4.65-4.81 -> 5.42-5.65, 70B N = 8 6.03-6.07 -> 6.50-6.53,
+// 13B N = 3 6.05-6.08 -> 6.46-6.51; 16-bit output tied (N = 8) or -2.5%
+// (N = 2) in the group layout, so it keeps its own.
 template <int NW, int GF, bool FP32R>
 __global__ __launch_bounds__(kThreads) void k_reduce_scatter(
     GradPtrs<NW> g, int world, int64_t S, int64_t nvec, void* __restrict__ out, ReduceScalars rs) {
@@ -57,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_scatter(
     const GradsOf<NW> gp{g};
     for (int64_t vi = t0; vi < nvec; vi += stride) {
         float acc[8];
-        reduce8<NW, GF, FP32R, false, kGroup>(gp, world, vi, acc);
+        reduce8<NW, GF, FP32R, true, kGroup>(gp, world, vi, acc);
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[k] = finish<NW, GF, FP32R>(acc[k], rs);
         if constexpr (kGroup) store8g<OF>(out, vi, acc);
