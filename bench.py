@@ -6,7 +6,9 @@ per FSDP unit.  One step = every unit slot of the workload, each through
   fused reduce-scatter + AdamW + cast (rank 0's shard)  ->  all-gather x G
   ->  per-tensor views,
 on synthetic inputs already resident in HBM.  Flatten + pad is an init-time
-step: it is timed separately and reported beside the line.
+step: it is timed separately and reported beside the line, as is the
+materializing unflatten, each over independent buffer sets that together
+exceed the last-level cache.
 
 Four pipelines (--pipeline):
   units     (default) fsdp_step_units: the step of every unit of the workload
@@ -191,26 +193,41 @@ class Unit:
 SEG_PER_LAUNCH = 64   # segments (tensors + zero tail) per flatten launch
 
 
-def call_ms(fn, name, call, launches, torch, N, lib, reps=5):
-    """Mean device time of one C-ABI call (marshalled once) over `reps` calls
-    after two warm-up calls: events on the kernel's own dispatch when the call
+# Bytes that one rotation of the flatten / unflatten rate measurements touches
+# at least: four times the 256 MB last-level (Infinity) cache, so that a call's
+# buffers have been evicted before the rotation comes back to them and each call
+# streams HBM.
+ROTATION_BYTES = 4 * (256 << 20)
+ROTATION_MAX = 64
+
+
+def rotation(nbytes):
+    """Number of independent buffer sets for a call that moves `nbytes` bytes."""
+    return max(1, min(ROTATION_MAX, -(-ROTATION_BYTES // max(1, nbytes))))
+
+
+def call_ms(fn, name, calls, launches, torch, N, lib, reps=5):
+    """Mean device time of one C-ABI call over max(reps, len(calls)) calls after
+    two warm-up calls, rotating over `calls` (argument tuples marshalled once,
+    each on its own buffers): events on the kernel's own dispatch when the call
     makes one launch, else two stream events around the calls back to back."""
-    for _ in range(2):
-        N.check(name, fn(*call))
+    reps = max(reps, len(calls))
+    for r in range(2):
+        N.check(name, fn(*calls[r % len(calls)]))
     torch.cuda.synchronize()
     if launches == 1:   # events on the kernel's dispatch packet
         evs = HipEvents(2 * reps)
         for r in range(reps):
             N.check("fsdp_time_next_launch", lib.fsdp_time_next_launch(evs.ev[2 * r], evs.ev[2 * r + 1]))
-            N.check(name, fn(*call))
+            N.check(name, fn(*calls[r % len(calls)]))
         torch.cuda.synchronize()
         ms = statistics.fmean([evs.elapsed_ms(2 * r, 2 * r + 1) for r in range(reps)])
         evs.close()
     else:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(reps):
-            N.check(name, fn(*call))
+        for r in range(reps):
+            N.check(name, fn(*calls[r % len(calls)]))
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
@@ -219,50 +236,60 @@ def call_ms(fn, name, call, launches, torch, N, lib, reps=5):
 
 def flatten_rate(cfg, ss, torch, N, lib, workloads, state="f32", reps=5):
     """fsdp_flatten_pad of the first block's tensors into a preallocated flat
-    buffer, called through the C ABI (marshalled once): mean kernel duration
-    over `reps` calls after two warm-up calls, and the rate of its bytes (read
-    P, write the padded length)."""
+    buffer, called through the C ABI (marshalled once per buffer set): mean
+    kernel duration over the calls of a rotation over independent copies of the
+    tensors and the flat buffer (rotation(): at least 1 GB per rotation), after
+    two warm-up calls, and the rate of its bytes (read P, write the padded
+    length)."""
     params = workloads.param_tensors(cfg, 0, "cuda")
     if state != "f32":
         params = [t.to(workloads.TORCH_DTYPE[state]) for t in params]
     P, Pp, _ = ss.fsdp_layout(cfg.numels, cfg.world)
-    flat = torch.empty(Pp, dtype=params[0].dtype, device="cuda")
+    es = params[0].element_size()
+    nbytes = P * es + Pp * es
+    sets = [(params, torch.empty(Pp, dtype=params[0].dtype, device="cuda"))]
+    for _ in range(rotation(nbytes) - 1):
+        sets.append(([t.clone() for t in params], torch.empty(Pp, dtype=params[0].dtype, device="cuda")))
     padded = ctypes.c_int64()
-    call = (N.ptr_array([t.data_ptr() for t in params]), N.i64_array(cfg.numels), len(cfg.numels),
-            ss.dtype_code(flat.dtype), cfg.world, ctypes.c_void_p(flat.data_ptr()), flat.numel(),
-            ctypes.byref(padded), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    calls = [(N.ptr_array([t.data_ptr() for t in ps]), N.i64_array(cfg.numels), len(cfg.numels),
+              ss.dtype_code(flat.dtype), cfg.world, ctypes.c_void_p(flat.data_ptr()), flat.numel(),
+              ctypes.byref(padded), stream) for ps, flat in sets]
     segs = sum(1 for n in cfg.numels if n > 0) + (1 if Pp > P else 0)
     launches = (segs + SEG_PER_LAUNCH - 1) // SEG_PER_LAUNCH
-    ms = call_ms(lib.fsdp_flatten_pad, "fsdp_flatten_pad", call, launches, torch, N, lib, reps)
-    es = flat.element_size()
-    nbytes = P * es + Pp * es
-    del params, flat
+    ms = call_ms(lib.fsdp_flatten_pad, "fsdp_flatten_pad", calls, launches, torch, N, lib, reps)
+    del params, sets, calls
     return {"avg_ms": round(ms, 4), "bytes": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "tensors": len(cfg.numels), "launches": launches}
+            "tensors": len(cfg.numels), "launches": launches, "buffer_sets": rotation(nbytes)}
 
 
 def unflatten_rate(cfg, ss, torch, N, lib, workloads, state="f32", reps=5):
     """fsdp_unflatten_views materializing the first block's tensors out of a
     gathered full buffer of the compute dtype into preallocated per-tensor
-    destinations, called through the C ABI (marshalled once), timed as the
-    flatten; bytes: P elements read and P written (the padding is no view)."""
+    destinations, called through the C ABI, timed as the flatten (a rotation
+    over independent full buffers and destinations); bytes: P elements read and
+    P written (the padding is no view)."""
     cdt = workloads.TORCH_DTYPE[cfg.compute_dt if state == "f32" else state]
     P, Pp, _ = ss.fsdp_layout(cfg.numels, cfg.world)
-    full = torch.empty(Pp, dtype=cdt, device="cuda")
-    full.view(torch.uint8).fill_(0x3c)
-    dsts = [torch.empty(n, dtype=cdt, device="cuda") for n in cfg.numels]
+    es = torch.empty(0, dtype=cdt).element_size()
+    nbytes = 2 * P * es
     views = (N.View * len(cfg.numels))()
-    call = (N.i64_array(cfg.numels), len(cfg.numels), Pp, views, ctypes.c_void_p(full.data_ptr()),
-            ss.dtype_code(cdt), N.ptr_array([d.data_ptr() for d in dsts]),
-            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sets, calls = [], []
+    for _ in range(rotation(nbytes)):
+        full = torch.empty(Pp, dtype=cdt, device="cuda")
+        full.view(torch.uint8).fill_(0x3c)
+        dsts = [torch.empty(n, dtype=cdt, device="cuda") for n in cfg.numels]
+        sets.append((full, dsts))
+        calls.append((N.i64_array(cfg.numels), len(cfg.numels), Pp, views, ctypes.c_void_p(full.data_ptr()),
+                      ss.dtype_code(cdt), N.ptr_array([d.data_ptr() for d in dsts]), stream))
     segs = sum(1 for n in cfg.numels if n > 0)
     launches = (segs + SEG_PER_LAUNCH - 1) // SEG_PER_LAUNCH
-    ms = call_ms(lib.fsdp_unflatten_views, "fsdp_unflatten_views", call, launches, torch, N, lib, reps)
-    es = full.element_size()
-    nbytes = 2 * P * es
-    del full, dsts
+    ms = call_ms(lib.fsdp_unflatten_views, "fsdp_unflatten_views", calls, launches, torch, N, lib, reps)
+    del sets, calls
     return {"avg_ms": round(ms, 4), "bytes": nbytes, "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-            "tensors": len(cfg.numels), "launches": launches, "dtype": str(cdt).replace("torch.", "")}
+            "tensors": len(cfg.numels), "launches": launches, "dtype": str(cdt).replace("torch.", ""),
+            "buffer_sets": rotation(nbytes)}
 
 
 def cpu_host_model():

@@ -1,6 +1,7 @@
 """bench.py's host logic (no GPU): the byte accounting against the closed forms
-of the algorithmic bytes per shard element, the counter-summary key, and the
-refusal of more than one GPU."""
+of the algorithmic bytes per shard element, the counter-summary key, the buffer
+rotation of the flatten and unflatten rates, and the refusal of more than one
+GPU."""
 import os
 import subprocess
 import sys
@@ -130,3 +131,16 @@ def test_cpu_baseline_whole_units_and_extrapolation():
     assert many["seconds_per_step"] > 0
     # the device inputs were copied before timing: the host state moved, the device state did not
     assert not (units[0].master.numpy() == hosts[0].p).all()
+
+
+def test_flatten_rate_rotation_streams_past_the_last_level_cache():
+    # a rotation of the flatten / unflatten rate measurements touches at least
+    # four times the 256 MB cache, unless the set count is capped; a call that
+    # alone exceeds that needs one set
+    for nbytes in (1, 8_000_000, 78_709_760, 157_419_520, 1 << 30, 2_517_114_880, 12_460_864_000):
+        k = bench.rotation(nbytes)
+        assert 1 <= k <= bench.ROTATION_MAX
+        assert k * nbytes >= bench.ROTATION_BYTES or k == bench.ROTATION_MAX
+        assert k == 1 or (k - 1) * nbytes < bench.ROTATION_BYTES
+    assert bench.ROTATION_BYTES >= 4 * (256 << 20)
+    assert bench.rotation(157_419_520) == 7 and bench.rotation(6_845_104_128) == 1
