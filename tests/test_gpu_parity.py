@@ -123,6 +123,26 @@ def test_unaligned_buffers_take_the_scalar_path():
     assert_bitexact(np_of(rs), oracle.reduce_scatter(gn, 1, "f16", False), "rs 16-bit")
 
 
+@pytest.mark.parametrize("grad_dt,fp32_reduce", [("f16", True), ("f16", False), ("bf16", True), ("bf16", False)])
+def test_reduce_scatter_of_rows_at_an_odd_stride(grad_dt, fp32_reduce):
+    """Three ranks' gradients as the rows of one buffer whose row length, 3 S,
+    is an odd number of 16-bit elements: rows 1 and 2 start 14 and 12 bytes past
+    a 16-byte boundary, so every rank's reads take the per-element path for
+    every row but the first; each rank's shard equals the oracle's, in fp32 and
+    in 16-bit mode."""
+    world, S = 3, 3 * 4096 + 517
+    tdt = torch.float16 if grad_dt == "f16" else torch.bfloat16
+    g = torch.Generator().manual_seed(17)
+    rows = (torch.randn(world, world * S, generator=g) * 1e-3).to(tdt).cuda()
+    assert (rows[1].data_ptr() - rows.data_ptr()) % 16 == 14 and (rows[2].data_ptr() - rows.data_ptr()) % 16 == 12
+    grads = list(rows.unbind(0))
+    host = [np_of(x) for x in grads]
+    for rank in range(world):
+        out = ss.fsdp_reduce_scatter_local(grads, rank, fp32_reduce)
+        torch.cuda.synchronize()
+        assert_bitexact(np_of(out), oracle.reduce_scatter(host, rank, grad_dt, fp32_reduce), "rank %d" % rank)
+
+
 def test_unflatten_and_flatten_with_odd_offsets():
     """The tiny unit's last tensor is one element at an offset that is not a
     multiple of 4 elements; 16-bit tensors of odd sizes break 16-byte alignment."""
